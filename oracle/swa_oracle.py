@@ -1,0 +1,353 @@
+"""Plain fp64 CPU definition of causal sliding-window attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import or call this module.  It
+shares no code with the HIP library and never imports it.
+
+Sources (the five pages on the subject; cited by title and section):
+  [P1] "27. Sliding-Window Attention" (ai-labs PyTorch problem set)
+  [P2] "25. Sliding-Window Causal Attention for Streaming Inference"
+       (cartesia PyTorch problem set)
+  [P3] "Implementation: Sliding Window Attention" (Mistral Architecture
+       chapter of the Language AI Handbook)
+  [P4] "Sliding Window Attention" (bembew.net article)
+  [P5] "NNX Sliding-Window Attention" (crackedaicode exercise)
+
+What is computed.  Attention is the ordinary scaled dot-product attention
+softmax(q k^T / sqrt(D)) v with a band mask applied before the softmax
+[P1 Step-by-Step Approach, steps 1-5; P2 steps 1-5; P3 Step 2; P5 "Mask before
+softmax"].
+
+Window convention.  W counts keys *including the query itself*: key j is
+visible to query i iff j <= i and i - j < W [P1 step 2; P2 step 3 and its note
+that the lower bound is strict; P3 Step 1, the blocking rule and the printed
+8-token mask; P5 "Build the band by index difference" and its printed 5-token
+mask].  P4 ("Mathematical Formulation and Attention Masking") states
+max(0, i - W) <= j <= i, which admits W + 1 keys once i >= W; P5 names exactly
+that form as including one key too many.  The oracle takes the four-page
+reading; ``band_mask_max_form`` keeps P4's form only so that the tests can show
+that it is the off-by-one.
+
+Masking is a *select* to -inf (P1 ``masked_fill``, P5 ``where``), not P3's
+additive 0/-inf matrix: the two agree for finite scores, and the select form
+stays defined when an out-of-window score is itself infinite.
+
+Precision.  Inputs are upcast exactly to float64 (fp32 and bf16 values are
+exactly representable), and everything is computed in float64.
+
+Pins: every function here is checked in ``tests/test_oracle.py`` against the
+masks the pages print, P5's worked example, W >= T reducing to a library
+causal-attention routine, W = 1 returning v, the trailing moving average for
+zero Q/K, out-of-window corruption invariance, and brute force on tiny inputs.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Iterable, Sequence
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------
+# Window predicate
+# ----------------------------------------------------------------------------
+
+def _check_window(W) -> int:
+    """Positive integer window.  [P5 "Mask before softmax": a positive W keeps
+    the diagonal, so no row is entirely masked; a fully masked row is outside
+    the contract.]  W < 1 is rejected rather than producing NaN rows."""
+    if isinstance(W, bool) or not isinstance(W, (int, np.integer)):
+        raise TypeError(f"window size must be an integer, got {type(W).__name__}")
+    W = int(W)
+    if W < 1:
+        raise ValueError(f"window size must be >= 1, got {W}")
+    return W
+
+
+def band_mask(T: int, W: int) -> np.ndarray:
+    """Boolean (T, T) band: ``[i, j]`` is True iff key j is visible to query i.
+
+    [P1 step 2: keep (j <= i) & ((i - j) < window_size).  P5 "Build the band by
+    index difference": diff = i - j, keep (diff >= 0) & (diff < W).]
+    """
+    W = _check_window(W)
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    diff = i - j
+    return (diff >= 0) & (diff < W)
+
+
+def band_mask_max_form(T: int, W: int) -> np.ndarray:
+    """P4's printed visibility rule, max(0, i - W) <= j <= i.
+
+    [P4 "Mathematical Formulation and Attention Masking".]  Kept only so that
+    tests can show it equals ``band_mask(T, W + 1)`` (one extra key, as P5's
+    "Build the band by index difference" warns) and differs from both printed
+    masks.  Not used by any attention function here.
+    """
+    W = _check_window(W)
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    return (j >= np.maximum(0, i - W)) & (j <= i)
+
+
+# ----------------------------------------------------------------------------
+# Prefill: three independent tiers of the same definition
+# ----------------------------------------------------------------------------
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def swa_dense(q, k, v, W: int, return_weights: bool = False):
+    """The pages' dense recipe in float64.
+
+    q, k: (..., T, D); v: (..., T, Dv); any leading dims (P1 and P4 use
+    (B, H, T, D), P2 uses (B, T, D), P5 uses (H, T, Dh)).
+
+    1. scores = q @ k^T / sqrt(D)          [P1 step 1; P2 step 1; P5 code]
+    2. band mask, select -inf outside it   [P1 steps 2-3; P5 "Mask before softmax"]
+    3. stable softmax over keys            [P3 Step 2: subtract the row max,
+                                            exponentiate, divide by the sum]
+    4. weights @ v                         [P1 step 5]
+
+    Returns (..., T, Dv) float64, and the (..., T, T) weights when asked
+    (P3's function returns both).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    T, D = q.shape[-2], q.shape[-1]
+    if k.shape[-2] != T or v.shape[-2] != T or k.shape[-1] != D:
+        raise ValueError("q, k, v must share T, and q, k must share D")
+    scores = np.matmul(q, np.swapaxes(k, -1, -2)) / math.sqrt(D)
+    mask = band_mask(T, W)
+    scores = np.where(mask, scores, -np.inf)
+    row_max = scores.max(axis=-1, keepdims=True)
+    e = np.exp(scores - row_max)
+    weights = e / e.sum(axis=-1, keepdims=True)
+    out = np.matmul(weights, v)
+    if return_weights:
+        return out, weights
+    return out
+
+
+def swa_rows(q, k, v, W: int, rows: Iterable[int]):
+    """Output rows ``rows`` computed one by one from the definition.
+
+    For query i the visible keys are j in [max(0, i - W + 1), i] (the same set
+    as ``band_mask``: j <= i and i - j < W, P1 step 2, P5 "Build the band by
+    index difference").  Over that set: s_j = q_i . k_j / sqrt(D), then a
+    stable softmax and the weighted sum of v_j (P3 Step 2).  Only the band is
+    touched, so this works at full size for a sample of rows.
+
+    q, k: (..., T, D); v: (..., T, Dv) (float arrays of any float dtype).
+    Returns (..., len(rows), Dv) float64.
+    """
+    W = _check_window(W)
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    T, D = q.shape[-2], q.shape[-1]
+    Dv = v.shape[-1]
+    lead = q.shape[:-2]
+    Q = q.reshape(-1, T, D)
+    K = k.reshape(-1, T, D)
+    V = v.reshape(-1, T, Dv)
+    rows = [int(r) for r in rows]
+    out = np.empty((Q.shape[0], len(rows), Dv), dtype=np.float64)
+    root_d = math.sqrt(D)
+    for r, i in enumerate(rows):
+        if not 0 <= i < T:
+            raise IndexError(f"row {i} outside [0, {T})")
+        lo = max(0, i - W + 1)
+        kk = K[:, lo:i + 1, :].astype(np.float64)              # (N, n, D)
+        vv = V[:, lo:i + 1, :].astype(np.float64)              # (N, n, Dv)
+        qi = Q[:, i, :].astype(np.float64)                     # (N, D)
+        s = np.matmul(kk, qi[:, :, None])[:, :, 0] / root_d     # (N, n)
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        w = e / e.sum(axis=1, keepdims=True)
+        out[:, r, :] = np.matmul(w[:, None, :], vv)[:, 0, :]
+    return out.reshape(lead + (len(rows), Dv))
+
+
+def swa_loop(q, k, v, W: int):
+    """Pure-Python triple loop (tiny inputs only, T * W * D small).
+
+    Same definition as ``swa_dense``, written with scalar arithmetic so that no
+    library routine is involved.  q, k: (..., T, D); v: (..., T, Dv).
+    """
+    W = _check_window(W)
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    T, D = q.shape[-2], q.shape[-1]
+    Dv = v.shape[-1]
+    lead = q.shape[:-2]
+    Q = q.reshape(-1, T, D)
+    K = k.reshape(-1, T, D)
+    V = v.reshape(-1, T, Dv)
+    out = np.zeros((Q.shape[0], T, Dv), dtype=np.float64)
+    root_d = math.sqrt(D)
+    for n in range(Q.shape[0]):
+        for i in range(T):
+            keys = [j for j in range(T) if j <= i and i - j < W]
+            s = []
+            for j in keys:
+                acc = 0.0
+                for d in range(D):
+                    acc += float(Q[n, i, d]) * float(K[n, j, d])
+                s.append(acc / root_d)
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            total = sum(e)
+            for d in range(Dv):
+                acc = 0.0
+                for j, ej in zip(keys, e):
+                    acc += (ej / total) * float(V[n, j, d])
+                out[n, i, d] = acc
+    return out.reshape(lead + (T, Dv))
+
+
+# ----------------------------------------------------------------------------
+# Decode against a bounded W-slot ring
+# ----------------------------------------------------------------------------
+
+def ring_slot(p: int, W: int) -> int:
+    """Slot of absolute position p in a W-slot ring.
+
+    Reading of the bounded cache that keeps only the window and drops anything
+    older [P2 Problem; P4 Key Advantages, "KV cache of size W"]: W slots, and a
+    token overwrites the one exactly W positions older, so position p lives in
+    slot p mod W.
+    """
+    W = _check_window(W)
+    if p < 0:
+        raise ValueError("position must be >= 0")
+    return int(p) % W
+
+
+def ring_fill(kseq, vseq, pos: Sequence[int], W: int, fill: float = np.nan):
+    """Build ring contents from whole token sequences.
+
+    kseq, vseq: (S, H, T, D) per-stream token sequences; pos: (S,) current
+    absolute position per stream (pos[s] < T).  Every token t in
+    (pos - W, pos] is written to slot ``ring_slot(t, W)``; slots no token has
+    reached yet hold ``fill``.  Returns float64 rings (S, H, W, D).
+    """
+    W = _check_window(W)
+    kseq = np.asarray(kseq)
+    vseq = np.asarray(vseq)
+    S, H, T, D = kseq.shape
+    Dv = vseq.shape[-1]
+    kring = np.full((S, H, W, D), fill, dtype=np.float64)
+    vring = np.full((S, H, W, Dv), fill, dtype=np.float64)
+    for s in range(S):
+        p = int(pos[s])
+        if not 0 <= p < T:
+            raise ValueError("pos must lie in [0, T)")
+        for t in range(max(0, p - W + 1), p + 1):
+            w = ring_slot(t, W)
+            kring[s, :, w, :] = kseq[s, :, t, :]
+            vring[s, :, w, :] = vseq[s, :, t, :]
+    return kring, vring
+
+
+def _ring_tokens(p: int, W: int) -> list:
+    """(slot, token) pairs held by a ring whose newest token is at position p.
+
+    Slot w holds the token t in (p - W, p] with t mod W == w, i.e.
+    t = p - ((p - w) mod W); slots whose token would be negative are empty.
+    """
+    pairs = []
+    for w in range(W):
+        t = p - ((p - w) % W)
+        if t >= 0:
+            pairs.append((w, t))
+    return pairs
+
+
+def swa_decode(q, kring, vring, pos: Sequence[int], W: int):
+    """One decode step per stream against its ring.
+
+    q: (S, H, D) query of each stream at absolute position pos[s], whose own
+    K/V are already in the ring; kring, vring: (S, H, W, D).  The visible keys
+    are exactly the ring's occupied slots, which hold the tokens
+    (pos - W, pos] (the same window as prefill row pos).  Softmax over them and
+    the weighted sum of their values (P3 Step 2).  Empty slots are never read,
+    so they may hold anything.  Returns (S, H, Dv) float64.
+    """
+    W = _check_window(W)
+    q = np.asarray(q)
+    kring = np.asarray(kring)
+    vring = np.asarray(vring)
+    S, H, D = q.shape
+    Dv = vring.shape[-1]
+    if kring.shape[:3] != (S, H, W) or vring.shape[:3] != (S, H, W):
+        raise ValueError("rings must be (S, H, W, D)")
+    out = np.empty((S, H, Dv), dtype=np.float64)
+    root_d = math.sqrt(D)
+    for s in range(S):
+        p = int(pos[s])
+        if p < 0:
+            raise ValueError("pos must be >= 0")
+        slots = [w for w, _ in _ring_tokens(p, W)]
+        kk = kring[s][:, slots, :].astype(np.float64)           # (H, n, D)
+        vv = vring[s][:, slots, :].astype(np.float64)           # (H, n, Dv)
+        qs = q[s].astype(np.float64)                            # (H, D)
+        sc = np.matmul(kk, qs[:, :, None])[:, :, 0] / root_d
+        m = sc.max(axis=1, keepdims=True)
+        e = np.exp(sc - m)
+        w = e / e.sum(axis=1, keepdims=True)
+        out[s] = np.matmul(w[:, None, :], vv)[:, 0, :]
+    return out
+
+
+def swa_chunk(q, kc, vc, kring, vring, pos0: Sequence[int], W: int):
+    """Chunked prefill that continues a stream held in a W-slot ring.
+
+    A chunk of C new tokens at absolute positions pos0[s] .. pos0[s] + C - 1
+    arrives for every stream; the ring holds the stream's tokens before pos0
+    (positions (pos0 - W, pos0), see ``ring_fill``).  Query p of the chunk sees
+    the tokens (p - W, p]: those older than pos0 come from the ring, the rest
+    from the chunk itself.  This is the definition of prefill row p over the
+    stream's whole history [P1 Problem, the rolling-buffer follow-up; P2
+    Problem, bounded cache].
+
+    q, kc, vc: (S, H, C, D); kring, vring: (S, H, W, D).  Returns
+    (S, H, C, Dv) float64.
+    """
+    W = _check_window(W)
+    q = np.asarray(q)
+    kc = np.asarray(kc)
+    vc = np.asarray(vc)
+    kring = np.asarray(kring)
+    vring = np.asarray(vring)
+    S, H, C, D = q.shape
+    Dv = vc.shape[-1]
+    out = np.empty((S, H, C, Dv), dtype=np.float64)
+    root_d = math.sqrt(D)
+    for s in range(S):
+        p0 = int(pos0[s])
+        if p0 < 0:
+            raise ValueError("pos0 must be >= 0")
+        for c in range(C):
+            p = p0 + c
+            ks, vs = [], []
+            for t in range(max(0, p - W + 1), p + 1):
+                if t < p0:
+                    w = t % W
+                    ks.append(kring[s, :, w, :])
+                    vs.append(vring[s, :, w, :])
+                else:
+                    ks.append(kc[s, :, t - p0, :])
+                    vs.append(vc[s, :, t - p0, :])
+            kk = np.stack(ks, axis=1).astype(np.float64)        # (H, n, D)
+            vv = np.stack(vs, axis=1).astype(np.float64)        # (H, n, Dv)
+            qs = q[s, :, c, :].astype(np.float64)               # (H, D)
+            sc = np.matmul(kk, qs[:, :, None])[:, :, 0] / root_d
+            m = sc.max(axis=1, keepdims=True)
+            e = np.exp(sc - m)
+            w = e / e.sum(axis=1, keepdims=True)
+            out[s, :, c, :] = np.matmul(w[:, None, :], vv)[:, 0, :]
+    return out
