@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Throughput of the causal sliding-window attention hot path on one GPU.
+
+One step is one pass of the whole path over resident synthetic inputs:
+  * prefill of one Mistral-7B-shaped attention layer, bf16 [1, 32, 8192, 128],
+    window 4096 (swa_forward), and
+  * one decode token for 256 independent streams, 32 heads, head size 128,
+    against full 4096-slot bf16 rings (swa_decode).
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+
+Prints one JSON line.  ``value`` is the prefill's useful band TFLOP/s,
+4 * B * H * D * sum_i min(i + 1, W) flops per launch; the decode's KV GB/s
+(bytes of the valid slots' k and v plus q and out) is reported beside it.
+Kernel times come from HIP events recorded on the stream the kernels are
+launched on; ms_per_step is the wall time of the K timed steps between two
+device synchronisations.  The ``cpu_baseline`` leg times the fp64 CPU oracle
+on a bounded sample of the same prefill workload (one BLAS thread).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("band attention TFLOP/s & % MFMA peak (prefill); KV GB/s & % HBM peak (decode)")
+PREFILL = "prefill_bf16_b1_h32_t8192_d128_w4096"
+DECODE = "decode_bf16_s256_h32_d128_w4096"
+# MI355X published peaks: dense bf16 matrix throughput and HBM3E bandwidth.
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+PREFILL_SOURCES = ["sliding_window_causal_amd/csrc/swa_prefill_bf16.hip",
+                   "sliding_window_causal_amd/csrc/swa_internal.h"]
+DECODE_SOURCES = ["sliding_window_causal_amd/csrc/swa_decode_bf16.hip",
+                  "sliding_window_causal_amd/csrc/swa_internal.h"]
+
+
+def band_pairs(T: int, W: int) -> int:
+    """sum_{i<T} min(i + 1, W): (query, key) pairs inside the band."""
+    if W >= T:
+        return T * (T + 1) // 2
+    return W * T - W * (W - 1) // 2
+
+
+def prefill_flops(B, H, T, D, W) -> int:
+    return 4 * B * H * D * band_pairs(T, W)
+
+
+def decode_bytes(S, H, D, n, elem=2) -> int:
+    """k and v of the n valid slots, plus q and out, per launch."""
+    return 2 * S * H * n * D * elem + 2 * S * H * D * elem
+
+
+def source_sha(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(name: str, sha: str):
+    """HBM bytes per launch from a committed PMC summary, if it was taken on
+    this exact kernel source (else None)."""
+    path = os.path.join(PROFILES, name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for ln in open(path):
+        if ":" in ln and not ln.startswith("#"):
+            key, val = ln.split(":", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("kernel_source_sha") != sha or "hbm_bytes_per_launch" not in kv:
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def cpu_baseline_prefill(q, k, v, W, seconds: float):
+    """Time the fp64 oracle's per-row tier on rows of the prefill workload
+    until about ``seconds`` have passed; returns useful TFLOP/s."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import swa_oracle as so
+
+    qh = q[0].float().cpu().numpy()
+    kh = k[0].float().cpu().numpy()
+    vh = v[0].float().cpu().numpy()
+    H, T, D = qh.shape
+    rng = np.random.default_rng(0)
+    rows = rng.integers(W, T, size=4096)          # full-window rows, the steady state
+    flops = 0
+    done = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for i in rows:
+            so.swa_rows(qh, kh, vh, W, [int(i)])
+            flops += 4 * H * D * min(int(i) + 1, W)
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} random full-window rows (all {H} heads) of the {PREFILL} layer, "
+                  f"fp64 per-row oracle tier, one BLAS thread, {dt:.1f} s",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
+                    help="profiling aid: run one kernel only (the JSON line is then partial)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the path shards by heads, batch or streams with no communication, and this build "
+              "does not launch multi-GPU runs.", file=sys.stderr)
+        return 2
+
+    import torch
+    import sliding_window_causal_amd as swa
+    import swa_inputs as si
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.only == "copy":
+        # Plain copy of a known size, the reference for PMC byte counters.
+        n = 1 << 28                              # 256 Mi floats = 1 GiB read + 1 GiB written
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(args.warmup + args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n,
+                          "launches": args.warmup + args.steps}))
+        return 0
+
+    wp = si.WORKLOADS[PREFILL]
+    wd = si.WORKLOADS[DECODE]
+    do_p = args.only in ("all", "prefill")
+    do_d = args.only in ("all", "decode")
+    print(f"# device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}",
+          file=sys.stderr, flush=True)
+    if do_p:
+        q, k, v = si.workload_qkv(wp, dev)
+        out = torch.empty_like(q)
+    if do_d:
+        qd, kr, vr, pos = si.decode_inputs(wd.S, wd.H, wd.D, wd.W, torch.bfloat16, wd.seed, dev)
+        od = torch.empty_like(qd)
+        n_valid = min(int(pos.min().item()) + 1, wd.W)
+        assert n_valid == wd.W
+    torch.cuda.synchronize()
+    print("# inputs resident", file=sys.stderr, flush=True)
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        if do_p:
+            swa.swa_forward(q, k, v, out, wp.W, stream=stream)
+        if evs is not None:
+            evs[1].record(stream)
+        if do_d:
+            swa.swa_decode(qd, kr, vr, pos, od, stream=stream)
+        if evs is not None:
+            evs[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    p_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    d_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    print("# timed steps done", file=sys.stderr, flush=True)
+
+    res = {
+        "metric": METRIC,
+        "value": None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{PREFILL} + {DECODE}" if args.only == "all" else
+                   (PREFILL if do_p else DECODE)},
+    }
+    if do_p:
+        flops = prefill_flops(wp.B, wp.H, wp.T, wp.D, wp.W)
+        pm = sum(p_ms) / len(p_ms)
+        tflops = flops / (pm * 1e-3) / 1e12
+        sha = source_sha(PREFILL_SOURCES)
+        res["value"] = tflops
+        res["config"]["prefill"] = {"B": wp.B, "H": wp.H, "T": wp.T, "D": wp.D, "W": wp.W,
+                                    "useful_flop_per_launch": flops, "kernel_ms_mean": pm,
+                                    "kernel_ms_min": min(p_ms)}
+        res["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
+                           "traffic": read_traffic("prefill_bf16_t8192_w4096_traffic.txt", sha),
+                           "kernel": "prefill_bf16_kernel<128,4>", "kernel_source_sha": sha}
+    if do_d:
+        nbytes = decode_bytes(wd.S, wd.H, wd.D, wd.W)
+        dm = sum(d_ms) / len(d_ms)
+        gbs = nbytes / (dm * 1e-3) / 1e9
+        sha = source_sha(DECODE_SOURCES)
+        res["decode"] = {
+            "value": gbs, "unit": "GB/s", "kernel_ms_mean": dm, "kernel_ms_min": min(d_ms),
+            "S": wd.S, "H": wd.H, "D": wd.D, "W": wd.W, "bytes_per_launch": nbytes,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS,
+                         "traffic": read_traffic("decode_bf16_s256_w4096_traffic.txt", sha),
+                         "kernel": "decode_bf16_kernel<128>", "kernel_source_sha": sha},
+        }
+        if not do_p:
+            res["value"], res["unit"] = gbs, "GB/s"
+    if do_p and args.only == "all" and not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(q, k, v, wp.W, args.cpu_seconds)
+    res["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+                     "compute_units": props.multi_processor_count,
+                     "torch": torch.__version__, "hip": torch.version.hip}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,117 @@
+/*
+ * swa.h -- C ABI of libswa, causal sliding-window attention for AMD gfx950.
+ *
+ * Operation.  For every query position i, attention over the W most recent
+ * keys including i itself:
+ *
+ *     out[i] = sum_{j in J(i)} softmax_j( q[i] . k[j] / sqrt(D) ) v[j],
+ *     J(i)   = { j : j <= i  and  i - j < W }.
+ *
+ * This is the band of "27. Sliding-Window Attention" (Step-by-Step Approach,
+ * step 2), "25. Sliding-Window Causal Attention for Streaming Inference"
+ * (step 3: a strict lower bound j > i - W), "Implementation: Sliding Window
+ * Attention" (Step 1, the printed 8-token mask) and "NNX Sliding-Window
+ * Attention" (Build the band by index difference).  W >= T is ordinary causal
+ * attention; W = 1 returns v.  The scale is 1/sqrt(D) as on every page.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensors are device memory, dense and row-major (C-contiguous) in the
+ *    stated layout; element type is the `dtype` argument (SWA_F32 = float,
+ *    SWA_BF16 = bfloat16).  Output has the input dtype.
+ *  - The caller owns every buffer.  The library never allocates, frees or
+ *    synchronises; it keeps no state beyond cached device attributes.
+ *  - `out` must not alias any input.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  A launch failure returns SWA_ERR_LAUNCH; faults surface when
+ *    the caller synchronises.
+ *  - Argument errors are reported before any HIP call: SWA_ERR_INVALID_ARG for
+ *    a NULL pointer, a size < 1, or W < 1 (a positive window keeps the
+ *    diagonal, so no row is ever fully masked: "NNX Sliding-Window
+ *    Attention", Mask before softmax); SWA_ERR_UNSUPPORTED for a dtype or
+ *    head size the kernels do not cover.
+ *  - Sizes are int64_t; element offsets are computed in 64 bits.
+ */
+#ifndef SWA_H
+#define SWA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SWA_F32 = 0,   /* IEEE binary32 */
+    SWA_BF16 = 1   /* bfloat16, rounded to nearest even on output */
+} swa_dtype_t;
+
+typedef enum {
+    SWA_OK = 0,
+    SWA_ERR_INVALID_ARG = 1,
+    SWA_ERR_UNSUPPORTED = 2,
+    SWA_ERR_LAUNCH = 3
+} swa_status_t;
+
+/* Version of this ABI (bumped on any signature or semantic change). */
+int swa_abi_version(void);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* swa_status_string(int status);
+
+/*
+ * Prefill: out = band attention of q, k, v.
+ *
+ *   q, k, v, out : [B, H, T, D]  (the (batch, heads, seq, head_dim) layout of
+ *                  "27. Sliding-Window Attention", Reference solution)
+ *   W            : window in keys including the query itself (W >= 1)
+ *   dtype        : SWA_BF16 needs D in {64, 128}; SWA_F32 takes 1 <= D <= 256
+ *
+ * Work is O(B * H * T * min(W, T) * D): only key tiles that intersect a
+ * query tile's band are read ("NNX Sliding-Window Attention", A local mask is
+ * not a sparse implementation).
+ */
+int swa_forward(const void* q, const void* k, const void* v, void* out,
+                int64_t B, int64_t H, int64_t T, int64_t D, int64_t W,
+                int dtype, void* stream);
+
+/*
+ * Decode: one query per stream against a bounded W-slot ring of keys/values
+ * (the bounded cache that drops anything older than the window,
+ * "25. Sliding-Window Causal Attention for Streaming Inference", Problem; a
+ * KV cache of size W, "Sliding Window Attention", Key Advantages).
+ *
+ *   q, out       : [S, H, D]
+ *   kring, vring : [S, H, W, D]; the token at absolute position p lives in
+ *                  slot p mod W
+ *   pos          : device int64[S]; absolute position of each stream's
+ *                  current query, whose own k/v are already in the ring.  The
+ *                  visible keys are the occupied slots [0, min(pos + 1, W)),
+ *                  i.e. tokens (pos - W, pos], so the result equals prefill
+ *                  row pos.  Unoccupied slots are never read.  pos < 0 is
+ *                  outside the contract: the kernel stays in bounds and writes
+ *                  zeros for that stream.
+ *   dtype        : SWA_BF16 needs D in {64, 128}; SWA_F32 takes 1 <= D <= 256
+ */
+int swa_decode(const void* q, const void* kring, const void* vring,
+               const int64_t* pos, void* out,
+               int64_t S, int64_t H, int64_t D, int64_t W,
+               int dtype, void* stream);
+
+/*
+ * Ring append (not part of the timed path): for every stream s and head h,
+ * kring[s, h, pos[s] mod W, :] = knew[s, h, :] and the same for v.
+ *
+ *   knew, vnew   : [S, H, D];  kring, vring : [S, H, W, D];  pos : device int64[S]
+ *   dtype        : SWA_F32 or SWA_BF16, any D >= 1
+ * A negative pos is reduced into [0, W) (the kernel never writes outside
+ * the ring).
+ */
+int swa_ring_append(const void* knew, const void* vnew, void* kring, void* vring,
+                    const int64_t* pos, int64_t S, int64_t H, int64_t D, int64_t W,
+                    int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H */

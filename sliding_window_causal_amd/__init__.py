@@ -1,0 +1,183 @@
+"""Python binding of libswa, causal sliding-window attention on gfx950.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/swa.h``.  PyTorch provides the
+device memory and the stream; nothing here computes attention, and there is
+no CPU fallback: if ``libswa.so`` is missing every entry point raises.
+
+Entry points (same names as the C ABI):
+  swa_forward(q, k, v, out, window_size)        prefill, [B, H, T, D]
+  swa_decode(q, kring, vring, pos, out)          decode against a W-slot ring
+  swa_ring_append(knew, vnew, kring, vring, pos) write position pos into slot pos mod W
+Conveniences that allocate the output with torch:
+  sliding_window_attention(q, k, v, window_size) -> out
+  decode(q, kring, vring, pos) -> out
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "SWA_F32", "SWA_BF16", "SWA_OK", "SWA_ERR_INVALID_ARG",
+    "SWA_ERR_UNSUPPORTED", "SWA_ERR_LAUNCH", "SWAError", "lib", "abi_version",
+    "status_string", "swa_forward", "swa_decode", "swa_ring_append",
+    "sliding_window_attention", "decode",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa.so")
+
+SWA_F32, SWA_BF16 = 0, 1
+SWA_OK, SWA_ERR_INVALID_ARG, SWA_ERR_UNSUPPORTED, SWA_ERR_LAUNCH = 0, 1, 2, 3
+
+_DTYPES = {torch.float32: SWA_F32, torch.bfloat16: SWA_BF16}
+_lib = None
+
+
+class SWAError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libswa error {status}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libswa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m sliding_window_causal_amd.build` "
+            "(there is no fallback implementation)")
+    L = ctypes.CDLL(LIB_PATH)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.swa_abi_version.argtypes = []
+    L.swa_abi_version.restype = i32
+    L.swa_status_string.argtypes = [i32]
+    L.swa_status_string.restype = ctypes.c_char_p
+    L.swa_forward.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i32, p]
+    L.swa_forward.restype = i32
+    L.swa_decode.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, p]
+    L.swa_decode.restype = i32
+    L.swa_ring_append.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, p]
+    L.swa_ring_append.restype = i32
+    _lib = L
+    return L
+
+
+def abi_version() -> int:
+    return int(lib().swa_abi_version())
+
+
+def status_string(status: int) -> str:
+    return lib().swa_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != SWA_OK:
+        raise SWAError(status, status_string(status))
+
+
+def _stream(t: torch.Tensor, stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return ctypes.c_void_p(handle)
+
+
+def _dtype_code(*ts: torch.Tensor) -> int:
+    dt = ts[0].dtype
+    if any(t.dtype != dt for t in ts):
+        raise TypeError("all tensors must share one dtype")
+    if dt not in _DTYPES:
+        raise TypeError(f"dtype {dt} not supported (float32 or bfloat16)")
+    return _DTYPES[dt]
+
+
+def _check_device(*ts: torch.Tensor) -> None:
+    dev = ts[0].device
+    for t in ts:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("expected torch tensors")
+        if t.device.type != "cuda":
+            raise ValueError("tensors must be on a GPU device (no CPU fallback)")
+        if t.device != dev:
+            raise ValueError("tensors must be on one device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _window(window_size) -> int:
+    if isinstance(window_size, bool) or not isinstance(window_size, int):
+        raise TypeError("window_size must be an int")
+    if window_size < 1:
+        raise ValueError("window_size must be >= 1")
+    return window_size
+
+
+def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def swa_forward(q, k, v, out, window_size: int, stream=None) -> None:
+    """Prefill into ``out``; q, k, v, out are contiguous [B, H, T, D]."""
+    W = _window(window_size)
+    _check_device(q, k, v, out)
+    code = _dtype_code(q, k, v, out)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or out.shape != q.shape:
+        raise ValueError("q, k, v, out must all be [B, H, T, D] of one shape")
+    B, H, T, D = q.shape
+    _check(lib().swa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, T, D, W, code,
+                             _stream(q, stream)))
+
+
+def swa_decode(q, kring, vring, pos, out, stream=None) -> None:
+    """Decode into ``out``; q, out [S, H, D]; rings [S, H, W, D]; pos int64 [S]."""
+    _check_device(q, kring, vring, pos, out)
+    code = _dtype_code(q, kring, vring, out)
+    if q.dim() != 3 or kring.dim() != 4 or vring.shape != kring.shape or out.shape != q.shape:
+        raise ValueError("q/out must be [S, H, D] and rings [S, H, W, D]")
+    S, H, D = q.shape
+    if kring.shape[0] != S or kring.shape[1] != H or kring.shape[3] != D:
+        raise ValueError("ring shape does not match q")
+    if pos.dtype != torch.int64 or pos.shape != (S,):
+        raise ValueError("pos must be int64 [S]")
+    W = kring.shape[2]
+    _check(lib().swa_decode(_ptr(q), _ptr(kring), _ptr(vring), _ptr(pos), _ptr(out), S, H, D, W,
+                            code, _stream(q, stream)))
+
+
+def swa_ring_append(knew, vnew, kring, vring, pos, stream=None) -> None:
+    """kring[s, h, pos[s] mod W] = knew[s, h] (and v); knew [S, H, D]."""
+    _check_device(knew, vnew, kring, vring, pos)
+    code = _dtype_code(knew, vnew, kring, vring)
+    if knew.dim() != 3 or vnew.shape != knew.shape or kring.dim() != 4 or vring.shape != kring.shape:
+        raise ValueError("knew/vnew must be [S, H, D] and rings [S, H, W, D]")
+    S, H, D = knew.shape
+    if kring.shape[0] != S or kring.shape[1] != H or kring.shape[3] != D:
+        raise ValueError("ring shape does not match knew")
+    if pos.dtype != torch.int64 or pos.shape != (S,):
+        raise ValueError("pos must be int64 [S]")
+    W = kring.shape[2]
+    _check(lib().swa_ring_append(_ptr(knew), _ptr(vnew), _ptr(kring), _ptr(vring), _ptr(pos),
+                                 S, H, D, W, code, _stream(knew, stream)))
+
+
+def sliding_window_attention(q, k, v, window_size: int):
+    """Prefill returning a new tensor.  [B, H, T, D], or [B, T, D] as one head."""
+    squeeze = q.dim() == 3
+    if squeeze:
+        q, k, v = q.unsqueeze(1), k.unsqueeze(1), v.unsqueeze(1)
+    out = torch.empty_like(q)
+    swa_forward(q, k, v, out, window_size)
+    return out.squeeze(1) if squeeze else out
+
+
+def decode(q, kring, vring, pos):
+    """Decode returning a new [S, H, D] tensor."""
+    out = torch.empty_like(q)
+    swa_decode(q, kring, vring, pos, out)
+    return out

@@ -1,0 +1,103 @@
+// libswa C ABI: argument validation and kernel dispatch.  Declarations and
+// the contract of every entry point are in include/swa.h.
+
+#include "../../include/swa.h"
+#include "swa_internal.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int64_t kMaxRowD = 256;
+
+bool positive(int64_t x) { return x >= 1; }
+
+// Element counts must stay addressable with 64-bit offsets and grid sizes
+// must fit a 32-bit launch.
+bool fits(int64_t a, int64_t b, int64_t c, int64_t d) {
+    const int64_t lim = (int64_t)1 << 62;
+    int64_t x = a;
+    for (int64_t y : {b, c, d}) {
+        if (x > lim / y) return false;
+        x *= y;
+    }
+    return true;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int swa_abi_version(void) { return kAbiVersion; }
+
+const char* swa_status_string(int status) {
+    switch (status) {
+        case SWA_OK: return "ok";
+        case SWA_ERR_INVALID_ARG: return "invalid argument (null pointer, size < 1 or window < 1)";
+        case SWA_ERR_UNSUPPORTED: return "unsupported dtype or head size for this entry point";
+        case SWA_ERR_LAUNCH: return "kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int swa_forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H,
+                int64_t T, int64_t D, int64_t W, int dtype, void* stream) {
+    if (!q || !k || !v || !out) return SWA_ERR_INVALID_ARG;
+    if (!positive(B) || !positive(H) || !positive(T) || !positive(D) || !positive(W))
+        return SWA_ERR_INVALID_ARG;
+    if (!fits(B, H, T, D) || B * H * T >= ((int64_t)1 << 31)) return SWA_ERR_UNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    if (dtype == SWA_BF16) {
+        if (D == 64 || D == 128)
+            return from_hip(swa::launch_prefill_bf16((const swa::bf16*)q, (const swa::bf16*)k,
+                                                     (const swa::bf16*)v, (swa::bf16*)out, B, H, T,
+                                                     (int)D, W, st));
+        return SWA_ERR_UNSUPPORTED;
+    }
+    if (dtype == SWA_F32) {
+        if (D > kMaxRowD) return SWA_ERR_UNSUPPORTED;
+        return from_hip(swa::launch_rowwise_prefill<float>((const float*)q, (const float*)k,
+                                                           (const float*)v, (float*)out, B, H, T,
+                                                           (int)D, W, st));
+    }
+    return SWA_ERR_UNSUPPORTED;
+}
+
+int swa_decode(const void* q, const void* kring, const void* vring, const int64_t* pos, void* out,
+               int64_t S, int64_t H, int64_t D, int64_t W, int dtype, void* stream) {
+    if (!q || !kring || !vring || !pos || !out) return SWA_ERR_INVALID_ARG;
+    if (!positive(S) || !positive(H) || !positive(D) || !positive(W)) return SWA_ERR_INVALID_ARG;
+    if (!fits(S, H, W, D) || S * H >= ((int64_t)1 << 31)) return SWA_ERR_UNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    if (dtype == SWA_BF16) {
+        if (D != 64 && D != 128) return SWA_ERR_UNSUPPORTED;
+        if (W <= swa::kDecodeMaxW)
+            return from_hip(swa::launch_decode_bf16((const swa::bf16*)q, (const swa::bf16*)kring,
+                                                    (const swa::bf16*)vring, pos, (swa::bf16*)out,
+                                                    S, H, (int)D, W, st));
+        return from_hip(swa::launch_rowwise_decode<swa::bf16>(
+            (const swa::bf16*)q, (const swa::bf16*)kring, (const swa::bf16*)vring, pos,
+            (swa::bf16*)out, S, H, (int)D, W, st));
+    }
+    if (dtype == SWA_F32) {
+        if (D > kMaxRowD) return SWA_ERR_UNSUPPORTED;
+        return from_hip(swa::launch_rowwise_decode<float>((const float*)q, (const float*)kring,
+                                                          (const float*)vring, pos, (float*)out, S,
+                                                          H, (int)D, W, st));
+    }
+    return SWA_ERR_UNSUPPORTED;
+}
+
+int swa_ring_append(const void* knew, const void* vnew, void* kring, void* vring,
+                    const int64_t* pos, int64_t S, int64_t H, int64_t D, int64_t W, int dtype,
+                    void* stream) {
+    if (!knew || !vnew || !kring || !vring || !pos) return SWA_ERR_INVALID_ARG;
+    if (!positive(S) || !positive(H) || !positive(D) || !positive(W)) return SWA_ERR_INVALID_ARG;
+    if (!fits(S, H, W, D) || S * H >= ((int64_t)1 << 31)) return SWA_ERR_UNSUPPORTED;
+    if (dtype != SWA_F32 && dtype != SWA_BF16) return SWA_ERR_UNSUPPORTED;
+    return from_hip(swa::launch_ring_append(knew, vnew, kring, vring, pos, S, H, D, W,
+                                            dtype == SWA_F32 ? 4 : 2, (hipStream_t)stream));
+}
+
+}  // extern "C"

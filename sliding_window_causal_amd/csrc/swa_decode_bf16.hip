@@ -1,0 +1,234 @@
+// One-token decode against a bounded W-slot ring of keys and values, bf16 in
+// and out, fp32 arithmetic.  The ring is the bounded cache that keeps only
+// the window ("25. Sliding-Window Causal Attention for Streaming Inference",
+// Problem; "Sliding Window Attention", Key Advantages: a KV cache of size W).
+//
+// The path is bound by HBM: every occupied slot's k and v row is read once
+// (2 * n * D * 2 bytes per (stream, head)) for 4 * n * D flops.  One
+// workgroup of 256 threads owns one (stream, head):
+//   phase 1  scores: a quad of 4 lanes owns a slot row; each lane reads its
+//            D/32 16-byte chunks (a quad reads 64 contiguous bytes per
+//            load), dots them against the query with v_dot2_f32_bf16, and
+//            the quad sums with two DPP steps.  Scores go to LDS, pre-scaled
+//            by log2(e)/sqrt(D).
+//   softmax  exact two-pass over the n LDS scores (max, then exp2 and sum).
+//   phase 2  output: the same quad/slot mapping streams v rows, each lane
+//            accumulating p * v for its 8 * D/32 columns; partial outputs
+//            are reduced across the 64 quads through LDS.
+// Occupied slots are [0, min(pos + 1, W)): unoccupied slots are never read.
+
+#include "swa_internal.h"
+
+namespace swa {
+namespace {
+
+constexpr int kDecThreads = 256;
+constexpr int kQuads = kDecThreads / 4;
+constexpr int kUnroll = 4;
+
+// Sum over the 4 lanes of a quad (DPP quad_perm; no LDS traffic).
+__device__ inline float quad_sum(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+    return x;
+}
+
+__device__ inline float dot8(const u32x4& k, const u32x4& q, float acc) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        // Copy the lanes out first: a bit_cast of a vector-element lvalue
+        // reads element 0 whatever the index.
+        const uint32_t kj = k[j], qj = q[j];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kj),
+                                              __builtin_bit_cast(bf16x2, qj), acc, false);
+    }
+    return acc;
+}
+
+__device__ inline float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ inline float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+template <int D>
+__global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ kring, const bf16* __restrict__ vring,
+    const int64_t* __restrict__ pos, bf16* __restrict__ out, int64_t H, int64_t W, float c) {
+    constexpr int CPL = D / 32;                 // 16-byte chunks per lane per row
+    extern __shared__ __attribute__((aligned(16))) float sm[];
+    float* sc = sm;                             // scores / probabilities, later partial outputs
+    __shared__ float red[kDecThreads / 64];
+
+    const int tid = threadIdx.x;
+    const int quad = tid >> 2, sig = tid & 3;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int64_t sh = blockIdx.x;
+    const int64_t s = sh / H;
+    const int64_t p = pos[s];
+    int64_t n64 = p + 1;
+    n64 = n64 < 0 ? 0 : (n64 > W ? W : n64);
+    const int n = (int)n64;
+    const bf16* __restrict__ Kr = kring + sh * W * D;
+    const bf16* __restrict__ Vr = vring + sh * W * D;
+
+    // query chunks 4 i + sig
+    u32x4 qv[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+        qv[i] = *reinterpret_cast<const u32x4*>(q + sh * D + (4 * i + sig) * 8);
+
+    // ---- phase 1: scores
+    for (int r0 = 0; r0 < n; r0 += kQuads * kUnroll) {
+        u32x4 kv[kUnroll][CPL];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int row = r0 + quad + kQuads * u;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i)
+                kv[u][i] = row < n ? *reinterpret_cast<const u32x4*>(Kr + (int64_t)row * D + (4 * i + sig) * 8)
+                                   : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int row = r0 + quad + kQuads * u;
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) acc = dot8(kv[u][i], qv[i], acc);
+            acc = quad_sum(acc);
+            if (sig == 0 && row < n) sc[row] = acc * c;
+        }
+    }
+    __syncthreads();
+
+    // ---- softmax over the n scores: max, then exp2 and sum
+    float mx = -__builtin_inff();
+    for (int r = tid; r < n; r += kDecThreads) mx = fmaxf(mx, sc[r]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) red[wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    float ls = 0.f;
+    for (int r = tid; r < n; r += kDecThreads) {
+        const float e = __builtin_amdgcn_exp2f(sc[r] - mx);
+        sc[r] = e;
+        ls += e;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ls += __shfl_xor(ls, o, 64);
+    if (lane == 0) red[wave] = ls;
+    __syncthreads();
+    const float l = (red[0] + red[1]) + (red[2] + red[3]);
+
+    // ---- phase 2: o = sum_r p_r v_r over this lane's columns
+    float acc[CPL][8];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+    for (int r0 = 0; r0 < n; r0 += kQuads * kUnroll) {
+        u32x4 vv[kUnroll][CPL];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int row = r0 + quad + kQuads * u;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i)
+                vv[u][i] = row < n ? *reinterpret_cast<const u32x4*>(Vr + (int64_t)row * D + (4 * i + sig) * 8)
+                                   : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int row = r0 + quad + kQuads * u;
+            const float pr = row < n ? sc[row] : 0.f;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc[i][2 * j] = fmaf(pr, bf_lo(vv[u][i][j]), acc[i][2 * j]);
+                    acc[i][2 * j + 1] = fmaf(pr, bf_hi(vv[u][i][j]), acc[i][2 * j + 1]);
+                }
+        }
+    }
+    __syncthreads();   // every lane is done with the probabilities
+
+    // ---- reduce partial outputs over the 64 quads: sm[quad][d]
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm[quad * D + (4 * i + sig) * 8 + e] = acc[i][e];
+    __syncthreads();
+    if (tid < D) {
+        float t = 0.f;
+        for (int qd = 0; qd < kQuads; ++qd) t += sm[qd * D + tid];
+        out[sh * D + tid] = (bf16)(n > 0 ? t / l : 0.f);
+    }
+}
+
+template <int D>
+hipError_t launch(const bf16* q, const bf16* kring, const bf16* vring, const int64_t* pos,
+                  bf16* out, int64_t S, int64_t H, int64_t W, hipStream_t stream) {
+    const int64_t floats = W > (int64_t)kQuads * D ? W : (int64_t)kQuads * D;
+    const unsigned lds = (unsigned)(floats * sizeof(float));
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)decode_bf16_kernel<D>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)(kDecodeMaxW * sizeof(float)));
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    float c = kLog2e / sqrtf((float)D);
+    void* args[] = {(void*)&q, (void*)&kring, (void*)&vring, (void*)&pos, (void*)&out,
+                    (void*)&H, (void*)&W, (void*)&c};
+    return hipLaunchKernel((const void*)decode_bf16_kernel<D>, dim3((unsigned)(S * H)),
+                           dim3(kDecThreads), args, lds, stream);
+}
+
+// ---- ring append -----------------------------------------------------------
+
+template <typename U>
+__global__ __launch_bounds__(256) void ring_append_kernel(
+    const U* __restrict__ knew, const U* __restrict__ vnew, U* __restrict__ kring,
+    U* __restrict__ vring, const int64_t* __restrict__ pos, int64_t H, int64_t D, int64_t W) {
+    const int64_t sh = blockIdx.x;
+    const int64_t s = sh / H;
+    int64_t slot = pos[s] % W;
+    if (slot < 0) slot += W;
+    const int64_t dst = (sh * W + slot) * D;
+    for (int64_t d = threadIdx.x; d < D; d += blockDim.x) {
+        kring[dst + d] = knew[sh * D + d];
+        vring[dst + d] = vnew[sh * D + d];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const bf16* q, const bf16* kring, const bf16* vring,
+                              const int64_t* pos, bf16* out, int64_t S, int64_t H, int D,
+                              int64_t W, hipStream_t stream) {
+    if (D == 128) return launch<128>(q, kring, vring, pos, out, S, H, W, stream);
+    return launch<64>(q, kring, vring, pos, out, S, H, W, stream);
+}
+
+hipError_t launch_ring_append(const void* knew, const void* vnew, void* kring, void* vring,
+                              const int64_t* pos, int64_t S, int64_t H, int64_t D, int64_t W,
+                              int elem_bytes, hipStream_t stream) {
+    const dim3 grid((unsigned)(S * H)), block(D >= 256 ? 256 : (unsigned)((D + 63) / 64 * 64));
+    if (elem_bytes == 4) {
+        const uint32_t* kn = (const uint32_t*)knew;
+        const uint32_t* vn = (const uint32_t*)vnew;
+        uint32_t* kr = (uint32_t*)kring;
+        uint32_t* vr = (uint32_t*)vring;
+        void* args[] = {(void*)&kn, (void*)&vn, (void*)&kr, (void*)&vr, (void*)&pos,
+                        (void*)&H, (void*)&D, (void*)&W};
+        return hipLaunchKernel((const void*)ring_append_kernel<uint32_t>, grid, block, args, 0, stream);
+    }
+    const uint16_t* kn = (const uint16_t*)knew;
+    const uint16_t* vn = (const uint16_t*)vnew;
+    uint16_t* kr = (uint16_t*)kring;
+    uint16_t* vr = (uint16_t*)vring;
+    void* args[] = {(void*)&kn, (void*)&vn, (void*)&kr, (void*)&vr, (void*)&pos,
+                    (void*)&H, (void*)&D, (void*)&W};
+    return hipLaunchKernel((const void*)ring_append_kernel<uint16_t>, grid, block, args, 0, stream);
+}
+
+}  // namespace swa

@@ -1,0 +1,48 @@
+// Internal declarations shared by the libswa translation units (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- launchers (each returns the hipError_t of its launch) -----------------
+
+// Generic wavefront-per-row kernels; T is float or bf16; 1 <= D <= 256.
+template <typename T>
+hipError_t launch_rowwise_prefill(const T* q, const T* k, const T* v, T* out,
+                                  int64_t B, int64_t H, int64_t Tn, int D, int64_t W,
+                                  hipStream_t stream);
+template <typename T>
+hipError_t launch_rowwise_decode(const T* q, const T* kring, const T* vring,
+                                 const int64_t* pos, T* out, int64_t S, int64_t H, int D,
+                                 int64_t W, hipStream_t stream);
+
+// bf16 MFMA band prefill; D in {64, 128}.
+hipError_t launch_prefill_bf16(const bf16* q, const bf16* k, const bf16* v, bf16* out,
+                               int64_t B, int64_t H, int64_t T, int D, int64_t W,
+                               hipStream_t stream);
+
+// bf16 ring decode; D in {64, 128}, W <= kDecodeMaxW.
+constexpr int64_t kDecodeMaxW = 16384;
+hipError_t launch_decode_bf16(const bf16* q, const bf16* kring, const bf16* vring,
+                              const int64_t* pos, bf16* out, int64_t S, int64_t H, int D,
+                              int64_t W, hipStream_t stream);
+
+// Ring append; any D >= 1; elem_bytes is 2 or 4.
+hipError_t launch_ring_append(const void* knew, const void* vnew, void* kring, void* vring,
+                              const int64_t* pos, int64_t S, int64_t H, int64_t D, int64_t W,
+                              int elem_bytes, hipStream_t stream);
+
+}  // namespace swa

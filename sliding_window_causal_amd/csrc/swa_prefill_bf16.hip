@@ -1,0 +1,338 @@
+// Causal sliding-window attention prefill, bf16 in / bf16 out, fp32
+// accumulation, on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
+//
+// Band-only iteration.  A workgroup owns a tile of BM = 32 * NW consecutive
+// queries [i0, i0 + BM) of one (batch, head) and walks only the 64-key tiles
+// that intersect the tile's band [max(0, i0 - W + 1), min(T, i0 + BM)), so the
+// work is O(T * min(W, T) * D) and never the dense O(T^2 * D) of the masked
+// recipe ("NNX Sliding-Window Attention", A local mask is not a sparse
+// implementation).  Each wavefront owns 32 queries and additionally skips the
+// key tiles that miss its own band.  The band predicate j <= i and i - j < W
+// ("27. Sliding-Window Attention", step 2) is evaluated, as a select to -inf,
+// only on the tiles that straddle an edge of the wavefront's band.
+//
+// Per wavefront and key tile (everything fp32 except the MFMA operands):
+//   S^T = K Q^T        32x32 output blocks: lane l holds query l % 32 and 16
+//                      keys of it, so row maxima and sums are mostly in-lane
+//                      plus one exchange with lane l ^ 32 (v_permlane32_swap)
+//   online softmax     running max m and sum l per query (exp2 with the
+//                      1/sqrt(D) * log2(e) scale folded into one FMA), the
+//                      output rescaled by exp2(m_old - m_new)
+//   O^T += V^T P^T     P^T goes from the S^T accumulator straight into the
+//                      B operand (converted to bf16, round to nearest even);
+//                      V^T comes from LDS, where V is stored transposed with
+//                      its keys permuted to match the accumulator's key order.
+// K and V^T tiles are staged in LDS, double buffered: the global loads of the
+// next tile are in flight while the current one is computed.
+
+#include "swa_internal.h"
+
+namespace swa {
+namespace {
+
+template <int D, int NW>
+struct Cfg {
+    static constexpr int BM = 32 * NW;          // queries per workgroup
+    static constexpr int BN = 64;               // keys per tile
+    static constexpr int NT = 64 * NW;          // threads
+    static constexpr int KSTR = D + 8;          // K tile row stride (elements), +16 B breaks bank aliasing
+    static constexpr int VSTR = BN + 8;         // V^T tile row stride (elements)
+    static constexpr int KTILE = BN * KSTR;     // elements
+    static constexpr int VTILE = D * VSTR;      // elements
+    static constexpr int STAGE = KTILE + VTILE; // elements per pipeline stage
+    static constexpr int LDS_BYTES = 2 * STAGE * 2;
+    static constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
+    static constexpr int KCHUNKS = BN * CPR;
+    static constexpr int KPT = (KCHUNKS + NT - 1) / NT;
+    static constexpr int VITEMS = (BN / 4) * CPR;   // (4-key group, 8-d chunk) items
+    static constexpr int VPT = (VITEMS + NT - 1) / NT;
+    static_assert(D == 64 || D == 128, "head size");
+};
+
+struct Args {
+    const bf16* q;
+    const bf16* k;
+    const bf16* v;
+    bf16* out;
+    int64_t T;
+    int64_t W;
+    int nqt;        // query tiles per (b, h)
+    int nblocks;    // grid size
+    int remap;      // 1: spread consecutive logical tiles over one XCD
+    float c;        // log2(e) / sqrt(D)
+};
+
+__device__ inline float swap_max(float x) {
+    // v_permlane32_swap exchanges the two 32-lane halves between its two
+    // outputs; max over both outputs is the max over lanes l and l ^ 32.
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float swap_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Position, inside a 64-key V^T row, of tile key 4 g + r.  Within each
+// 16-key chunk the key offset 8 a + 4 h + r is stored at 8 h + 4 a + r, so
+// that lane half h reads its eight B-operand keys as one 16-byte vector.
+__device__ inline int vt_pos(int g) {
+    const int c16 = g >> 2, gg = g & 3;
+    return 16 * c16 + 8 * (gg & 1) + 4 * (gg >> 1);
+}
+
+template <int D, int NW>
+__device__ inline void load_tile(const bf16* __restrict__ Kbh, const bf16* __restrict__ Vbh,
+                                 int64_t k0, int64_t T, int tid, u32x4 (&kreg)[Cfg<D, NW>::KPT],
+                                 u32x4 (&vreg)[Cfg<D, NW>::VPT][4]) {
+    using C = Cfg<D, NW>;
+#pragma unroll
+    for (int r = 0; r < C::KPT; ++r) {
+        const int c = tid + r * C::NT;
+        kreg[r] = u32x4{0, 0, 0, 0};
+        if (c < C::KCHUNKS) {
+            const int64_t key = k0 + c / C::CPR;
+            if (key < T)
+                kreg[r] = *reinterpret_cast<const u32x4*>(Kbh + key * D + (c % C::CPR) * 8);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < C::VPT; ++r) {
+        const int it = tid + r * C::NT;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vreg[r][e] = u32x4{0, 0, 0, 0};
+        if (it < C::VITEMS) {
+            const int g = it / C::CPR, cc = it % C::CPR;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t key = k0 + 4 * g + e;
+                if (key < T)
+                    vreg[r][e] = *reinterpret_cast<const u32x4*>(Vbh + key * D + cc * 8);
+            }
+        }
+    }
+}
+
+template <int D, int NW>
+__device__ inline void store_tile(bf16* __restrict__ stage, int tid,
+                                  const u32x4 (&kreg)[Cfg<D, NW>::KPT],
+                                  const u32x4 (&vreg)[Cfg<D, NW>::VPT][4]) {
+    using C = Cfg<D, NW>;
+    bf16* Ks = stage;
+    bf16* Vs = stage + C::KTILE;
+#pragma unroll
+    for (int r = 0; r < C::KPT; ++r) {
+        const int c = tid + r * C::NT;
+        if (c < C::KCHUNKS)
+            *reinterpret_cast<u32x4*>(Ks + (c / C::CPR) * C::KSTR + (c % C::CPR) * 8) = kreg[r];
+    }
+#pragma unroll
+    for (int r = 0; r < C::VPT; ++r) {
+        const int it = tid + r * C::NT;
+        if (it < C::VITEMS) {
+            const int g = it / C::CPR, cc = it % C::CPR;
+            bf16* dst = Vs + (cc * 8) * C::VSTR + vt_pos(g);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // keys 4g..4g+3 of d = 8cc + 2j (low halves) and 8cc + 2j + 1
+                const uint32_t lo_e = __builtin_amdgcn_perm(vreg[r][1][j], vreg[r][0][j], 0x05040100u);
+                const uint32_t hi_e = __builtin_amdgcn_perm(vreg[r][3][j], vreg[r][2][j], 0x05040100u);
+                const uint32_t lo_o = __builtin_amdgcn_perm(vreg[r][1][j], vreg[r][0][j], 0x07060302u);
+                const uint32_t hi_o = __builtin_amdgcn_perm(vreg[r][3][j], vreg[r][2][j], 0x07060302u);
+                *reinterpret_cast<u32x2*>(dst + (2 * j) * C::VSTR) = u32x2{lo_e, hi_e};
+                *reinterpret_cast<u32x2*>(dst + (2 * j + 1) * C::VSTR) = u32x2{lo_o, hi_o};
+            }
+        }
+    }
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(Args a) {
+    using C = Cfg<D, NW>;
+    extern __shared__ __attribute__((aligned(16))) bf16 lds[];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 31, hh = lane >> 5;
+
+    // Logical tile: consecutive logical tiles land on one XCD (the hardware
+    // deals workgroups round-robin over 8 XCDs), heads stay together, and
+    // within a head the tiles with the longest bands (the last ones) go first.
+    const int bid = blockIdx.x;
+    const int logical = a.remap ? (bid & 7) * (a.nblocks >> 3) + (bid >> 3) : bid;
+    const int bh = logical / a.nqt;
+    const int qt = a.nqt - 1 - (logical - bh * a.nqt);
+    const int64_t T = a.T, W = a.W;
+    const int64_t i0 = (int64_t)qt * C::BM;
+    const int64_t off = (int64_t)bh * T * D;
+    const bf16* __restrict__ Qbh = a.q + off;
+    const bf16* __restrict__ Kbh = a.k + off;
+    const bf16* __restrict__ Vbh = a.v + off;
+
+    const int64_t qw0 = i0 + 32 * wave;            // this wave's first query
+    const int64_t qi = qw0 + lr;                   // this lane's query
+    const bool wave_active = qw0 < T;
+    const int64_t wlo = qw0 - W + 1 > 0 ? qw0 - W + 1 : 0;       // wave's lowest visible key
+    const int64_t whi = qw0 + 32 < T ? qw0 + 32 : T;             // one past its highest
+
+    // Q^T operand: lane holds q[qi][16 dc + 8 hh .. + 7] for every 16-wide d chunk.
+    bf16x8 qf[D / 16];
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) {
+        if (qi < T)
+            qf[dc] = *reinterpret_cast<const bf16x8*>(Qbh + qi * D + 16 * dc + 8 * hh);
+        else
+            qf[dc] = bf16x8{};
+    }
+
+    const int64_t klo = i0 - W + 1 > 0 ? i0 - W + 1 : 0;
+    const int64_t khi = i0 + C::BM < T ? i0 + C::BM : T;
+    const int t0 = (int)(klo / C::BN);
+    const int t1 = (int)((khi + C::BN - 1) / C::BN);
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+    float m = -__builtin_inff();
+    float lsum = 0.f;
+
+    u32x4 kreg[C::KPT];
+    u32x4 vreg[C::VPT][4];
+    load_tile<D, NW>(Kbh, Vbh, (int64_t)t0 * C::BN, T, tid, kreg, vreg);
+    store_tile<D, NW>(lds, tid, kreg, vreg);
+    __syncthreads();
+
+    for (int t = t0; t < t1; ++t) {
+        const int cur = (t - t0) & 1;
+        const bool more = t + 1 < t1;
+        if (more) load_tile<D, NW>(Kbh, Vbh, (int64_t)(t + 1) * C::BN, T, tid, kreg, vreg);
+
+        const int64_t k0 = (int64_t)t * C::BN;
+        if (wave_active && k0 < whi && k0 + C::BN > wlo) {
+            const bf16* Ks = lds + cur * C::STAGE;
+            const bf16* Vs = Ks + C::KTILE;
+            // ---- S^T = K Q^T for two 32-key blocks
+            f32x16 s[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                s[b] = f32x16{};
+#pragma unroll
+                for (int dc = 0; dc < D / 16; ++dc) {
+                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
+                        Ks + (32 * b + lr) * C::KSTR + 16 * dc + 8 * hh);
+                    s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[dc], s[b], 0, 0, 0);
+                }
+            }
+            // ---- band mask, only where the tile straddles an edge of this wave's band
+            const bool interior = (k0 + C::BN - 1 <= qw0) && (qw0 + 31 - k0 < W);
+            if (!interior) {
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int64_t key = k0 + 32 * b + 8 * (v >> 2) + 4 * hh + (v & 3);
+                        const bool ok = (key <= qi) && (qi - key < W);
+                        s[b][v] = ok ? s[b][v] : -__builtin_inff();
+                    }
+            }
+            // ---- online softmax
+            float mx = s[0][0];
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[b][v]);
+            mx = swap_max(mx);
+            const float m_new = fmaxf(m, mx);
+            const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f((m - m_use) * a.c);
+            const float mc = m_use * a.c;
+            float psum = 0.f;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][v], a.c, -mc));
+                    s[b][v] = p;
+                    psum += p;
+                }
+            lsum = lsum * alpha + psum;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+            m = m_new;
+            // ---- O^T += V^T P^T, four 16-key chunks
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    bf16x8 pf;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pf[e] = (bf16)s[b][8 * c + e];
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) {
+                        const bf16x8 va = *reinterpret_cast<const bf16x8*>(
+                            Vs + (32 * db + lr) * C::VSTR + 32 * b + 16 * c + 8 * hh);
+                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf, o[db], 0, 0, 0);
+                    }
+                }
+        }
+
+        if (more) store_tile<D, NW>(lds + (cur ^ 1) * C::STAGE, tid, kreg, vreg);
+        __syncthreads();
+    }
+
+    // ---- finalise: O / l, bf16, store (lane holds d = 32 db + 8 g + 4 hh + 0..3)
+    const float l = swap_sum(lsum);
+    const float inv = 1.f / l;
+    if (qi < T) {
+        bf16* orow = a.out + off + qi * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = (bf16)(o[db][4 * g + e] * inv);
+                *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g + 4 * hh) = w;
+            }
+    }
+}
+
+template <int D, int NW>
+hipError_t launch(const bf16* q, const bf16* k, const bf16* v, bf16* out, int64_t B,
+                  int64_t H, int64_t T, int64_t W, hipStream_t stream) {
+    using C = Cfg<D, NW>;
+    static bool attr_set = false;   // per process; the attribute is per function
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<D, NW>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           C::LDS_BYTES);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    Args a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.T = T;
+    a.W = W;
+    a.nqt = (int)((T + C::BM - 1) / C::BM);
+    const int64_t nblocks = B * H * a.nqt;
+    a.nblocks = (int)nblocks;
+    a.remap = (nblocks % 8 == 0) ? 1 : 0;
+    a.c = kLog2e / sqrtf((float)D);
+    void* args[] = {(void*)&a};
+    return hipLaunchKernel((const void*)prefill_bf16_kernel<D, NW>, dim3((unsigned)nblocks),
+                           dim3(C::NT), args, C::LDS_BYTES, stream);
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const bf16* q, const bf16* k, const bf16* v, bf16* out,
+                               int64_t B, int64_t H, int64_t T, int D, int64_t W,
+                               hipStream_t stream) {
+    if (D == 128) return launch<128, 4>(q, k, v, out, B, H, T, W, stream);
+    return launch<64, 4>(q, k, v, out, B, H, T, W, stream);
+}
+
+}  // namespace swa

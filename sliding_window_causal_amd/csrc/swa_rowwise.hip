@@ -1,0 +1,160 @@
+// Wavefront-per-row band attention: the fp32 path (any 1 <= D <= 256) and
+// the fallback for shapes the bf16 fast kernels do not cover.
+//
+// One 64-lane wavefront owns one output row and walks only that row's
+// visible keys, 64 at a time: lane j scores key c0 + j, the chunk max and
+// sum are wave reductions, and the running max / sum of an online softmax
+// rescale the output accumulator between chunks (lanes own output columns
+// d = lane + 64 r).  For prefill the visible keys of query i are
+// [max(0, i - W + 1), i] ("27. Sliding-Window Attention", step 2); for decode
+// they are the occupied ring slots [0, min(pos + 1, W)).  Scores are the
+// fp32 dot product times 1/sqrt(D); the exponent argument is s - m with both
+// terms in the same (unscaled) units, so W = 1 yields exactly v.
+
+#include "swa_internal.h"
+
+namespace swa {
+namespace {
+
+constexpr int kRowMaxD = 256;
+constexpr int kRowDPL = kRowMaxD / 64;
+
+__device__ inline float to_f32(float x) { return x; }
+__device__ inline float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ inline T from_f32(float x);
+template <> __device__ inline float from_f32<float>(float x) { return x; }
+template <> __device__ inline bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+__device__ inline float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// Attend query row `qrow` to keys [kbeg, kend) of the [*, D] matrices K, V.
+template <typename T>
+__device__ void attend_row(const T* __restrict__ qrow, const T* __restrict__ K,
+                           const T* __restrict__ V, int64_t kbeg, int64_t kend, int D,
+                           float scale, T* __restrict__ orow) {
+    __shared__ float qs[kRowMaxD];
+    __shared__ float ps[64];
+    const int lane = threadIdx.x;
+    for (int d = lane; d < D; d += 64) qs[d] = to_f32(qrow[d]);
+    __syncthreads();
+
+    float m = -__builtin_inff();
+    float l = 0.f;
+    float o[kRowDPL];
+#pragma unroll
+    for (int r = 0; r < kRowDPL; ++r) o[r] = 0.f;
+
+    for (int64_t c0 = kbeg; c0 < kend; c0 += 64) {
+        const int64_t j = c0 + lane;
+        const bool valid = j < kend;
+        float s = -__builtin_inff();
+        if (valid) {
+            const T* kr = K + j * (int64_t)D;
+            float acc = 0.f;
+            for (int d = 0; d < D; ++d) acc = fmaf(qs[d], to_f32(kr[d]), acc);
+            s = acc * scale;
+        }
+        const float m_new = fmaxf(m, wave_max(s));   // finite: key c0 is valid
+        const float alpha = expf(m - m_new);          // 0 on the first chunk
+        const float p = valid ? expf(s - m_new) : 0.f;
+        l = l * alpha + wave_sum(p);
+        ps[lane] = p;
+        __syncthreads();
+        const int nk = (int)((kend - c0) < 64 ? (kend - c0) : 64);
+#pragma unroll
+        for (int r = 0; r < kRowDPL; ++r) {
+            const int d = lane + 64 * r;
+            if (d < D) {
+                float acc = o[r] * alpha;
+                const T* vc = V + c0 * (int64_t)D + d;
+                for (int jj = 0; jj < nk; ++jj) acc = fmaf(ps[jj], to_f32(vc[(int64_t)jj * D]), acc);
+                o[r] = acc;
+            }
+        }
+        m = m_new;
+        __syncthreads();
+    }
+    const float inv = kend > kbeg ? 1.f / l : 0.f;
+#pragma unroll
+    for (int r = 0; r < kRowDPL; ++r) {
+        const int d = lane + 64 * r;
+        if (d < D) orow[d] = from_f32<T>(o[r] * inv);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void rowwise_prefill_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    T* __restrict__ out, int64_t Tn, int D, int64_t W, float scale) {
+    const int64_t row = blockIdx.x;            // (b*H + h)*T + i
+    const int64_t bh = row / Tn;
+    const int64_t i = row - bh * Tn;
+    const int64_t base = bh * Tn * D;
+    const int64_t kbeg = i - W + 1 > 0 ? i - W + 1 : 0;
+    attend_row<T>(q + base + i * D, k + base, v + base, kbeg, i + 1, D, scale,
+                  out + base + i * D);
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void rowwise_decode_kernel(
+    const T* __restrict__ q, const T* __restrict__ kring, const T* __restrict__ vring,
+    const int64_t* __restrict__ pos, T* __restrict__ out, int64_t H, int D, int64_t W,
+    float scale) {
+    const int64_t sh = blockIdx.x;             // s*H + h
+    const int64_t s = sh / H;
+    const int64_t p = pos[s];
+    int64_t n = p + 1;
+    n = n < 0 ? 0 : (n > W ? W : n);
+    const int64_t rbase = sh * W * D;
+    attend_row<T>(q + sh * D, kring + rbase, vring + rbase, 0, n, D, scale, out + sh * D);
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_rowwise_prefill(const T* q, const T* k, const T* v, T* out, int64_t B,
+                                  int64_t H, int64_t Tn, int D, int64_t W,
+                                  hipStream_t stream) {
+    const int64_t rows = B * H * Tn;
+    float scale = 1.0f / sqrtf((float)D);
+    void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&out, (void*)&Tn,
+                    (void*)&D, (void*)&W, (void*)&scale};
+    return hipLaunchKernel((const void*)rowwise_prefill_kernel<T>, dim3((unsigned)rows),
+                           dim3(64), args, 0, stream);
+}
+
+template <typename T>
+hipError_t launch_rowwise_decode(const T* q, const T* kring, const T* vring,
+                                 const int64_t* pos, T* out, int64_t S, int64_t H, int D,
+                                 int64_t W, hipStream_t stream) {
+    const int64_t rows = S * H;
+    float scale = 1.0f / sqrtf((float)D);
+    void* args[] = {(void*)&q, (void*)&kring, (void*)&vring, (void*)&pos, (void*)&out,
+                    (void*)&H, (void*)&D, (void*)&W, (void*)&scale};
+    return hipLaunchKernel((const void*)rowwise_decode_kernel<T>, dim3((unsigned)rows),
+                           dim3(64), args, 0, stream);
+}
+
+template hipError_t launch_rowwise_prefill<float>(const float*, const float*, const float*,
+                                                  float*, int64_t, int64_t, int64_t, int,
+                                                  int64_t, hipStream_t);
+template hipError_t launch_rowwise_prefill<bf16>(const bf16*, const bf16*, const bf16*, bf16*,
+                                                 int64_t, int64_t, int64_t, int, int64_t,
+                                                 hipStream_t);
+template hipError_t launch_rowwise_decode<float>(const float*, const float*, const float*,
+                                                 const int64_t*, float*, int64_t, int64_t,
+                                                 int, int64_t, hipStream_t);
+template hipError_t launch_rowwise_decode<bf16>(const bf16*, const bf16*, const bf16*,
+                                                const int64_t*, bf16*, int64_t, int64_t, int,
+                                                int64_t, hipStream_t);
+
+}  // namespace swa

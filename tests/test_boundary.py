@@ -1,0 +1,132 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every symbol that
+include/swa.h declares, and rejects bad arguments with the documented status
+codes before any HIP call (so no GPU is touched).  The Python binding rejects
+bad tensors before reaching the library."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import sliding_window_causal_amd as swa
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "swa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(swa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = _declared_functions()
+    for n in ("swa_forward", "swa_decode", "swa_ring_append", "swa_status_string",
+              "swa_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = swa.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_exported_symbols_are_c_linkage():
+    out = os.popen(f"nm -D --defined-only {swa.LIB_PATH}").read()
+    exported = set(re.findall(r"\b(swa_[a-z_0-9]+)\b", out))
+    assert set(_declared_functions()) <= exported
+
+
+def test_abi_version_and_status_strings():
+    assert swa.abi_version() == 1
+    for code in (swa.SWA_OK, swa.SWA_ERR_INVALID_ARG, swa.SWA_ERR_UNSUPPORTED,
+                 swa.SWA_ERR_LAUNCH, 99):
+        s = swa.status_string(code)
+        assert isinstance(s, str) and s
+
+
+DUMMY = ctypes.c_void_p(0x1000)   # never dereferenced: every case below fails validation
+
+
+def _fwd(q=DUMMY, k=DUMMY, v=DUMMY, o=DUMMY, B=1, H=1, T=8, D=64, W=4, dt=swa.SWA_BF16):
+    return swa.lib().swa_forward(q, k, v, o, B, H, T, D, W, dt, None)
+
+
+def _dec(q=DUMMY, kr=DUMMY, vr=DUMMY, pos=DUMMY, o=DUMMY, S=1, H=1, D=64, W=4, dt=swa.SWA_BF16):
+    return swa.lib().swa_decode(q, kr, vr, pos, o, S, H, D, W, dt, None)
+
+
+def _app(kn=DUMMY, vn=DUMMY, kr=DUMMY, vr=DUMMY, pos=DUMMY, S=1, H=1, D=64, W=4, dt=swa.SWA_BF16):
+    return swa.lib().swa_ring_append(kn, vn, kr, vr, pos, S, H, D, W, dt, None)
+
+
+@pytest.mark.parametrize("kw", [dict(q=None), dict(k=None), dict(v=None), dict(o=None),
+                                dict(B=0), dict(H=0), dict(T=0), dict(D=0), dict(W=0),
+                                dict(W=-3), dict(T=-1)])
+def test_forward_invalid_args(kw):
+    assert _fwd(**kw) == swa.SWA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(dt=7), dict(dt=-1), dict(D=96), dict(D=256),
+                                dict(D=32), dict(dt=swa.SWA_F32, D=257)])
+def test_forward_unsupported(kw):
+    assert _fwd(**kw) == swa.SWA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(q=None), dict(kr=None), dict(vr=None), dict(pos=None),
+                                dict(o=None), dict(S=0), dict(H=0), dict(D=0), dict(W=0)])
+def test_decode_invalid_args(kw):
+    assert _dec(**kw) == swa.SWA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(dt=3), dict(D=80), dict(dt=swa.SWA_F32, D=300)])
+def test_decode_unsupported(kw):
+    assert _dec(**kw) == swa.SWA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(kn=None), dict(vn=None), dict(kr=None), dict(vr=None),
+                                dict(pos=None), dict(S=0), dict(W=0), dict(D=0)])
+def test_append_invalid_args(kw):
+    assert _app(**kw) == swa.SWA_ERR_INVALID_ARG
+
+
+def test_append_unsupported_dtype():
+    assert _app(dt=5) == swa.SWA_ERR_UNSUPPORTED
+
+
+def test_oversized_grid_is_unsupported():
+    assert _fwd(B=1 << 20, H=1 << 10, T=1 << 10, D=64) == swa.SWA_ERR_UNSUPPORTED
+
+
+# ---- Python-level checks (no library call is reached) ----------------------
+
+def test_binding_rejects_cpu_tensors():
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        swa.swa_forward(x, x, x, x.clone(), 4)
+
+
+@pytest.mark.parametrize("W,exc", [(0, ValueError), (-1, ValueError), (True, TypeError),
+                                   (2.0, TypeError)])
+def test_binding_rejects_bad_window(W, exc):
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(exc):
+        swa.swa_forward(x, x, x, x.clone(), W)
+
+
+def test_error_is_raised_with_status():
+    err = swa.SWAError(swa.SWA_ERR_UNSUPPORTED, swa.status_string(swa.SWA_ERR_UNSUPPORTED))
+    assert err.status == swa.SWA_ERR_UNSUPPORTED and "unsupported" in str(err)
+
+
+def test_product_package_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "sliding_window_causal_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.replace("no fallback", ""), f

@@ -1,0 +1,351 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bars (written in each test):
+  fp32 inputs  max |gpu - oracle| <= 1e-5
+  bf16 inputs  |gpu - oracle| <= 2e-2 + 1e-2 |oracle| elementwise
+  bitwise      out-of-window corruption (finite values), W = 1 (out == v),
+               the integer worked example, determinism across runs
+The oracle always receives exactly the values the GPU received (bf16 inputs
+upcast exactly).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import sliding_window_causal_amd as swa
+import swa_inputs as si
+from conftest import read_golden
+from oracle import swa_oracle as so
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+F32_ATOL = 1e-5
+BF_ATOL, BF_RTOL = 2e-2, 1e-2
+
+
+def npy(t):
+    return t.detach().float().cpu().numpy()
+
+
+def assert_close(gpu, ref, dtype, what=""):
+    g = npy(gpu).astype(np.float64)
+    assert np.all(np.isfinite(g)), f"non-finite output {what}"
+    err = np.abs(g - ref)
+    if dtype == torch.float32:
+        assert err.max() <= F32_ATOL, f"{what}: max abs err {err.max():.3e}"
+    else:
+        bound = BF_ATOL + BF_RTOL * np.abs(ref)
+        worst = np.argmax(err - bound)
+        assert np.all(err <= bound), (
+            f"{what}: err {err.flat[worst]:.3e} > bound {bound.flat[worst]:.3e} "
+            f"(max abs err {err.max():.3e})")
+
+
+def run_fwd(q, k, v, W):
+    out = swa.sliding_window_attention(q, k, v, W)
+    torch.cuda.synchronize()
+    return out
+
+
+def _masks():
+    res = []
+    for name in ("mask_8tok_w4.txt", "mask_5tok_w3.txt"):
+        lines = read_golden(name)
+        hdr = dict(t.split("=") for t in lines[0].split())
+        grid = lines[1:]
+        m = np.array([[c in ".1" for c in row] for row in grid])
+        res.append((int(hdr["T"]), int(hdr["W"]), m))
+    return res
+
+
+# ----------------------------------------------------------------------------
+# fp32 path: the small workload, its window sweep, the pages' examples
+# ----------------------------------------------------------------------------
+
+TINY = si.WORKLOADS["prefill_f32_b1_h2_t128_d64_w32"]
+
+
+@pytest.mark.parametrize("W", [TINY.W, *TINY.sweep])
+def test_f32_tiny_workload_and_window_sweep(W):
+    q, k, v = si.workload_qkv(TINY, DEV)
+    out = run_fwd(q, k, v, W)
+    ref = so.swa_dense(npy(q), npy(k), npy(v), W)
+    assert_close(out, ref, torch.float32, f"W={W}")
+
+
+@pytest.mark.parametrize("shape,W", [((1, 2, 6, 4), 3), ((1, 1, 5, 3), 2), ((1, 4, 16, 32), 4),
+                                     ((2, 3, 37, 1), 5), ((1, 2, 200, 256), 70),
+                                     ((3, 1, 65, 17), 64), ((1, 1, 1, 8), 1)])
+def test_f32_page_shapes_and_odd_head_sizes(shape, W):
+    q, k, v = si.prefill_qkv(*shape, dtype=torch.float32, seed=7, device=DEV)
+    out = run_fwd(q, k, v, W)
+    assert out.shape == q.shape
+    assert_close(out, so.swa_dense(npy(q), npy(k), npy(v), W), torch.float32, str(shape))
+
+
+def test_f32_three_dim_input_is_one_head():
+    """P2's (batch, seq, dim) layout through the binding."""
+    g = si.generator(8, DEV)
+    q, k, v = (si.normal((1, 5, 3), g, torch.float32, DEV) for _ in range(3))
+    out = run_fwd(q, k, v, 2)
+    assert out.shape == (1, 5, 3)
+    assert_close(out, so.swa_dense(npy(q), npy(k), npy(v), 2), torch.float32)
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.float32, 8), (torch.bfloat16, 64)])
+def test_mask_probe_reproduces_printed_masks(dtype, D):
+    """q = k = 0, v = one-hot rows: out[i, j] > 0 exactly on visible keys."""
+    for T, W, m in _masks():
+        z = torch.zeros(1, 1, T, D, dtype=dtype, device=DEV)
+        v = torch.zeros(1, 1, T, D, dtype=dtype, device=DEV)
+        v[0, 0, torch.arange(T), torch.arange(T)] = 1
+        out = npy(run_fwd(z, z, v, W))[0, 0, :, :T]
+        assert np.array_equal(out > 0, m), f"T={T} W={W}"
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.float32, 7), (torch.float32, 64),
+                                     (torch.bfloat16, 64), (torch.bfloat16, 128)])
+def test_window_one_returns_v_exactly(dtype, D):
+    q, k, v = si.prefill_qkv(2, 3, 150, D, dtype=dtype, seed=9, device=DEV)
+    out = run_fwd(q, k, v, 1)
+    assert torch.equal(out, v)
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.float32, 1), (torch.bfloat16, 64)])
+def test_p5_worked_example(dtype, D):
+    lines = read_golden("p5_moving_average.txt")
+    W = int(lines[0].split("=")[1])
+    x = np.array([[float(t) for t in ln.split()] for ln in lines[lines.index("x") + 1:lines.index("out")]])
+    exp = np.array([[float(t) for t in ln.split()]
+                    for ln in lines[lines.index("out") + 1:lines.index("corrupt_row0")]])
+    T = x.shape[0]
+    z = torch.zeros(1, 2, T, D, dtype=dtype, device=DEV)
+    v = torch.zeros(1, 2, T, D, dtype=dtype, device=DEV)
+    v[0, :, :, 0] = torch.tensor(x.T, dtype=dtype)
+    out = npy(run_fwd(z, z, v, W))[0, :, :, 0].T
+    assert np.array_equal(out, exp)
+    v2 = v.clone()
+    v2[0, :, 0, 0] = torch.tensor([100.0, 200.0], dtype=dtype)
+    out2 = npy(run_fwd(z, z, v2, W))[0, :, :, 0].T
+    assert np.array_equal(out2[3:], out[3:])
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.float32, 64), (torch.bfloat16, 64), (torch.bfloat16, 128)])
+def test_zero_qk_is_trailing_moving_average(dtype, D):
+    g = si.generator(10, DEV)
+    T, W = 300, 37
+    v = si.normal((1, 2, T, D), g, dtype, DEV)
+    z = torch.zeros_like(v)
+    out = run_fwd(z, z, v, W)
+    vv = npy(v).astype(np.float64)
+    C = np.concatenate([np.zeros((1, 2, 1, D)), np.cumsum(vv, axis=2)], axis=2)
+    lo = np.maximum(0, np.arange(T) - W + 1)
+    n = (np.arange(T) - lo + 1)[None, None, :, None]
+    ref = (C[:, :, np.arange(T) + 1] - C[:, :, lo]) / n
+    assert_close(out, ref, dtype)
+
+
+# ----------------------------------------------------------------------------
+# bf16 MFMA path at oracle-friendly sizes: tiles, ragged tails, windows
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T,W", [(1, 1), (2, 5), (63, 7), (65, 64), (127, 3), (129, 128),
+                                 (333, 17), (333, 100), (333, 333), (333, 1000), (520, 129),
+                                 (700, 256), (1000, 1)])
+def test_bf16_prefill_vs_dense_oracle(T, W, D):
+    q, k, v = si.prefill_qkv(2, 3, T, D, dtype=torch.bfloat16, seed=T * 31 + W, device=DEV)
+    out = run_fwd(q, k, v, W)
+    ref = so.swa_dense(npy(q), npy(k), npy(v), W)
+    assert_close(out, ref, torch.bfloat16, f"T={T} W={W} D={D}")
+
+
+def test_bf16_scaled_inputs_stay_within_tolerance():
+    """Larger logits (q, k ~ N(0, 3^2)) exercise the running-max rescale."""
+    q, k, v = si.prefill_qkv(1, 4, 600, 128, dtype=torch.float32, seed=12, device=DEV)
+    q, k, v = (3 * q).bfloat16(), (3 * k).bfloat16(), v.bfloat16()
+    out = run_fwd(q, k, v, 200)
+    assert_close(out, so.swa_dense(npy(q), npy(k), npy(v), 200), torch.bfloat16)
+
+
+# ----------------------------------------------------------------------------
+# Bitwise invariants
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,D,T,W", [(torch.float32, 64, 300, 50),
+                                         (torch.bfloat16, 128, 700, 100),
+                                         (torch.bfloat16, 128, 700, 64),
+                                         (torch.bfloat16, 64, 520, 129)])
+def test_out_of_window_corruption_is_bitwise_invisible(dtype, D, T, W):
+    """Corrupt k and v at j0 with large finite values: every row outside
+    [j0, j0 + W - 1] is bit-identical, including row j0 + W (the sharp lower
+    edge) and row j0 - 1 (the causal edge); rows inside change."""
+    q, k, v = si.prefill_qkv(1, 2, T, D, dtype=dtype, seed=13, device=DEV)
+    base = run_fwd(q, k, v, W)
+    for j0 in (0, 63, 64, 127, 128, 200, T - W - 1):
+        k2, v2 = k.clone(), v.clone()
+        k2[:, :, j0] = 30.0
+        v2[:, :, j0] = -1000.0
+        out = run_fwd(q, k2, v2, W)
+        for i in range(T):
+            same = torch.equal(out[:, :, i], base[:, :, i])
+            inside = j0 <= i <= j0 + W - 1
+            assert same != inside, f"j0={j0} row={i} inside={inside} same={same}"
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.float32, 64), (torch.bfloat16, 128)])
+def test_lower_edge_is_w_keys_not_w_plus_one(dtype, D):
+    """q = k = 0 and one large value at i - W: a window of W + 1 keys would
+    move row i by about 1e3 / (W + 1)."""
+    T = 600
+    for W in (64, 100, 256):
+        v = torch.zeros(1, 1, T, D, dtype=dtype, device=DEV)
+        z = torch.zeros_like(v)
+        i = T - 1
+        v[0, 0, i - W] = 1000.0
+        out = npy(run_fwd(z, z, v, W))
+        assert np.all(out[0, 0, i] == 0.0)
+        assert np.all(out[0, 0, i - 1] > 1000.0 / (W + 1) * 0.9)
+
+
+def test_determinism_bitwise():
+    q, k, v = si.prefill_qkv(2, 8, 1000, 128, dtype=torch.bfloat16, seed=14, device=DEV)
+    a = run_fwd(q, k, v, 300)
+    b = run_fwd(q, k, v, 300)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.float32, 64), (torch.bfloat16, 128)])
+def test_output_guard_canaries(dtype, D):
+    """Writes stay inside out: canary regions on both sides are untouched."""
+    B, H, T, W = 1, 3, 200, 50
+    q, k, v = si.prefill_qkv(B, H, T, D, dtype=dtype, seed=15, device=DEV)
+    n = B * H * T * D
+    pad = 4096
+    buf = torch.full((n + 2 * pad,), 123.0, dtype=dtype, device=DEV)
+    out = buf[pad:pad + n].view(B, H, T, D)
+    swa.swa_forward(q, k, v, out, W)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == 123.0) and torch.all(buf[pad + n:] == 123.0)
+    assert_close(out, so.swa_dense(npy(q), npy(k), npy(v), W), dtype)
+
+
+# ----------------------------------------------------------------------------
+# Full-size workloads, sampled rows
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["prefill_bf16_b1_h32_t8192_d128_w4096",
+                                  "prefill_bf16_b8_h32_t4096_d128_w1024",
+                                  "prefill_bf16_b1_h32_t65536_d128_w4096"])
+def test_full_size_prefill_sampled_rows(name):
+    w = si.WORKLOADS[name]
+    q, k, v = si.workload_qkv(w, DEV)
+    out = run_fwd(q, k, v, w.W)
+    rows = si.sample_rows(w.T, w.W, n_random=24, seed=w.seed)
+    for b in range(w.B):
+        qb, kb, vb = npy(q[b]), npy(k[b]), npy(v[b])
+        rb = rows if b == 0 else rows[::6]
+        ref = so.swa_rows(qb, kb, vb, w.W, rb)
+        got = out[b][:, torch.as_tensor(rb, device=DEV)]
+        assert_close(got, ref, torch.bfloat16, f"{name} b={b}")
+        del qb, kb, vb
+    # two (b, h) pairs checked on every row
+    for b, h in ((0, 0), (w.B - 1, w.H - 1)):
+        rr = np.arange(w.T) if w.T <= 8192 else np.arange(0, w.T, 7)
+        ref = so.swa_rows(npy(q[b, h]), npy(k[b, h]), npy(v[b, h]), w.W, rr)
+        assert_close(out[b, h][torch.as_tensor(rr, device=DEV)], ref, torch.bfloat16,
+                     f"{name} all rows of b={b} h={h}")
+
+
+# ----------------------------------------------------------------------------
+# Decode against the ring
+# ----------------------------------------------------------------------------
+
+def _ring_from_appends(kseq, vseq, pos, W):
+    """Fill rings with the GPU append kernel, token by token, leaving NaN in
+    the slots no token reaches (they must never be read)."""
+    S, H, T, D = kseq.shape
+    kr = torch.full((S, H, W, D), float("nan"), dtype=kseq.dtype, device=DEV)
+    vr = torch.full_like(kr, float("nan"))
+    for s in range(S):
+        for t in range(max(0, pos[s] - W + 1), pos[s] + 1):
+            tt = torch.tensor([t], dtype=torch.int64, device=DEV)
+            swa.swa_ring_append(kseq[s:s + 1, :, t].contiguous(), vseq[s:s + 1, :, t].contiguous(),
+                                kr[s:s + 1], vr[s:s + 1], tt)
+    torch.cuda.synchronize()
+    return kr, vr
+
+
+@pytest.mark.parametrize("dtype,D,W", [(torch.bfloat16, 128, 37), (torch.bfloat16, 64, 64),
+                                       (torch.float32, 128, 37), (torch.float32, 5, 9),
+                                       (torch.bfloat16, 128, 300)])
+def test_decode_matches_oracle_and_prefill_row(dtype, D, W):
+    S, H = 5, 3
+    T = 2 * W + 10
+    g = si.generator(16, DEV)
+    q, k, v = (si.normal((S, H, T, D), g, dtype, DEV) for _ in range(3))
+    pos = [0, W - 2, W - 1, W + 3, T - 1]     # empty-ish, partly filled, just full, wrapped
+    kr, vr = _ring_from_appends(k, v, pos, W)
+    qs = torch.stack([q[s, :, pos[s]] for s in range(S)]).contiguous()
+    out = swa.decode(qs, kr, vr, torch.as_tensor(pos, device=DEV))
+    torch.cuda.synchronize()
+    ref = np.stack([so.swa_rows(npy(q[s]), npy(k[s]), npy(v[s]), W, [pos[s]])[:, 0]
+                    for s in range(S)])
+    assert_close(out, ref, dtype, "decode vs oracle prefill row")
+    # oracle decode on the very ring contents the GPU wrote
+    ref2 = so.swa_decode(npy(qs), npy(kr), npy(vr), pos, W)
+    assert_close(out, ref2, dtype, "decode vs oracle decode")
+    # the GPU prefill row of the same sequence
+    pre = swa.sliding_window_attention(q, k, v, W)
+    torch.cuda.synchronize()
+    rows = torch.stack([pre[s, :, pos[s]] for s in range(S)])
+    assert_close(out, npy(rows).astype(np.float64), dtype, "decode vs gpu prefill row")
+
+
+def test_decode_window_one_returns_current_value():
+    S, H, D, W = 4, 2, 128, 1
+    q, kr, vr, pos = si.decode_inputs(S, H, D, W, torch.bfloat16, seed=17, device=DEV)
+    out = swa.decode(q, kr, vr, pos)
+    torch.cuda.synchronize()
+    assert torch.equal(out, vr[:, :, 0])
+
+
+def test_decode_large_window_fallback_path():
+    """W above the LDS-resident score limit goes through the row kernel."""
+    S, H, D, W = 2, 2, 128, 20000
+    q, kr, vr, pos = si.decode_inputs(S, H, D, W, torch.bfloat16, seed=18, device=DEV)
+    out = swa.decode(q, kr, vr, pos)
+    torch.cuda.synchronize()
+    ref = so.swa_decode(npy(q), npy(kr), npy(vr), pos.cpu().numpy(), W)
+    assert_close(out, ref, torch.bfloat16)
+
+
+def test_decode_negative_position_writes_zeros():
+    S, H, D, W = 2, 2, 128, 16
+    q, kr, vr, pos = si.decode_inputs(S, H, D, W, torch.bfloat16, seed=19, device=DEV)
+    pos = torch.tensor([-1, 3], dtype=torch.int64, device=DEV)
+    out = swa.decode(q, kr, vr, pos)
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0)
+    ref = so.swa_decode(npy(q[1:]), npy(kr[1:]), npy(vr[1:]), [3], W)
+    assert_close(out[1:], ref, torch.bfloat16)
+
+
+def test_full_size_decode_sampled_streams():
+    w = si.WORKLOADS["decode_bf16_s256_h32_d128_w4096"]
+    q, kr, vr, pos = si.decode_inputs(w.S, w.H, w.D, w.W, torch.bfloat16, w.seed, DEV)
+    out = swa.decode(q, kr, vr, pos)
+    torch.cuda.synchronize()
+    pos_h = pos.cpu().numpy()
+    assert np.all(pos_h > w.W)
+    streams = np.unique(np.concatenate([[0, 1, w.S - 1],
+                                        np.random.default_rng(w.seed).integers(0, w.S, 21)]))
+    for s in streams:
+        ref = so.swa_decode(npy(q[s:s + 1]), npy(kr[s:s + 1]), npy(vr[s:s + 1]), pos_h[s:s + 1], w.W)
+        assert_close(out[s:s + 1], ref, torch.bfloat16, f"stream {s}")
+    # determinism of the full launch
+    out2 = swa.decode(q, kr, vr, pos)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
