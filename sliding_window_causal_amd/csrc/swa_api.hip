@@ -49,7 +49,8 @@ int swa_forward(const void* q, const void* k, const void* v, void* out, int64_t 
     if (!fits(B, H, T, D) || B * H * T >= ((int64_t)1 << 31)) return SWA_ERR_UNSUPPORTED;
     hipStream_t st = (hipStream_t)stream;
     if (dtype == SWA_BF16) {
-        if (D == 64 || D == 128)
+        // the bf16 kernel indexes one (batch, head) slab with 32-bit offsets
+        if ((D == 64 || D == 128) && T * D < ((int64_t)1 << 31))
             return from_hip(swa::launch_prefill_bf16((const swa::bf16*)q, (const swa::bf16*)k,
                                                      (const swa::bf16*)v, (swa::bf16*)out, B, H, T,
                                                      (int)D, W, st));

@@ -44,7 +44,10 @@ struct Cfg {
     static constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
     static constexpr int KCHUNKS = BN * CPR;
     static constexpr int KPT = (KCHUNKS + NT - 1) / NT;
-    static constexpr int VITEMS = (BN / 4) * CPR;   // (4-key group, 8-d chunk) items
+    // V items: (4-key group g, 8-d chunk cc) with g fastest across lanes, so
+    // 16 consecutive lanes store one contiguous 128-byte run of a V^T row
+    // (no LDS bank conflicts) and load 64-byte runs of 16 key rows.
+    static constexpr int VITEMS = (BN / 4) * CPR;
     static constexpr int VPT = (VITEMS + NT - 1) / NT;
     static_assert(D == 64 || D == 128, "head size");
 };
@@ -54,8 +57,8 @@ struct Args {
     const bf16* k;
     const bf16* v;
     bf16* out;
-    int64_t T;
-    int64_t W;
+    int T;
+    int W;          // min(W, T)
     int nqt;        // query tiles per (b, h)
     int nblocks;    // grid size
     int remap;      // 1: spread consecutive logical tiles over one XCD
@@ -81,33 +84,33 @@ __device__ inline int vt_pos(int g) {
     return 16 * c16 + 8 * (gg & 1) + 4 * (gg >> 1);
 }
 
+// Global -> registers for key tile [k0, k0 + 64).  Rows past the sequence
+// are clamped to row T - 1: those keys lie above every valid query's
+// diagonal, so the band mask sends their scores to -inf and their values are
+// multiplied by an exact zero.  No branch, so the loads stay in flight while
+// the current tile is computed.
 template <int D, int NW>
 __device__ inline void load_tile(const bf16* __restrict__ Kbh, const bf16* __restrict__ Vbh,
-                                 int64_t k0, int64_t T, int tid, u32x4 (&kreg)[Cfg<D, NW>::KPT],
+                                 int k0, int Tm1, int tid, u32x4 (&kreg)[Cfg<D, NW>::KPT],
                                  u32x4 (&vreg)[Cfg<D, NW>::VPT][4]) {
     using C = Cfg<D, NW>;
 #pragma unroll
     for (int r = 0; r < C::KPT; ++r) {
         const int c = tid + r * C::NT;
-        kreg[r] = u32x4{0, 0, 0, 0};
-        if (c < C::KCHUNKS) {
-            const int64_t key = k0 + c / C::CPR;
-            if (key < T)
-                kreg[r] = *reinterpret_cast<const u32x4*>(Kbh + key * D + (c % C::CPR) * 8);
+        if (C::KCHUNKS % C::NT == 0 || c < C::KCHUNKS) {
+            const int key = min(k0 + c / C::CPR, Tm1);
+            kreg[r] = *reinterpret_cast<const u32x4*>(Kbh + key * D + (c % C::CPR) * 8);
         }
     }
 #pragma unroll
     for (int r = 0; r < C::VPT; ++r) {
         const int it = tid + r * C::NT;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vreg[r][e] = u32x4{0, 0, 0, 0};
-        if (it < C::VITEMS) {
-            const int g = it / C::CPR, cc = it % C::CPR;
+        if (C::VITEMS % C::NT == 0 || it < C::VITEMS) {
+            const int g = it % (C::BN / 4), cc = it / (C::BN / 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t key = k0 + 4 * g + e;
-                if (key < T)
-                    vreg[r][e] = *reinterpret_cast<const u32x4*>(Vbh + key * D + cc * 8);
+                const int key = min(k0 + 4 * g + e, Tm1);
+                vreg[r][e] = *reinterpret_cast<const u32x4*>(Vbh + key * D + cc * 8);
             }
         }
     }
@@ -123,28 +126,36 @@ __device__ inline void store_tile(bf16* __restrict__ stage, int tid,
 #pragma unroll
     for (int r = 0; r < C::KPT; ++r) {
         const int c = tid + r * C::NT;
-        if (c < C::KCHUNKS)
+        if (C::KCHUNKS % C::NT == 0 || c < C::KCHUNKS)
             *reinterpret_cast<u32x4*>(Ks + (c / C::CPR) * C::KSTR + (c % C::CPR) * 8) = kreg[r];
     }
 #pragma unroll
     for (int r = 0; r < C::VPT; ++r) {
         const int it = tid + r * C::NT;
-        if (it < C::VITEMS) {
-            const int g = it / C::CPR, cc = it % C::CPR;
+        if (C::VITEMS % C::NT == 0 || it < C::VITEMS) {
+            const int g = it % (C::BN / 4), cc = it / (C::BN / 4);
             bf16* dst = Vs + (cc * 8) * C::VSTR + vt_pos(g);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 // keys 4g..4g+3 of d = 8cc + 2j (low halves) and 8cc + 2j + 1
-                const uint32_t lo_e = __builtin_amdgcn_perm(vreg[r][1][j], vreg[r][0][j], 0x05040100u);
-                const uint32_t hi_e = __builtin_amdgcn_perm(vreg[r][3][j], vreg[r][2][j], 0x05040100u);
-                const uint32_t lo_o = __builtin_amdgcn_perm(vreg[r][1][j], vreg[r][0][j], 0x07060302u);
-                const uint32_t hi_o = __builtin_amdgcn_perm(vreg[r][3][j], vreg[r][2][j], 0x07060302u);
+                const uint32_t r0 = vreg[r][0][j], r1 = vreg[r][1][j];
+                const uint32_t r2 = vreg[r][2][j], r3 = vreg[r][3][j];
+                const uint32_t lo_e = __builtin_amdgcn_perm(r1, r0, 0x05040100u);
+                const uint32_t hi_e = __builtin_amdgcn_perm(r3, r2, 0x05040100u);
+                const uint32_t lo_o = __builtin_amdgcn_perm(r1, r0, 0x07060302u);
+                const uint32_t hi_o = __builtin_amdgcn_perm(r3, r2, 0x07060302u);
                 *reinterpret_cast<u32x2*>(dst + (2 * j) * C::VSTR) = u32x2{lo_e, hi_e};
                 *reinterpret_cast<u32x2*>(dst + (2 * j + 1) * C::VSTR) = u32x2{lo_o, hi_o};
             }
         }
     }
 }
+
+// Lazy rescale threshold, in log2 units: the reference max of a row is only
+// raised when a new score exceeds it by more than this, so probabilities stay
+// below 2^8 and the output accumulator is rarely rescaled.  The final O / l
+// is the same quotient whichever reference is used.
+constexpr float kRescaleLog2 = 8.0f;
 
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(Args a) {
@@ -162,121 +173,128 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int logical = a.remap ? (bid & 7) * (a.nblocks >> 3) + (bid >> 3) : bid;
     const int bh = logical / a.nqt;
     const int qt = a.nqt - 1 - (logical - bh * a.nqt);
-    const int64_t T = a.T, W = a.W;
-    const int64_t i0 = (int64_t)qt * C::BM;
+    const int T = a.T, W = a.W;        // W is clamped to T on the host (W >= T is causal)
+    const int i0 = qt * C::BM;
     const int64_t off = (int64_t)bh * T * D;
     const bf16* __restrict__ Qbh = a.q + off;
     const bf16* __restrict__ Kbh = a.k + off;
     const bf16* __restrict__ Vbh = a.v + off;
 
-    const int64_t qw0 = i0 + 32 * wave;            // this wave's first query
-    const int64_t qi = qw0 + lr;                   // this lane's query
+    const int qw0 = i0 + 32 * wave;                  // this wave's first query
+    const int qi = qw0 + lr;                         // this lane's query
     const bool wave_active = qw0 < T;
-    const int64_t wlo = qw0 - W + 1 > 0 ? qw0 - W + 1 : 0;       // wave's lowest visible key
-    const int64_t whi = qw0 + 32 < T ? qw0 + 32 : T;             // one past its highest
+    const int wlo = max(qw0 - W + 1, 0);             // wave's lowest visible key
+    const int whi = min(qw0 + 32, T);                // one past its highest
 
-    // Q^T operand: lane holds q[qi][16 dc + 8 hh .. + 7] for every 16-wide d chunk.
+    // Q^T operand: lane holds q[qi][16 dc + 8 hh .. + 7] for every 16-wide d
+    // chunk (rows past T read row T - 1; their outputs are never stored).
     bf16x8 qf[D / 16];
+    {
+        const bf16* qp = Qbh + min(qi, T - 1) * D + 8 * hh;
 #pragma unroll
-    for (int dc = 0; dc < D / 16; ++dc) {
-        if (qi < T)
-            qf[dc] = *reinterpret_cast<const bf16x8*>(Qbh + qi * D + 16 * dc + 8 * hh);
-        else
-            qf[dc] = bf16x8{};
+        for (int dc = 0; dc < D / 16; ++dc) qf[dc] = *reinterpret_cast<const bf16x8*>(qp + 16 * dc);
     }
 
-    const int64_t klo = i0 - W + 1 > 0 ? i0 - W + 1 : 0;
-    const int64_t khi = i0 + C::BM < T ? i0 + C::BM : T;
-    const int t0 = (int)(klo / C::BN);
-    const int t1 = (int)((khi + C::BN - 1) / C::BN);
+    const int klo = max(i0 - W + 1, 0);
+    const int khi = min(i0 + C::BM, T);
+    const int t0 = klo / C::BN;
+    const int t1 = (khi + C::BN - 1) / C::BN;
 
     f32x16 o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-    float m = -__builtin_inff();
-    float lsum = 0.f;
+    float m = -__builtin_inff();      // reference max (raw score units)
+    float lsum = 0.f;                 // this lane's half of the row sum
+    const float c = a.c;
+    const float tau = kRescaleLog2 / c;
 
     u32x4 kreg[C::KPT];
     u32x4 vreg[C::VPT][4];
-    load_tile<D, NW>(Kbh, Vbh, (int64_t)t0 * C::BN, T, tid, kreg, vreg);
+    load_tile<D, NW>(Kbh, Vbh, t0 * C::BN, T - 1, tid, kreg, vreg);
     store_tile<D, NW>(lds, tid, kreg, vreg);
+    // Everything loaded so far (Q fragments, first tile) has landed: the
+    // in-loop waits then only concern the prefetch of the next tile.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int t = t0; t < t1; ++t) {
         const int cur = (t - t0) & 1;
-        const bool more = t + 1 < t1;
-        if (more) load_tile<D, NW>(Kbh, Vbh, (int64_t)(t + 1) * C::BN, T, tid, kreg, vreg);
+        // Prefetch the next tile (the last iteration re-reads its own tile
+        // into the idle buffer, which keeps the loop free of branches).
+        load_tile<D, NW>(Kbh, Vbh, min(t + 1, t1 - 1) * C::BN, T - 1, tid, kreg, vreg);
 
-        const int64_t k0 = (int64_t)t * C::BN;
+        const int k0 = t * C::BN;
         if (wave_active && k0 < whi && k0 + C::BN > wlo) {
             const bf16* Ks = lds + cur * C::STAGE;
             const bf16* Vs = Ks + C::KTILE;
-            // ---- S^T = K Q^T for two 32-key blocks
-            f32x16 s[2];
+            // ---- S^T = K Q^T, two 32-key blocks; K fragments are read ahead
+            constexpr int NF = 2 * (D / 16);
+            const bf16* kp = Ks + lr * C::KSTR + 8 * hh;
+            bf16x8 kf[NF];
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                s[b] = f32x16{};
+            for (int f = 0; f < NF; ++f)
+                kf[f] = *reinterpret_cast<const bf16x8*>(kp + (f & 1) * 32 * C::KSTR + 16 * (f >> 1));
+            f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-                for (int dc = 0; dc < D / 16; ++dc) {
-                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
-                        Ks + (32 * b + lr) * C::KSTR + 16 * dc + 8 * hh);
-                    s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[dc], s[b], 0, 0, 0);
-                }
+            for (int dc = 0; dc < D / 16; ++dc) {
+                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[2 * dc], qf[dc], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[2 * dc + 1], qf[dc], s1, 0, 0, 0);
             }
-            // ---- band mask, only where the tile straddles an edge of this wave's band
+            // ---- band mask where the tile straddles an edge of this wave's band:
+            // key j is visible iff 0 <= qi - j < W (one unsigned compare)
             const bool interior = (k0 + C::BN - 1 <= qw0) && (qw0 + 31 - k0 < W);
             if (!interior) {
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int64_t key = k0 + 32 * b + 8 * (v >> 2) + 4 * hh + (v & 3);
-                        const bool ok = (key <= qi) && (qi - key < W);
-                        s[b][v] = ok ? s[b][v] : -__builtin_inff();
-                    }
-            }
-            // ---- online softmax
-            float mx = s[0][0];
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[b][v]);
-            mx = swap_max(mx);
-            const float m_new = fmaxf(m, mx);
-            const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f((m - m_use) * a.c);
-            const float mc = m_use * a.c;
-            float psum = 0.f;
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
+                const int base = qi - k0 - 4 * hh;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][v], a.c, -mc));
-                    s[b][v] = p;
-                    psum += p;
+                    const int kof = 8 * (v >> 2) + (v & 3);
+                    s0[v] = (unsigned)(base - kof) < (unsigned)W ? s0[v] : -__builtin_inff();
+                    s1[v] = (unsigned)(base - kof - 32) < (unsigned)W ? s1[v] : -__builtin_inff();
                 }
-            lsum = lsum * alpha + psum;
+            }
+            // ---- online softmax with a lazily raised reference max
+            float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-            m = m_new;
+            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
+            mx = swap_max(mx);
+            const bool raise = mx > m + tau;           // false while the row is fully masked
+            if (__any(raise)) {
+                // 1 for rows keeping their reference (also rows still fully
+                // masked, where m - m would be NaN); 0 when m = -inf.
+                const float alpha = raise ? __builtin_amdgcn_exp2f((m - mx) * c) : 1.f;
+                const float m_new = raise ? mx : m;
+                lsum *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+                m = m_new;
+            }
+            const float mc = m == -__builtin_inff() ? 0.f : m * c;
+            float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                s0[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[v], c, -mc));
+                s1[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[v], c, -mc));
+                ps[v & 3] += s0[v] + s1[v];
+            }
+            lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
             // ---- O^T += V^T P^T, four 16-key chunks
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int ch = 0; ch < 4; ++ch) {
+                const f32x16& sb = (ch >> 1) ? s1 : s0;
+                const int e0 = 8 * (ch & 1);
+                bf16x8 pf;
 #pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    bf16x8 pf;
+                for (int e = 0; e < 8; ++e) pf[e] = (bf16)sb[e0 + e];
+                const bf16* vp = Vs + lr * C::VSTR + 16 * ch + 8 * hh;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) pf[e] = (bf16)s[b][8 * c + e];
-#pragma unroll
-                    for (int db = 0; db < D / 32; ++db) {
-                        const bf16x8 va = *reinterpret_cast<const bf16x8*>(
-                            Vs + (32 * db + lr) * C::VSTR + 32 * b + 16 * c + 8 * hh);
-                        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf, o[db], 0, 0, 0);
-                    }
+                for (int db = 0; db < D / 32; ++db) {
+                    const bf16x8 va = *reinterpret_cast<const bf16x8*>(vp + 32 * db * C::VSTR);
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf, o[db], 0, 0, 0);
                 }
+            }
         }
 
-        if (more) store_tile<D, NW>(lds + (cur ^ 1) * C::STAGE, tid, kreg, vreg);
+        store_tile<D, NW>(lds + (cur ^ 1) * C::STAGE, tid, kreg, vreg);
         __syncthreads();
     }
 
@@ -284,7 +302,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const float l = swap_sum(lsum);
     const float inv = 1.f / l;
     if (qi < T) {
-        bf16* orow = a.out + off + qi * D;
+        bf16* orow = a.out + off + (int64_t)qi * D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -314,8 +332,8 @@ hipError_t launch(const bf16* q, const bf16* k, const bf16* v, bf16* out, int64_
     a.k = k;
     a.v = v;
     a.out = out;
-    a.T = T;
-    a.W = W;
+    a.T = (int)T;
+    a.W = (int)(W < T ? W : T);
     a.nqt = (int)((T + C::BM - 1) / C::BM);
     const int64_t nblocks = B * H * a.nqt;
     a.nblocks = (int)nblocks;
