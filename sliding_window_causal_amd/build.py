@@ -37,6 +37,15 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source additions.  The prefill kernel relies on no NaN semantics
+# (infinities are still honoured: masked scores are -inf); without
+# -fno-honor-nans every fmaxf of an MFMA result carries an extra
+# canonicalising instruction.
+EXTRA_FLAGS = {
+    "swa_prefill_bf16.hip": ["-fno-honor-nans"],
+}
+
+
 def hipcc() -> str:
     exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(exe):
@@ -66,7 +75,8 @@ def build(verbose: bool = False) -> str:
     objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
     jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")), 8)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = [ex.submit(_run, [cc, *HIPCC_FLAGS, "-c", s, "-o", o], verbose)
+        futs = [ex.submit(_run, [cc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(os.path.basename(s), []),
+                                 "-c", s, "-o", o], verbose)
                 for s, o in zip(srcs, objs)]
         for f in futs:
             f.result()

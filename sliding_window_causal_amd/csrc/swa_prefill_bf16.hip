@@ -1,55 +1,65 @@
 // Causal sliding-window attention prefill, bf16 in / bf16 out, fp32
 // accumulation, on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
 //
-// Band-only iteration.  A workgroup owns a tile of BM = 32 * NW consecutive
-// queries [i0, i0 + BM) of one (batch, head) and walks only the 64-key tiles
-// that intersect the tile's band [max(0, i0 - W + 1), min(T, i0 + BM)), so the
-// work is O(T * min(W, T) * D) and never the dense O(T^2 * D) of the masked
-// recipe ("NNX Sliding-Window Attention", A local mask is not a sparse
-// implementation).  Each wavefront owns 32 queries and additionally skips the
-// key tiles that miss its own band.  The band predicate j <= i and i - j < W
-// ("27. Sliding-Window Attention", step 2) is evaluated, as a select to -inf,
-// only on the tiles that straddle an edge of the wavefront's band.
+// Band-only iteration.  A workgroup owns BM = 32 * NW consecutive queries
+// [i0, i0 + BM) of one (batch, head) and walks only the 32-key tiles that
+// intersect their band [max(0, i0 - W + 1), min(T, i0 + BM)), so the work is
+// O(T * min(W, T) * D) rather than the dense O(T^2 * D) of the masked recipe
+// ("NNX Sliding-Window Attention", A local mask is not a sparse
+// implementation).  Each wavefront owns 32 queries and skips the key tiles
+// that miss its own band.  The band predicate j <= i and i - j < W
+// ("27. Sliding-Window Attention", step 2) is applied, as a select to -inf,
+// only on tiles that straddle an edge of the wavefront's band.
 //
-// Per wavefront and key tile (everything fp32 except the MFMA operands):
-//   S^T = K Q^T        32x32 output blocks: lane l holds query l % 32 and 16
-//                      keys of it, so row maxima and sums are mostly in-lane
-//                      plus one exchange with lane l ^ 32 (v_permlane32_swap)
-//   online softmax     running max m and sum l per query (exp2 with the
-//                      1/sqrt(D) * log2(e) scale folded into one FMA), the
-//                      output rescaled by exp2(m_old - m_new)
-//   O^T += V^T P^T     P^T goes from the S^T accumulator straight into the
-//                      B operand (converted to bf16, round to nearest even);
-//                      V^T comes from LDS, where V is stored transposed with
-//                      its keys permuted to match the accumulator's key order.
-// K and V^T tiles are staged in LDS, double buffered: the global loads of the
-// next tile are in flight while the current one is computed.
+// Per wavefront and key tile (fp32 everywhere except the MFMA operands):
+//   S^T = K Q^T      32x32 blocks: lane l holds query l % 32 and 16 of its
+//                    keys, so row max / sum are in-lane plus one exchange with
+//                    lane l ^ 32 (v_permlane32_swap).
+//   softmax          running reference max m and sum l per query; exp2 with
+//                    the scale 1/sqrt(D) * log2(e) folded into one FMA.  The
+//                    reference is raised, and O rescaled by exp2(m_old -
+//                    m_new), only when a row max grows by more than 2^8.
+//   O^T += V^T P^T   P^T goes from the S^T accumulator straight into the B
+//                    operand (bf16, round to nearest even); the row sum is
+//                    taken over those same bf16 weights (v_dot2 with ones).
+//                    V stays row-major in LDS; the key-contiguous A operand
+//                    comes from transposing LDS reads (ds_read_b64_tr_b16).
+//
+// Data movement: K and V tiles go HBM -> LDS directly (buffer loads with an
+// LDS destination; the hardware range check returns zeros past the sequence
+// end) through rings of PF + 1 slots, issued PF tiles ahead, with K one tile
+// ahead of V.  Iteration j therefore
+// issues S(j+1) = K(j+1) Q^T on the matrix cores while the vector ALUs run
+// the softmax of tile j, then O += V(j)^T P(j)^T.  The LDS layouts are XOR
+// swizzled on 16-byte chunks so every LDS read is bank-conflict free.
 
 #include "swa_internal.h"
 
 namespace swa {
 namespace {
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
 template <int D, int NW>
 struct Cfg {
     static constexpr int BM = 32 * NW;          // queries per workgroup
-    static constexpr int BN = 64;               // keys per tile
+    static constexpr int BN = 32;               // keys per tile
     static constexpr int NT = 64 * NW;          // threads
-    static constexpr int KSTR = D + 8;          // K tile row stride (elements), +16 B breaks bank aliasing
-    static constexpr int VSTR = BN + 8;         // V^T tile row stride (elements)
-    static constexpr int KTILE = BN * KSTR;     // elements
-    static constexpr int VTILE = D * VSTR;      // elements
-    static constexpr int STAGE = KTILE + VTILE; // elements per pipeline stage
-    static constexpr int LDS_BYTES = 2 * STAGE * 2;
-    static constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
-    static constexpr int KCHUNKS = BN * CPR;
-    static constexpr int KPT = (KCHUNKS + NT - 1) / NT;
-    // V items: (4-key group g, 8-d chunk cc) with g fastest across lanes, so
-    // 16 consecutive lanes store one contiguous 128-byte run of a V^T row
-    // (no LDS bank conflicts) and load 64-byte runs of 16 key rows.
-    static constexpr int VITEMS = (BN / 4) * CPR;
-    static constexpr int VPT = (VITEMS + NT - 1) / NT;
+    static constexpr int ROWB = D * 2;          // bytes per K / V row
+    static constexpr int TILEB = BN * ROWB;     // bytes per K or V tile
+    static constexpr int PF = 3;                // prefetch distance in tiles
+    static constexpr int R = PF + 1;            // LDS ring slots per matrix
+    static constexpr int LDS_BYTES = 2 * R * TILEB;
+    static constexpr int NLD_W = TILEB / 1024 / NW;   // 1-KiB LDS loads per wave per tile
+    // vmcnt that leaves the loads of the 2 PF - 2 most recent tile loads in
+    // flight (see the issue order in the kernel)
+    static constexpr int VM_WAIT = (2 * PF - 2) * NLD_W;
+    static_assert(VM_WAIT < 64, "vmcnt range");
     static_assert(D == 64 || D == 128, "head size");
+    static_assert((TILEB / 1024) % NW == 0, "tile loads split evenly over waves");
 };
 
 struct Args {
@@ -76,94 +86,146 @@ __device__ inline float swap_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Position, inside a 64-key V^T row, of tile key 4 g + r.  Within each
-// 16-key chunk the key offset 8 a + 4 h + r is stored at 8 h + 4 a + r, so
-// that lane half h reads its eight B-operand keys as one 16-byte vector.
-__device__ inline int vt_pos(int g) {
-    const int c16 = g >> 2, gg = g & 3;
-    return 16 * c16 + 8 * (gg & 1) + 4 * (gg >> 1);
+// K tile: 16-byte chunk c of row r is stored at chunk c ^ kswz(r), so the 16
+// lanes that read one chunk column of 16 consecutive rows (the S MFMA A
+// operand) touch 16 different bank groups.
+template <int D> __device__ inline int kswz(int row) {
+    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+// V tile: chunk c of row r is stored at c ^ vswz(r).  A transposing read
+// covers 4 consecutive rows x 32 bytes per 16 lanes; XOR with 4 (r & 3)
+// spreads the two 16-lane groups of a pass over 16 distinct chunks.
+template <int D> __device__ inline int vswz(int row) {
+    return D == 128 ? 4 * (row & 3) : 4 * (row & 1);
 }
 
-// Global -> registers for key tile [k0, k0 + 64).  Rows past the sequence
-// are clamped to row T - 1: those keys lie above every valid query's
-// diagonal, so the band mask sends their scores to -inf and their values are
-// multiplied by an exact zero.  No branch, so the loads stay in flight while
-// the current tile is computed.
-template <int D, int NW>
-__device__ inline void load_tile(const bf16* __restrict__ Kbh, const bf16* __restrict__ Vbh,
-                                 int k0, int Tm1, int tid, u32x4 (&kreg)[Cfg<D, NW>::KPT],
-                                 u32x4 (&vreg)[Cfg<D, NW>::VPT][4]) {
+// Buffer resource over rows [k0, T) of one (batch, head) slab: loads past
+// the sequence end return zeros.  Keys past the end lie above every valid
+// query's diagonal, so their scores are masked to -inf and their (zero)
+// values get weight 0.
+__device__ inline __amdgpu_buffer_rsrc_t rows_rsrc(const bf16* slab, int k0, int T, int D) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(slab + k0 * D), 0,
+                                            (T - k0) * D * 2, 0x00020000);
+}
+
+// One 16-byte-per-lane buffer load into LDS: lane l's 16 bytes land at
+// lds_base + 16 l (lds_base goes to M0).  Written as asm so the compiler
+// does not see an LDS write: otherwise it cannot tell later LDS reads of
+// other ring slots apart from the loads still streaming in and drains all
+// in-flight loads before them.  The kernel orders these loads itself
+// (counted vmcnt waits and a barrier before a slot is read).  No register
+// is written, so nothing is left in flight into a VGPR.
+__device__ inline void lds_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_base, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_base), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+__device__ inline uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Start the HBM -> LDS copy of one tile.  Load n of this wave writes tile
+// bytes [1024 n, 1024 n + 1024), lane l the 16 bytes at 1024 n + 16 l; it
+// fetches the chunk that the swizzle stores there.
+template <int D, int NW, bool IS_V>
+__device__ inline void dma_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t buf, int wave, int lane) {
     using C = Cfg<D, NW>;
 #pragma unroll
-    for (int r = 0; r < C::KPT; ++r) {
-        const int c = tid + r * C::NT;
-        if (C::KCHUNKS % C::NT == 0 || c < C::KCHUNKS) {
-            const int key = min(k0 + c / C::CPR, Tm1);
-            kreg[r] = *reinterpret_cast<const u32x4*>(Kbh + key * D + (c % C::CPR) * 8);
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < C::VPT; ++r) {
-        const int it = tid + r * C::NT;
-        if (C::VITEMS % C::NT == 0 || it < C::VITEMS) {
-            const int g = it % (C::BN / 4), cc = it / (C::BN / 4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int key = min(k0 + 4 * g + e, Tm1);
-                vreg[r][e] = *reinterpret_cast<const u32x4*>(Vbh + key * D + cc * 8);
-            }
-        }
+    for (int i = 0; i < C::NLD_W; ++i) {
+        const int n = wave * C::NLD_W + i;
+        const int p = n * 1024 + lane * 16;
+        const int row = p / C::ROWB;
+        const int phys = (p % C::ROWB) >> 4;
+        const int logical = phys ^ (IS_V ? vswz<D>(row) : kswz<D>(row));
+        lds_load16(rsrc, buf + n * 1024, row * C::ROWB + logical * 16);
     }
 }
 
-template <int D, int NW>
-__device__ inline void store_tile(bf16* __restrict__ stage, int tid,
-                                  const u32x4 (&kreg)[Cfg<D, NW>::KPT],
-                                  const u32x4 (&vreg)[Cfg<D, NW>::VPT][4]) {
-    using C = Cfg<D, NW>;
-    bf16* Ks = stage;
-    bf16* Vs = stage + C::KTILE;
+// S^T for a 32-key tile: s holds keys 8 (v/4) + 4 hh + v%4 of query lr
+// (v = register index).
+template <int D>
+__device__ inline void qk_tile(const char* Kt, const bf16x8 (&qf)[D / 16], int lr, int hh,
+                               int ksw, f32x16& s) {
+    const char* r0 = Kt + lr * (2 * D);
+    s = f32x16{};
 #pragma unroll
-    for (int r = 0; r < C::KPT; ++r) {
-        const int c = tid + r * C::NT;
-        if (C::KCHUNKS % C::NT == 0 || c < C::KCHUNKS)
-            *reinterpret_cast<u32x4*>(Ks + (c / C::CPR) * C::KSTR + (c % C::CPR) * 8) = kreg[r];
-    }
-#pragma unroll
-    for (int r = 0; r < C::VPT; ++r) {
-        const int it = tid + r * C::NT;
-        if (C::VITEMS % C::NT == 0 || it < C::VITEMS) {
-            const int g = it % (C::BN / 4), cc = it / (C::BN / 4);
-            bf16* dst = Vs + (cc * 8) * C::VSTR + vt_pos(g);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                // keys 4g..4g+3 of d = 8cc + 2j (low halves) and 8cc + 2j + 1
-                const uint32_t r0 = vreg[r][0][j], r1 = vreg[r][1][j];
-                const uint32_t r2 = vreg[r][2][j], r3 = vreg[r][3][j];
-                const uint32_t lo_e = __builtin_amdgcn_perm(r1, r0, 0x05040100u);
-                const uint32_t hi_e = __builtin_amdgcn_perm(r3, r2, 0x05040100u);
-                const uint32_t lo_o = __builtin_amdgcn_perm(r1, r0, 0x07060302u);
-                const uint32_t hi_o = __builtin_amdgcn_perm(r3, r2, 0x07060302u);
-                *reinterpret_cast<u32x2*>(dst + (2 * j) * C::VSTR) = u32x2{lo_e, hi_e};
-                *reinterpret_cast<u32x2*>(dst + (2 * j + 1) * C::VSTR) = u32x2{lo_o, hi_o};
-            }
-        }
+    for (int dc = 0; dc < D / 16; ++dc) {
+        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(r0 + (((2 * dc + hh) ^ ksw) << 4));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[dc], s, 0, 0, 0);
     }
 }
 
-// Lazy rescale threshold, in log2 units: the reference max of a row is only
-// raised when a new score exceeds it by more than this, so probabilities stay
-// below 2^8 and the output accumulator is rarely rescaled.  The final O / l
-// is the same quotient whichever reference is used.
+// Band mask of a tile starting at key k0: key j is visible to query qi iff
+// 0 <= qi - j < W (one unsigned compare).
+__device__ inline void mask_tile(f32x16& s, int qi, int k0, int hh, int W) {
+    const int base = qi - k0 - 4 * hh;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int kof = 8 * (v >> 2) + (v & 3);
+        s[v] = (unsigned)(base - kof) < (unsigned)W ? s[v] : -__builtin_inff();
+    }
+}
+
+__device__ inline void exp_block(f32x16& s, float c, float mc) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], c, -mc));
+}
+
+// Eight probabilities as the bf16 B operand; their sum is added to acc with
+// v_dot2 against ones, so l sums exactly the weights the MFMA applies.
+__device__ inline bf16x8 pack_p(const f32x16& s, int e0, float& acc) {
+    bf16x8 pf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf[e] = (bf16)s[e0 + e];
+    const u32x4 pw = __builtin_bit_cast(u32x4, pf);
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t w = pw[j];   // scalar copy: bit_cast of a vector element reads element 0
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, acc, false);
+    }
+    return pf;
+}
+
+// O^T += V^T P^T for the 16-key chunk ch.  Lane l (i = l % 16, group half
+// dh = (l / 16) % 2, hh = l / 32) needs, for d = 32 db + l % 32, the keys
+// 16 ch + 8 a + 4 hh + e (a = 0, 1; e = 0..3).  One ds_read_b64_tr_b16 over
+// the 16 lanes of a group hands lane i column (group base + i) of the 4 x 16
+// block whose row r0 + i/4, columns 4 (i % 4) .. + 3, lane i addresses.
+template <int D>
+__device__ inline void pv_chunk(const char* Vt, const bf16x8& pf, int ch, int lane,
+                                f32x16 (&o)[D / 32]) {
+    const int i = lane & 15, hh = lane >> 5, dh = (lane >> 4) & 1;
+    const int row = 16 * ch + 4 * hh + (i >> 2);           // + 8 a
+    const int vsw = vswz<D>(i >> 2);                        // row + 8 a keeps the swizzle
+    const char* rp = Vt + row * (2 * D) + 8 * (i & 1);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        const int chunk = (4 * db + 2 * dh + ((i & 3) >> 1)) ^ vsw;
+        const char* p0 = rp + (chunk << 4);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p0);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0 + 8 * 2 * D));
+        const i16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pf, o[db],
+                                                         0, 0, 0);
+    }
+}
+
+// Lazy rescale threshold in log2 units: probabilities stay below 2^8 and the
+// output accumulator is rarely rescaled.  O / l is the same quotient for any
+// reference.
 constexpr float kRescaleLog2 = 8.0f;
 
 template <int D, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(Args a) {
     using C = Cfg<D, NW>;
-    extern __shared__ __attribute__((aligned(16))) bf16 lds[];
-
+    // Tile t lives in slot (t - t0) % R of the K ring and of the V ring.
+    __shared__ __attribute__((aligned(1024))) char ring[2 * C::R * C::TILEB];
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS load bases go to M0
+    const int lane = tid & 63;
     const int lr = lane & 31, hh = lane >> 5;
 
     // Logical tile: consecutive logical tiles land on one XCD (the hardware
@@ -173,7 +235,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int logical = a.remap ? (bid & 7) * (a.nblocks >> 3) + (bid >> 3) : bid;
     const int bh = logical / a.nqt;
     const int qt = a.nqt - 1 - (logical - bh * a.nqt);
-    const int T = a.T, W = a.W;        // W is clamped to T on the host (W >= T is causal)
+    const int T = a.T, W = a.W;
     const int i0 = qt * C::BM;
     const int64_t off = (int64_t)bh * T * D;
     const bf16* __restrict__ Qbh = a.q + off;
@@ -182,23 +244,33 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     const int qw0 = i0 + 32 * wave;                  // this wave's first query
     const int qi = qw0 + lr;                         // this lane's query
-    const bool wave_active = qw0 < T;
-    const int wlo = max(qw0 - W + 1, 0);             // wave's lowest visible key
-    const int whi = min(qw0 + 32, T);                // one past its highest
+    const int klo = max(i0 - W + 1, 0);
+    const int khi = min(i0 + C::BM, T);
+    const int t0 = klo / C::BN;                      // workgroup's key tiles [t0, t1)
+    const int t1 = (khi + C::BN - 1) / C::BN;
+    int wt0 = t1, wt1 = t1;                          // this wave's key tiles [wt0, wt1)
+    if (qw0 < T) {
+        wt0 = max(qw0 - W + 1, 0) / C::BN;
+        wt1 = (min(qw0 + 32, T) + C::BN - 1) / C::BN;
+    }
+    auto needs = [&](int t) { return t >= wt0 && t < wt1; };
+    auto interior = [&](int t) {
+        const int k0 = t * C::BN;
+        return (k0 + C::BN - 1 <= qw0) && (qw0 + 31 - k0 < W);
+    };
 
-    // Q^T operand: lane holds q[qi][16 dc + 8 hh .. + 7] for every 16-wide d
-    // chunk (rows past T read row T - 1; their outputs are never stored).
+    // Q^T operand: q[qi][16 dc + 8 hh .. + 7] (rows past T read row T - 1;
+    // their outputs are never stored).
     bf16x8 qf[D / 16];
     {
         const bf16* qp = Qbh + min(qi, T - 1) * D + 8 * hh;
 #pragma unroll
         for (int dc = 0; dc < D / 16; ++dc) qf[dc] = *reinterpret_cast<const bf16x8*>(qp + 16 * dc);
     }
-
-    const int klo = max(i0 - W + 1, 0);
-    const int khi = min(i0 + C::BM, T);
-    const int t0 = klo / C::BN;
-    const int t1 = (khi + C::BN - 1) / C::BN;
+    // Land Q before any tile load is issued: the compiler's own waits for
+    // these registers would otherwise count (and drain) the tile loads.
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
+    const int ksw = kswz<D>(lr);
 
     f32x16 o[D / 32];
 #pragma unroll
@@ -208,95 +280,140 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const float c = a.c;
     const float tau = kRescaleLog2 / c;
 
-    u32x4 kreg[C::KPT];
-    u32x4 vreg[C::VPT][4];
-    load_tile<D, NW>(Kbh, Vbh, t0 * C::BN, T - 1, tid, kreg, vreg);
-    store_tile<D, NW>(lds, tid, kreg, vreg);
-    // Everything loaded so far (Q fragments, first tile) has landed: the
-    // in-loop waits then only concern the prefetch of the next tile.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    for (int t = t0; t < t1; ++t) {
-        const int cur = (t - t0) & 1;
-        // Prefetch the next tile (the last iteration re-reads its own tile
-        // into the idle buffer, which keeps the loop free of branches).
-        load_tile<D, NW>(Kbh, Vbh, min(t + 1, t1 - 1) * C::BN, T - 1, tid, kreg, vreg);
-
-        const int k0 = t * C::BN;
-        if (wave_active && k0 < whi && k0 + C::BN > wlo) {
-            const bf16* Ks = lds + cur * C::STAGE;
-            const bf16* Vs = Ks + C::KTILE;
-            // ---- S^T = K Q^T, two 32-key blocks; K fragments are read ahead
-            constexpr int NF = 2 * (D / 16);
-            const bf16* kp = Ks + lr * C::KSTR + 8 * hh;
-            bf16x8 kf[NF];
+    // ---- prologue.  Tile loads are issued in the order K(t0) V(t0) K(t0+1)
+    // V(t0+1) ... K(t0+PF-1) V(t0+PF-1) K(t0+PF), and then, in step j,
+    // V(j+PF) K(j+1+PF); tile indices past the band are clamped to its last
+    // tile (loaded into a free slot, never read), so every step issues the
+    // same number of loads and a fixed vmcnt waits for exactly the oldest.
+    auto kslot = [&](int t) { return ring + ((t - t0) % C::R) * C::TILEB; };
+    auto vslot = [&](int t) { return ring + (C::R + (t - t0) % C::R) * C::TILEB; };
+    auto load_k = [&](int t) {
+        dma_tile<D, NW, false>(rows_rsrc(Kbh, min(t, t1 - 1) * C::BN, T, D), lds_addr(kslot(t)),
+                               wave, lane);
+    };
+    auto load_v = [&](int t) {
+        dma_tile<D, NW, true>(rows_rsrc(Vbh, min(t, t1 - 1) * C::BN, T, D), lds_addr(vslot(t)),
+                              wave, lane);
+    };
+    // Publish loads: wait until at most VM_WAIT of this wave's loads are in
+    // flight and its LDS reads are done, then barrier.  No fence is needed:
+    // the only LDS writes are the tile loads, covered by the count.
+    auto publish = [&]() {
+        __builtin_amdgcn_s_waitcnt((C::VM_WAIT & 15) | ((C::VM_WAIT >> 4) << 14) | (7 << 4) | (0 << 8));
+        __builtin_amdgcn_s_barrier();
+    };
 #pragma unroll
-            for (int f = 0; f < NF; ++f)
-                kf[f] = *reinterpret_cast<const bf16x8*>(kp + (f & 1) * 32 * C::KSTR + 16 * (f >> 1));
-            f32x16 s0 = f32x16{}, s1 = f32x16{};
-#pragma unroll
-            for (int dc = 0; dc < D / 16; ++dc) {
-                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[2 * dc], qf[dc], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[2 * dc + 1], qf[dc], s1, 0, 0, 0);
-            }
-            // ---- band mask where the tile straddles an edge of this wave's band:
-            // key j is visible iff 0 <= qi - j < W (one unsigned compare)
-            const bool interior = (k0 + C::BN - 1 <= qw0) && (qw0 + 31 - k0 < W);
-            if (!interior) {
-                const int base = qi - k0 - 4 * hh;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int kof = 8 * (v >> 2) + (v & 3);
-                    s0[v] = (unsigned)(base - kof) < (unsigned)W ? s0[v] : -__builtin_inff();
-                    s1[v] = (unsigned)(base - kof - 32) < (unsigned)W ? s1[v] : -__builtin_inff();
-                }
-            }
-            // ---- online softmax with a lazily raised reference max
-            float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-            for (int v = 1; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
-            mx = swap_max(mx);
-            const bool raise = mx > m + tau;           // false while the row is fully masked
-            if (__any(raise)) {
-                // 1 for rows keeping their reference (also rows still fully
-                // masked, where m - m would be NaN); 0 when m = -inf.
-                const float alpha = raise ? __builtin_amdgcn_exp2f((m - mx) * c) : 1.f;
-                const float m_new = raise ? mx : m;
-                lsum *= alpha;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-                m = m_new;
-            }
-            const float mc = m == -__builtin_inff() ? 0.f : m * c;
-            float ps[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                s0[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[v], c, -mc));
-                s1[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[v], c, -mc));
-                ps[v & 3] += s0[v] + s1[v];
-            }
-            lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-            // ---- O^T += V^T P^T, four 16-key chunks
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
-                const f32x16& sb = (ch >> 1) ? s1 : s0;
-                const int e0 = 8 * (ch & 1);
-                bf16x8 pf;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pf[e] = (bf16)sb[e0 + e];
-                const bf16* vp = Vs + lr * C::VSTR + 16 * ch + 8 * hh;
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const bf16x8 va = *reinterpret_cast<const bf16x8*>(vp + 32 * db * C::VSTR);
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf, o[db], 0, 0, 0);
-                }
-            }
-        }
-
-        store_tile<D, NW>(lds + (cur ^ 1) * C::STAGE, tid, kreg, vreg);
-        __syncthreads();
+    for (int i = 0; i < C::PF; ++i) {
+        load_k(t0 + i);
+        load_v(t0 + i);
     }
+    load_k(t0 + C::PF);
+    publish();   // K(t0), V(t0), K(t0+1) have landed
+
+    // Reference update for a freshly computed (and masked) score tile: raise
+    // m if the tile's max exceeds it by more than 2^8 and rescale what has
+    // been accumulated so far.  Runs between tiles, outside the MFMA/VALU
+    // overlap regions.
+    auto update_ref = [&](const f32x16& s) {
+        float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+        for (int v = 2; v < 16; v += 2) mx = fmaxf(fmaxf(mx, s[v]), s[v + 1]);
+        mx = swap_max(mx);
+        const bool raise = mx > m + tau;               // false while the row is fully masked
+        if (__any(raise)) {
+            // 1 for rows keeping their reference (also rows still fully
+            // masked, where m - m would be NaN); 0 when m = -inf.
+            const float alpha = __builtin_amdgcn_exp2f(raise ? (m - mx) * c : 0.f);
+            m = raise ? mx : m;
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+        }
+    };
+
+    // Score tiles start finite: a wave computes (and discards) tiles outside
+    // its band, and their probabilities must come out as exact zeros.
+    f32x16 sA = f32x16{}, sB = f32x16{};
+    if (needs(t0)) {
+        qk_tile<D>(kslot(t0), qf, lr, hh, ksw, sA);
+        if (!interior(t0)) mask_tile(sA, qi, t0 * C::BN, hh, W);
+        update_ref(sA);
+    }
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8) | 15 | (3 << 14));   // LDS reads done
+    __builtin_amdgcn_s_barrier();   // every wave is done with K(t0) before its slot is reloaded
+
+    // ---- one key tile j: S(j+1) on the matrix cores alongside softmax(j)
+    auto body = [&](f32x16& sc, f32x16& sn, int j) {
+        // Slots released by the barrier that ended the previous step:
+        // V(j+PF) replaces V(j-1), K(j+1+PF) replaces K(j).
+        load_v(j + C::PF);
+        load_k(j + 1 + C::PF);
+        const bool nj = needs(j), nn = needs(j + 1);
+        const char* Kn = kslot(j + 1);
+        const char* Vc = vslot(j);
+
+        // Every wave runs every tile of the workgroup, so the accumulator
+        // path has no branches; a tile outside this wave's band gets
+        // mc = +inf and hence probabilities exp2(-inf) = 0 exactly.
+        {
+            const float mc = !nj ? __builtin_inff() : (m == -__builtin_inff() ? 0.f : m * c);
+            float ps = 0.f;
+            // The schedule is written out slice by slice; each sched_barrier
+            // closes a slice, so the MFMAs at the top of a slice run on the
+            // matrix core while the slice's (independent) vector ALU work
+            // issues behind them.
+            //
+            // Region A: S(j+1) = K(j+1) Q^T, one MFMA per 16-wide d slice, with
+            // the probabilities of keys 0..11 of tile j and the operand p0 of
+            // keys 0..15.  S(j+1) is computed even where this wave does not
+            // need it (at the end from a stale but finite buffer); it is then
+            // never used.
+            constexpr int ND = D / 16;
+            constexpr int NEA = 12;                 // exps issued in region A
+            bf16x8 p0, p1;
+            {
+                const char* r0 = Kn + lr * (2 * D);
+                sn = f32x16{};
+                bf16x8 ka = *reinterpret_cast<const bf16x8*>(r0 + ((hh ^ ksw) << 4));
+#pragma unroll
+                for (int dc = 0; dc < ND; ++dc) {
+                    bf16x8 na = ka;
+                    if (dc + 1 < ND)
+                        na = *reinterpret_cast<const bf16x8*>(r0 + (((2 * (dc + 1) + hh) ^ ksw) << 4));
+                    sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[dc], sn, 0, 0, 0);
+#pragma unroll
+                    for (int v = dc * NEA / ND; v < (dc + 1) * NEA / ND; ++v)
+                        sc[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], c, -mc));
+                    if (dc == ND - 1) p0 = pack_p(sc, 0, ps);
+                    ka = na;
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // Region B: O += V(j) P(j), two 16-key chunks of D/32 MFMAs, with
+            // the rest of the probabilities produced alongside chunk 0.
+            pv_chunk<D>(Vc, p0, 0, lane, o);
+#pragma unroll
+            for (int v = NEA; v < 16; ++v) sc[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], c, -mc));
+            p1 = pack_p(sc, 8, ps);
+            __builtin_amdgcn_sched_barrier(0);
+            pv_chunk<D>(Vc, p1, 1, lane, o);
+            lsum += ps;
+        }
+        if (nn) {
+            if (!interior(j + 1)) mask_tile(sn, qi, (j + 1) * C::BN, hh, W);
+            update_ref(sn);
+        }
+        publish();   // V(j+1) and K(j+2), needed by the next step, have landed
+    };
+
+    for (int j = t0;;) {
+        body(sA, sB, j);
+        if (++j >= t1) break;
+        body(sB, sA, j);
+        if (++j >= t1) break;
+    }
+
+    __builtin_amdgcn_s_waitcnt(0);   // no LDS load may outlive the workgroup
 
     // ---- finalise: O / l, bf16, store (lane holds d = 32 db + 8 g + 4 hh + 0..3)
     const float l = swap_sum(lsum);
@@ -319,14 +436,6 @@ template <int D, int NW>
 hipError_t launch(const bf16* q, const bf16* k, const bf16* v, bf16* out, int64_t B,
                   int64_t H, int64_t T, int64_t W, hipStream_t stream) {
     using C = Cfg<D, NW>;
-    static bool attr_set = false;   // per process; the attribute is per function
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<D, NW>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           C::LDS_BYTES);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
     Args a;
     a.q = q;
     a.k = k;
@@ -341,7 +450,7 @@ hipError_t launch(const bf16* q, const bf16* k, const bf16* v, bf16* out, int64_
     a.c = kLog2e / sqrtf((float)D);
     void* args[] = {(void*)&a};
     return hipLaunchKernel((const void*)prefill_bf16_kernel<D, NW>, dim3((unsigned)nblocks),
-                           dim3(C::NT), args, C::LDS_BYTES, stream);
+                           dim3(C::NT), args, 0, stream);
 }
 
 }  // namespace
