@@ -7,7 +7,7 @@ One step is one pass of the whole path over resident synthetic inputs:
   * one decode token for 256 independent streams, 32 heads, head size 128,
     against full 4096-slot bf16 rings (swa_decode).
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 20]
 
 Prints one JSON line.  ``value`` is the prefill's useful band TFLOP/s,
 4 * B * H * D * sum_i min(i + 1, W) flops per launch; the decode's KV GB/s
@@ -121,7 +121,9 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The GPU's clocks ramp up over the first ~50 ms of sustained matrix work;
+    # 20 steps (~70 ms) reach the plateau before timing starts.
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
                     help="profiling aid: run one kernel only (the JSON line is then partial)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
