@@ -126,6 +126,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
                     help="profiling aid: run one kernel only (the JSON line is then partial)")
+    ap.add_argument("--workload", default=PREFILL,
+                    help="prefill workload for --only prefill (the default step always uses the "
+                         "T=8192/W=4096 layer)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -161,7 +164,10 @@ def main() -> int:
                           "launches": args.warmup + args.steps}))
         return 0
 
-    wp = si.WORKLOADS[PREFILL]
+    if args.workload != PREFILL and args.only != "prefill":
+        print("--workload applies to --only prefill", file=sys.stderr)
+        return 2
+    wp = si.WORKLOADS[args.workload]
     wd = si.WORKLOADS[DECODE]
     do_p = args.only in ("all", "prefill")
     do_d = args.only in ("all", "decode")
@@ -217,7 +223,7 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{PREFILL} + {DECODE}" if args.only == "all" else
-                   (PREFILL if do_p else DECODE)},
+                   (wp.name if do_p else DECODE)},
     }
     if do_p:
         flops = prefill_flops(wp.B, wp.H, wp.T, wp.D, wp.W)

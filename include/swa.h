@@ -111,6 +111,41 @@ int swa_ring_append(const void* knew, const void* vnew, void* kring, void* vring
                     const int64_t* pos, int64_t S, int64_t H, int64_t D, int64_t W,
                     int dtype, void* stream);
 
+/*
+ * Chunked prefill continuing a stream held in a W-slot ring (the rolling
+ * buffer that "27. Sliding-Window Attention", Problem, names as the follow-up
+ * to the dense version; the bounded cache of "25. Sliding-Window Causal
+ * Attention for Streaming Inference", Problem).  C new tokens per stream sit
+ * at absolute positions pos0[s] .. pos0[s] + C - 1; the ring holds the
+ * stream's earlier tokens (pos0 - W, pos0) in slots p mod W (slots of
+ * negative positions are never read).  Query p attends to the tokens
+ * (p - W, p]: those before pos0 from the ring, the rest from the chunk, so
+ * the result equals prefill rows pos0 .. pos0 + C - 1 of the whole sequence.
+ *
+ *   q, kc, vc, out : [S, H, C, D]
+ *   kring, vring   : [S, H, W, D]  read only
+ *   pos0           : device int64[S], >= 0 (negative values are treated as 0)
+ *   dtype          : SWA_F32 or SWA_BF16, 1 <= D <= 256
+ * Append the chunk afterwards with swa_ring_append_chunk (the attention of
+ * the chunk still needs ring slots the append overwrites).
+ */
+int swa_chunk_forward(const void* q, const void* kc, const void* vc,
+                      const void* kring, const void* vring, const int64_t* pos0,
+                      void* out, int64_t S, int64_t H, int64_t C, int64_t D, int64_t W,
+                      int dtype, void* stream);
+
+/*
+ * Chunk append (not part of the timed path): the last min(C, W) tokens of
+ * the chunk, at positions pos0 + c, go to ring slots (pos0 + c) mod W.
+ *
+ *   kc, vc : [S, H, C, D];  kring, vring : [S, H, W, D]
+ *   pos0   : device int64[S], >= 0 (negative values are treated as 0)
+ *   dtype  : SWA_F32 or SWA_BF16, any D >= 1
+ */
+int swa_ring_append_chunk(const void* kc, const void* vc, void* kring, void* vring,
+                          const int64_t* pos0, int64_t S, int64_t H, int64_t C, int64_t D,
+                          int64_t W, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,9 +9,14 @@ Entry points (same names as the C ABI):
   swa_forward(q, k, v, out, window_size)        prefill, [B, H, T, D]
   swa_decode(q, kring, vring, pos, out)          decode against a W-slot ring
   swa_ring_append(knew, vnew, kring, vring, pos) write position pos into slot pos mod W
+  swa_chunk_forward(q, kc, vc, kring, vring, pos0, out)
+                                                 chunk of new tokens continuing a ring
+  swa_ring_append_chunk(kc, vc, kring, vring, pos0)
+                                                 write a chunk's tokens into the ring
 Conveniences that allocate the output with torch:
   sliding_window_attention(q, k, v, window_size) -> out
   decode(q, kring, vring, pos) -> out
+  chunk_attention(q, kc, vc, kring, vring, pos0) -> out
 """
 
 from __future__ import annotations
@@ -24,8 +29,8 @@ import torch
 __all__ = [
     "LIB_PATH", "SWA_F32", "SWA_BF16", "SWA_OK", "SWA_ERR_INVALID_ARG",
     "SWA_ERR_UNSUPPORTED", "SWA_ERR_LAUNCH", "SWAError", "lib", "abi_version",
-    "status_string", "swa_forward", "swa_decode", "swa_ring_append",
-    "sliding_window_attention", "decode",
+    "status_string", "swa_forward", "swa_decode", "swa_ring_append", "swa_chunk_forward",
+    "swa_ring_append_chunk", "sliding_window_attention", "decode", "chunk_attention",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa.so")
@@ -64,6 +69,10 @@ def lib() -> ctypes.CDLL:
     L.swa_decode.restype = i32
     L.swa_ring_append.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, p]
     L.swa_ring_append.restype = i32
+    L.swa_chunk_forward.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i32, p]
+    L.swa_chunk_forward.restype = i32
+    L.swa_ring_append_chunk.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i32, p]
+    L.swa_ring_append_chunk.restype = i32
     _lib = L
     return L
 
@@ -164,6 +173,45 @@ def swa_ring_append(knew, vnew, kring, vring, pos, stream=None) -> None:
     W = kring.shape[2]
     _check(lib().swa_ring_append(_ptr(knew), _ptr(vnew), _ptr(kring), _ptr(vring), _ptr(pos),
                                  S, H, D, W, code, _stream(knew, stream)))
+
+
+def _check_chunk(q, kc, vc, kring, vring, pos0):
+    if q.dim() != 4 or kc.shape != q.shape or vc.shape != q.shape:
+        raise ValueError("q, kc, vc must be [S, H, C, D] of one shape")
+    S, H, C, D = q.shape
+    if kring.dim() != 4 or vring.shape != kring.shape or kring.shape[0] != S or \
+            kring.shape[1] != H or kring.shape[3] != D:
+        raise ValueError("rings must be [S, H, W, D] matching the chunk")
+    if pos0.dtype != torch.int64 or pos0.shape != (S,):
+        raise ValueError("pos0 must be int64 [S]")
+    return S, H, C, D, kring.shape[2]
+
+
+def swa_chunk_forward(q, kc, vc, kring, vring, pos0, out, stream=None) -> None:
+    """Chunk continuation of a ring into ``out`` [S, H, C, D]; the ring is read only."""
+    _check_device(q, kc, vc, kring, vring, pos0, out)
+    code = _dtype_code(q, kc, vc, kring, vring, out)
+    S, H, C, D, W = _check_chunk(q, kc, vc, kring, vring, pos0)
+    if out.shape != q.shape:
+        raise ValueError("out must match q")
+    _check(lib().swa_chunk_forward(_ptr(q), _ptr(kc), _ptr(vc), _ptr(kring), _ptr(vring),
+                                   _ptr(pos0), _ptr(out), S, H, C, D, W, code, _stream(q, stream)))
+
+
+def swa_ring_append_chunk(kc, vc, kring, vring, pos0, stream=None) -> None:
+    """Write the chunk's last min(C, W) tokens into ring slots (pos0 + c) mod W."""
+    _check_device(kc, vc, kring, vring, pos0)
+    code = _dtype_code(kc, vc, kring, vring)
+    S, H, C, D, W = _check_chunk(kc, kc, vc, kring, vring, pos0)
+    _check(lib().swa_ring_append_chunk(_ptr(kc), _ptr(vc), _ptr(kring), _ptr(vring), _ptr(pos0),
+                                       S, H, C, D, W, code, _stream(kc, stream)))
+
+
+def chunk_attention(q, kc, vc, kring, vring, pos0):
+    """Chunk continuation returning a new [S, H, C, D] tensor."""
+    out = torch.empty_like(q)
+    swa_chunk_forward(q, kc, vc, kring, vring, pos0, out)
+    return out
 
 
 def sliding_window_attention(q, k, v, window_size: int):

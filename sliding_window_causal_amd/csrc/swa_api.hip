@@ -101,4 +101,40 @@ int swa_ring_append(const void* knew, const void* vnew, void* kring, void* vring
                                             dtype == SWA_F32 ? 4 : 2, (hipStream_t)stream));
 }
 
+int swa_chunk_forward(const void* q, const void* kc, const void* vc, const void* kring,
+                      const void* vring, const int64_t* pos0, void* out, int64_t S, int64_t H,
+                      int64_t C, int64_t D, int64_t W, int dtype, void* stream) {
+    if (!q || !kc || !vc || !kring || !vring || !pos0 || !out) return SWA_ERR_INVALID_ARG;
+    if (!positive(S) || !positive(H) || !positive(C) || !positive(D) || !positive(W))
+        return SWA_ERR_INVALID_ARG;
+    if (!fits(S, H, C, D) || !fits(S, H, W, D) || S * H * C >= ((int64_t)1 << 31))
+        return SWA_ERR_UNSUPPORTED;
+    if (D > kMaxRowD) return SWA_ERR_UNSUPPORTED;
+    hipStream_t st = (hipStream_t)stream;
+    if (dtype == SWA_BF16)
+        return from_hip(swa::launch_rowwise_chunk<swa::bf16>(
+            (const swa::bf16*)q, (const swa::bf16*)kc, (const swa::bf16*)vc,
+            (const swa::bf16*)kring, (const swa::bf16*)vring, pos0, (swa::bf16*)out, S, H, C,
+            (int)D, W, st));
+    if (dtype == SWA_F32)
+        return from_hip(swa::launch_rowwise_chunk<float>((const float*)q, (const float*)kc,
+                                                         (const float*)vc, (const float*)kring,
+                                                         (const float*)vring, pos0, (float*)out, S,
+                                                         H, C, (int)D, W, st));
+    return SWA_ERR_UNSUPPORTED;
+}
+
+int swa_ring_append_chunk(const void* kc, const void* vc, void* kring, void* vring,
+                          const int64_t* pos0, int64_t S, int64_t H, int64_t C, int64_t D,
+                          int64_t W, int dtype, void* stream) {
+    if (!kc || !vc || !kring || !vring || !pos0) return SWA_ERR_INVALID_ARG;
+    if (!positive(S) || !positive(H) || !positive(C) || !positive(D) || !positive(W))
+        return SWA_ERR_INVALID_ARG;
+    if (!fits(S, H, C, D) || !fits(S, H, W, D) || S * H >= ((int64_t)1 << 31))
+        return SWA_ERR_UNSUPPORTED;
+    if (dtype != SWA_F32 && dtype != SWA_BF16) return SWA_ERR_UNSUPPORTED;
+    return from_hip(swa::launch_ring_append_chunk(kc, vc, kring, vring, pos0, S, H, C, D, W,
+                                                  dtype == SWA_F32 ? 4 : 2, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -200,7 +200,56 @@ __global__ __launch_bounds__(256) void ring_append_kernel(
     }
 }
 
+// Chunk append: tokens pos0 + c for c in [cfirst, C) go to slot
+// (pos0 + c) mod W.  Only the last min(C, W) tokens of a chunk can survive,
+// so cfirst = max(0, C - W) and no two writes of one call share a slot.
+template <typename U>
+__global__ __launch_bounds__(256) void ring_append_chunk_kernel(
+    const U* __restrict__ kc, const U* __restrict__ vc, U* __restrict__ kring,
+    U* __restrict__ vring, const int64_t* __restrict__ pos0, int64_t H, int64_t C, int64_t D,
+    int64_t W, int64_t cfirst) {
+    const int64_t sh = blockIdx.x;
+    const int64_t s = sh / H;
+    const int64_t p0 = pos0[s] < 0 ? 0 : pos0[s];     // same clamp as the chunk forward
+    for (int64_t c = cfirst + blockIdx.y; c < C; c += gridDim.y) {
+        const int64_t slot = (p0 + c) % W;
+        const int64_t dst = (sh * W + slot) * D;
+        const int64_t src = (sh * C + c) * D;
+        for (int64_t d = threadIdx.x; d < D; d += blockDim.x) {
+            kring[dst + d] = kc[src + d];
+            vring[dst + d] = vc[src + d];
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_ring_append_chunk(const void* kc, const void* vc, void* kring, void* vring,
+                                    const int64_t* pos0, int64_t S, int64_t H, int64_t C,
+                                    int64_t D, int64_t W, int elem_bytes, hipStream_t stream) {
+    int64_t cfirst = C > W ? C - W : 0;
+    const int64_t n = C - cfirst;
+    const dim3 grid((unsigned)(S * H), (unsigned)(n < 65535 ? n : 65535));
+    const dim3 block(D >= 256 ? 256 : (unsigned)((D + 63) / 64 * 64));
+    if (elem_bytes == 4) {
+        const uint32_t* kn = (const uint32_t*)kc;
+        const uint32_t* vn = (const uint32_t*)vc;
+        uint32_t* kr = (uint32_t*)kring;
+        uint32_t* vr = (uint32_t*)vring;
+        void* args[] = {(void*)&kn, (void*)&vn, (void*)&kr, (void*)&vr, (void*)&pos0,
+                        (void*)&H, (void*)&C, (void*)&D, (void*)&W, (void*)&cfirst};
+        return hipLaunchKernel((const void*)ring_append_chunk_kernel<uint32_t>, grid, block, args,
+                               0, stream);
+    }
+    const uint16_t* kn = (const uint16_t*)kc;
+    const uint16_t* vn = (const uint16_t*)vc;
+    uint16_t* kr = (uint16_t*)kring;
+    uint16_t* vr = (uint16_t*)vring;
+    void* args[] = {(void*)&kn, (void*)&vn, (void*)&kr, (void*)&vr, (void*)&pos0,
+                    (void*)&H, (void*)&C, (void*)&D, (void*)&W, (void*)&cfirst};
+    return hipLaunchKernel((const void*)ring_append_chunk_kernel<uint16_t>, grid, block, args, 0,
+                           stream);
+}
 
 hipError_t launch_decode_bf16(const bf16* q, const bf16* kring, const bf16* vring,
                               const int64_t* pos, bf16* out, int64_t S, int64_t H, int D,

@@ -29,6 +29,12 @@ hipError_t launch_rowwise_decode(const T* q, const T* kring, const T* vring,
                                  const int64_t* pos, T* out, int64_t S, int64_t H, int D,
                                  int64_t W, hipStream_t stream);
 
+// Chunk continuation of a ring, wavefront per row; T is float or bf16.
+template <typename T>
+hipError_t launch_rowwise_chunk(const T* q, const T* kc, const T* vc, const T* kring,
+                                const T* vring, const int64_t* pos0, T* out, int64_t S, int64_t H,
+                                int64_t C, int D, int64_t W, hipStream_t stream);
+
 // bf16 MFMA band prefill; D in {64, 128}.
 hipError_t launch_prefill_bf16(const bf16* q, const bf16* k, const bf16* v, bf16* out,
                                int64_t B, int64_t H, int64_t T, int D, int64_t W,
@@ -39,6 +45,11 @@ constexpr int64_t kDecodeMaxW = 16384;
 hipError_t launch_decode_bf16(const bf16* q, const bf16* kring, const bf16* vring,
                               const int64_t* pos, bf16* out, int64_t S, int64_t H, int D,
                               int64_t W, hipStream_t stream);
+
+// Chunk append into the ring; any D >= 1; elem_bytes is 2 or 4.
+hipError_t launch_ring_append_chunk(const void* kc, const void* vc, void* kring, void* vring,
+                                    const int64_t* pos0, int64_t S, int64_t H, int64_t C,
+                                    int64_t D, int64_t W, int elem_bytes, hipStream_t stream);
 
 // Ring append; any D >= 1; elem_bytes is 2 or 4.
 hipError_t launch_ring_append(const void* knew, const void* vnew, void* kring, void* vring,

@@ -1,5 +1,6 @@
-// Wavefront-per-row band attention: the fp32 path (any 1 <= D <= 256) and
-// the fallback for shapes the bf16 fast kernels do not cover.
+// Wavefront-per-row band attention: the fp32 path (any 1 <= D <= 256), the
+// chunk continuation of a ring, and the fallback for shapes the bf16 fast
+// kernels do not cover.
 //
 // One 64-lane wavefront owns one output row and walks only that row's
 // visible keys, 64 at a time: lane j scores key c0 + j, the chunk max and
@@ -36,6 +37,76 @@ __device__ inline float wave_sum(float x) {
     return x;
 }
 
+// Online-softmax state of one wavefront's output row.  A row's visible keys
+// may come in several contiguous segments (ring slots that wrap, then the
+// rows of a new chunk); segments are folded in one after another.
+template <typename T>
+struct RowAttn {
+    float m = -__builtin_inff();
+    float l = 0.f;
+    float o[kRowDPL];
+    float* qs;
+    float* ps;
+    int D;
+    float scale;
+
+    __device__ void init(const T* __restrict__ qrow, float* qs_, float* ps_, int D_, float scale_) {
+        qs = qs_;
+        ps = ps_;
+        D = D_;
+        scale = scale_;
+        for (int d = threadIdx.x; d < D; d += 64) qs[d] = to_f32(qrow[d]);
+#pragma unroll
+        for (int r = 0; r < kRowDPL; ++r) o[r] = 0.f;
+        __syncthreads();
+    }
+
+    // Fold in keys [kbeg, kend) of the [*, D] matrices K, V.
+    __device__ void segment(const T* __restrict__ K, const T* __restrict__ V, int64_t kbeg,
+                            int64_t kend) {
+        const int lane = threadIdx.x;
+        for (int64_t c0 = kbeg; c0 < kend; c0 += 64) {
+            const int64_t j = c0 + lane;
+            const bool valid = j < kend;
+            float s = -__builtin_inff();
+            if (valid) {
+                const T* kr = K + j * (int64_t)D;
+                float acc = 0.f;
+                for (int d = 0; d < D; ++d) acc = fmaf(qs[d], to_f32(kr[d]), acc);
+                s = acc * scale;
+            }
+            const float m_new = fmaxf(m, wave_max(s));   // finite: key c0 is valid
+            const float alpha = expf(m - m_new);          // 0 while nothing was seen
+            const float p = valid ? expf(s - m_new) : 0.f;
+            l = l * alpha + wave_sum(p);
+            ps[lane] = p;
+            __syncthreads();
+            const int nk = (int)((kend - c0) < 64 ? (kend - c0) : 64);
+#pragma unroll
+            for (int r = 0; r < kRowDPL; ++r) {
+                const int d = lane + 64 * r;
+                if (d < D) {
+                    float acc = o[r] * alpha;
+                    const T* vc = V + c0 * (int64_t)D + d;
+                    for (int jj = 0; jj < nk; ++jj) acc = fmaf(ps[jj], to_f32(vc[(int64_t)jj * D]), acc);
+                    o[r] = acc;
+                }
+            }
+            m = m_new;
+            __syncthreads();
+        }
+    }
+
+    __device__ void finish(T* __restrict__ orow) const {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+        for (int r = 0; r < kRowDPL; ++r) {
+            const int d = threadIdx.x + 64 * r;
+            if (d < D) orow[d] = from_f32<T>(o[r] * inv);
+        }
+    }
+};
+
 // Attend query row `qrow` to keys [kbeg, kend) of the [*, D] matrices K, V.
 template <typename T>
 __device__ void attend_row(const T* __restrict__ qrow, const T* __restrict__ K,
@@ -43,52 +114,10 @@ __device__ void attend_row(const T* __restrict__ qrow, const T* __restrict__ K,
                            float scale, T* __restrict__ orow) {
     __shared__ float qs[kRowMaxD];
     __shared__ float ps[64];
-    const int lane = threadIdx.x;
-    for (int d = lane; d < D; d += 64) qs[d] = to_f32(qrow[d]);
-    __syncthreads();
-
-    float m = -__builtin_inff();
-    float l = 0.f;
-    float o[kRowDPL];
-#pragma unroll
-    for (int r = 0; r < kRowDPL; ++r) o[r] = 0.f;
-
-    for (int64_t c0 = kbeg; c0 < kend; c0 += 64) {
-        const int64_t j = c0 + lane;
-        const bool valid = j < kend;
-        float s = -__builtin_inff();
-        if (valid) {
-            const T* kr = K + j * (int64_t)D;
-            float acc = 0.f;
-            for (int d = 0; d < D; ++d) acc = fmaf(qs[d], to_f32(kr[d]), acc);
-            s = acc * scale;
-        }
-        const float m_new = fmaxf(m, wave_max(s));   // finite: key c0 is valid
-        const float alpha = expf(m - m_new);          // 0 on the first chunk
-        const float p = valid ? expf(s - m_new) : 0.f;
-        l = l * alpha + wave_sum(p);
-        ps[lane] = p;
-        __syncthreads();
-        const int nk = (int)((kend - c0) < 64 ? (kend - c0) : 64);
-#pragma unroll
-        for (int r = 0; r < kRowDPL; ++r) {
-            const int d = lane + 64 * r;
-            if (d < D) {
-                float acc = o[r] * alpha;
-                const T* vc = V + c0 * (int64_t)D + d;
-                for (int jj = 0; jj < nk; ++jj) acc = fmaf(ps[jj], to_f32(vc[(int64_t)jj * D]), acc);
-                o[r] = acc;
-            }
-        }
-        m = m_new;
-        __syncthreads();
-    }
-    const float inv = kend > kbeg ? 1.f / l : 0.f;
-#pragma unroll
-    for (int r = 0; r < kRowDPL; ++r) {
-        const int d = lane + 64 * r;
-        if (d < D) orow[d] = from_f32<T>(o[r] * inv);
-    }
+    RowAttn<T> st;
+    st.init(qrow, qs, ps, D, scale);
+    st.segment(K, V, kbeg, kend);
+    st.finish(orow);
 }
 
 template <typename T>
@@ -118,7 +147,54 @@ __global__ __launch_bounds__(64) void rowwise_decode_kernel(
     attend_row<T>(q + sh * D, kring + rbase, vring + rbase, 0, n, D, scale, out + sh * D);
 }
 
+// Chunk continuation: query c of the chunk sits at absolute position
+// p = pos0 + c and sees tokens (p - W, p]: those before pos0 live in the
+// ring at slot t mod W (a slot range that may wrap), the rest are chunk rows.
+template <typename T>
+__global__ __launch_bounds__(64) void rowwise_chunk_kernel(
+    const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
+    const T* __restrict__ kring, const T* __restrict__ vring, const int64_t* __restrict__ pos0,
+    T* __restrict__ out, int64_t H, int64_t C, int D, int64_t W, float scale) {
+    const int64_t row = blockIdx.x;            // (s*H + h)*C + c
+    const int64_t sh = row / C;
+    const int64_t c = row - sh * C;
+    const int64_t s = sh / H;
+    int64_t p0 = pos0[s];
+    p0 = p0 < 0 ? 0 : p0;                      // outside the contract; stay in bounds
+    const int64_t p = p0 + c;
+    const int64_t lo = p - W + 1 > 0 ? p - W + 1 : 0;
+    const int64_t cbase = sh * C * D;
+    const int64_t rbase = sh * W * D;
+    __shared__ float qs[kRowMaxD];
+    __shared__ float ps[64];
+    RowAttn<T> st;
+    st.init(q + cbase + c * D, qs, ps, D, scale);
+    if (lo < p0) {                             // ring tokens [lo, p0): slots from lo mod W
+        const int64_t n = p0 - lo;             // < W
+        const int64_t a = lo % W;
+        const int64_t first = a + n <= W ? n : W - a;
+        st.segment(kring + rbase, vring + rbase, a, a + first);
+        if (first < n) st.segment(kring + rbase, vring + rbase, 0, n - first);
+    }
+    const int64_t cb = lo > p0 ? lo - p0 : 0;  // chunk rows [cb, c]
+    st.segment(kc + cbase, vc + cbase, cb, c + 1);
+    st.finish(out + cbase + c * D);
+}
+
 }  // namespace
+
+template <typename T>
+hipError_t launch_rowwise_chunk(const T* q, const T* kc, const T* vc, const T* kring,
+                                const T* vring, const int64_t* pos0, T* out, int64_t S, int64_t H,
+                                int64_t C, int D, int64_t W, hipStream_t stream) {
+    const int64_t rows = S * H * C;
+    float scale = 1.0f / sqrtf((float)D);
+    void* args[] = {(void*)&q, (void*)&kc, (void*)&vc, (void*)&kring, (void*)&vring,
+                    (void*)&pos0, (void*)&out, (void*)&H, (void*)&C, (void*)&D, (void*)&W,
+                    (void*)&scale};
+    return hipLaunchKernel((const void*)rowwise_chunk_kernel<T>, dim3((unsigned)rows), dim3(64),
+                           args, 0, stream);
+}
 
 template <typename T>
 hipError_t launch_rowwise_prefill(const T* q, const T* k, const T* v, T* out, int64_t B,
@@ -150,6 +226,12 @@ template hipError_t launch_rowwise_prefill<float>(const float*, const float*, co
 template hipError_t launch_rowwise_prefill<bf16>(const bf16*, const bf16*, const bf16*, bf16*,
                                                  int64_t, int64_t, int64_t, int, int64_t,
                                                  hipStream_t);
+template hipError_t launch_rowwise_chunk<float>(const float*, const float*, const float*,
+                                                const float*, const float*, const int64_t*, float*,
+                                                int64_t, int64_t, int64_t, int, int64_t, hipStream_t);
+template hipError_t launch_rowwise_chunk<bf16>(const bf16*, const bf16*, const bf16*, const bf16*,
+                                               const bf16*, const int64_t*, bf16*, int64_t, int64_t,
+                                               int64_t, int, int64_t, hipStream_t);
 template hipError_t launch_rowwise_decode<float>(const float*, const float*, const float*,
                                                  const int64_t*, float*, int64_t, int64_t,
                                                  int, int64_t, hipStream_t);

@@ -25,7 +25,7 @@ def _declared_functions():
 def test_header_declares_entry_points():
     names = _declared_functions()
     for n in ("swa_forward", "swa_decode", "swa_ring_append", "swa_status_string",
-              "swa_abi_version"):
+              "swa_abi_version", "swa_chunk_forward", "swa_ring_append_chunk"):
         assert n in names
 
 
@@ -96,6 +96,38 @@ def test_append_invalid_args(kw):
 
 def test_append_unsupported_dtype():
     assert _app(dt=5) == swa.SWA_ERR_UNSUPPORTED
+
+
+def _chunk(q=DUMMY, kc=DUMMY, vc=DUMMY, kr=DUMMY, vr=DUMMY, pos=DUMMY, o=DUMMY, S=1, H=1, C=4,
+           D=64, W=8, dt=swa.SWA_BF16):
+    return swa.lib().swa_chunk_forward(q, kc, vc, kr, vr, pos, o, S, H, C, D, W, dt, None)
+
+
+def _app_chunk(kc=DUMMY, vc=DUMMY, kr=DUMMY, vr=DUMMY, pos=DUMMY, S=1, H=1, C=4, D=64, W=8,
+               dt=swa.SWA_BF16):
+    return swa.lib().swa_ring_append_chunk(kc, vc, kr, vr, pos, S, H, C, D, W, dt, None)
+
+
+@pytest.mark.parametrize("kw", [dict(q=None), dict(kc=None), dict(vc=None), dict(kr=None),
+                                dict(vr=None), dict(pos=None), dict(o=None), dict(S=0), dict(H=0),
+                                dict(C=0), dict(D=0), dict(W=0)])
+def test_chunk_invalid_args(kw):
+    assert _chunk(**kw) == swa.SWA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(dt=9), dict(D=300)])
+def test_chunk_unsupported(kw):
+    assert _chunk(**kw) == swa.SWA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(kc=None), dict(vr=None), dict(pos=None), dict(C=0),
+                                dict(W=-2)])
+def test_append_chunk_invalid_args(kw):
+    assert _app_chunk(**kw) == swa.SWA_ERR_INVALID_ARG
+
+
+def test_append_chunk_unsupported_dtype():
+    assert _app_chunk(dt=4) == swa.SWA_ERR_UNSUPPORTED
 
 
 def test_oversized_grid_is_unsupported():
