@@ -189,14 +189,14 @@ __device__ inline bf16x8 pack_p(const f32x16& s, int e0, float& acc) {
     return pf;
 }
 
-// O^T += V^T P^T for the 16-key chunk ch.  Lane l (i = l % 16, group half
-// dh = (l / 16) % 2, hh = l / 32) needs, for d = 32 db + l % 32, the keys
-// 16 ch + 8 a + 4 hh + e (a = 0, 1; e = 0..3).  One ds_read_b64_tr_b16 over
-// the 16 lanes of a group hands lane i column (group base + i) of the 4 x 16
-// block whose row r0 + i/4, columns 4 (i % 4) .. + 3, lane i addresses.
+// A operands of O^T += V^T P^T for the 16-key chunk ch.  Lane l (i = l % 16,
+// group half dh = (l / 16) % 2, hh = l / 32) needs, for d = 32 db + l % 32,
+// the keys 16 ch + 8 a + 4 hh + e (a = 0, 1; e = 0..3).  One
+// ds_read_b64_tr_b16 over the 16 lanes of a group hands lane i column
+// (group base + i) of the 4 x 16 block whose row r0 + i/4, columns
+// 4 (i % 4) .. + 3, lane i addresses.
 template <int D>
-__device__ inline void pv_chunk(const char* Vt, const bf16x8& pf, int ch, int lane,
-                                f32x16 (&o)[D / 32]) {
+__device__ inline void read_v_chunk(const char* Vt, int ch, int lane, bf16x8 (&va)[D / 32]) {
     const int i = lane & 15, hh = lane >> 5, dh = (lane >> 4) & 1;
     const int row = 16 * ch + 4 * hh + (i >> 2);           // + 8 a
     const int vsw = vswz<D>(i >> 2);                        // row + 8 a keeps the swizzle
@@ -207,9 +207,7 @@ __device__ inline void pv_chunk(const char* Vt, const bf16x8& pf, int ch, int la
         const char* p0 = rp + (chunk << 4);
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p0);
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0 + 8 * 2 * D));
-        const i16x8 v8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v8), pf, o[db],
-                                                         0, 0, 0);
+        va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 }
 
@@ -310,15 +308,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     load_k(t0 + C::PF);
     publish();   // K(t0), V(t0), K(t0+1) have landed
 
-    // Reference update for a freshly computed (and masked) score tile: raise
-    // m if the tile's max exceeds it by more than 2^8 and rescale what has
-    // been accumulated so far.  Runs between tiles, outside the MFMA/VALU
-    // overlap regions.
-    auto update_ref = [&](const f32x16& s) {
+    // Row max of a score tile (in-lane over 16 keys, then across the lane
+    // pair l, l ^ 32 that shares the query).
+    auto tile_max = [&](const f32x16& s) {
         float mx = fmaxf(s[0], s[1]);
 #pragma unroll
         for (int v = 2; v < 16; v += 2) mx = fmaxf(fmaxf(mx, s[v]), s[v + 1]);
-        mx = swap_max(mx);
+        return swap_max(mx);
+    };
+    // Reference update for a freshly computed (and masked) score tile whose
+    // row max is mx: raise m if mx exceeds it by more than 2^8 and rescale
+    // what has been accumulated so far.  Runs between tiles, outside the
+    // MFMA/VALU overlap regions.
+    auto raise_ref = [&](float mx) {
         const bool raise = mx > m + tau;               // false while the row is fully masked
         if (__any(raise)) {
             // 1 for rows keeping their reference (also rows still fully
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (needs(t0)) {
         qk_tile<D>(kslot(t0), qf, lr, hh, ksw, sA);
         if (!interior(t0)) mask_tile(sA, qi, t0 * C::BN, hh, W);
-        update_ref(sA);
+        raise_ref(tile_max(sA));
     }
     __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8) | 15 | (3 << 14));   // LDS reads done
     __builtin_amdgcn_s_barrier();   // every wave is done with K(t0) before its slot is reloaded
@@ -351,6 +353,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const bool nj = needs(j), nn = needs(j + 1);
         const char* Kn = kslot(j + 1);
         const char* Vc = vslot(j);
+        float mxn;
 
         // Every wave runs every tile of the workgroup, so the accumulator
         // path has no branches; a tile outside this wave's band gets
@@ -362,46 +365,68 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             // closes a slice, so the MFMAs at the top of a slice run on the
             // matrix core while the slice's (independent) vector ALU work
             // issues behind them.
-            //
-            // Region A: S(j+1) = K(j+1) Q^T, one MFMA per 16-wide d slice, with
-            // the probabilities of keys 0..11 of tile j and the operand p0 of
-            // keys 0..15.  S(j+1) is computed even where this wave does not
-            // need it (at the end from a stale but finite buffer); it is then
-            // never used.
             constexpr int ND = D / 16;
             constexpr int NEA = 12;                 // exps issued in region A
+            constexpr int NPRE = 2;                 // of which before the first MFMA
             bf16x8 p0, p1;
+            // All K(j+1) operands and the V(j) operands of chunk 0 are read
+            // from LDS up front, so their latency hides behind the first
+            // slices instead of stalling each MFMA.
+            bf16x8 kf[ND], va0[D / 32], va1[D / 32];
             {
                 const char* r0 = Kn + lr * (2 * D);
-                sn = f32x16{};
-                bf16x8 ka = *reinterpret_cast<const bf16x8*>(r0 + ((hh ^ ksw) << 4));
 #pragma unroll
-                for (int dc = 0; dc < ND; ++dc) {
-                    bf16x8 na = ka;
-                    if (dc + 1 < ND)
-                        na = *reinterpret_cast<const bf16x8*>(r0 + (((2 * (dc + 1) + hh) ^ ksw) << 4));
-                    sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[dc], sn, 0, 0, 0);
+                for (int dc = 0; dc < ND; ++dc)
+                    kf[dc] = *reinterpret_cast<const bf16x8*>(r0 + (((2 * dc + hh) ^ ksw) << 4));
+            }
+            read_v_chunk<D>(Vc, 0, lane, va0);
+            // The first probabilities need no LDS data: they cover the
+            // latency of the first operand reads.
 #pragma unroll
-                    for (int v = dc * NEA / ND; v < (dc + 1) * NEA / ND; ++v)
-                        sc[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], c, -mc));
-                    if (dc == ND - 1) p0 = pack_p(sc, 0, ps);
-                    ka = na;
-                    __builtin_amdgcn_sched_barrier(0);
+            for (int v = 0; v < NPRE; ++v) sc[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], c, -mc));
+            __builtin_amdgcn_sched_barrier(0);
+            // Region A: S(j+1) = K(j+1) Q^T, one MFMA per 16-wide d slice, with
+            // the probabilities of keys NPRE..NEA-1 of tile j and the operand
+            // p0 of keys 0..15.  S(j+1) is computed even where this wave does
+            // not need it (at the end from a stale but finite buffer); it is
+            // then never used.
+            sn = f32x16{};
+#pragma unroll
+            for (int dc = 0; dc < ND; ++dc) {
+                sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dc], qf[dc], sn, 0, 0, 0);
+#pragma unroll
+                for (int v = NPRE + dc * (NEA - NPRE) / ND; v < NPRE + (dc + 1) * (NEA - NPRE) / ND; ++v)
+                    sc[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], c, -mc));
+                if (dc == ND - 1) {
+                    p0 = pack_p(sc, 0, ps);
+                    read_v_chunk<D>(Vc, 1, lane, va1);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
             // Region B: O += V(j) P(j), two 16-key chunks of D/32 MFMAs, with
-            // the rest of the probabilities produced alongside chunk 0.
-            pv_chunk<D>(Vc, p0, 0, lane, o);
+            // the rest of the probabilities produced alongside chunk 0 and the
+            // row max of S(j+1) alongside chunk 1.
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0[db], p0, o[db], 0, 0, 0);
 #pragma unroll
             for (int v = NEA; v < 16; ++v) sc[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], c, -mc));
             p1 = pack_p(sc, 8, ps);
             __builtin_amdgcn_sched_barrier(0);
-            pv_chunk<D>(Vc, p1, 1, lane, o);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1[db], p1, o[db], 0, 0, 0);
+            mxn = tile_max(sn);
+            __builtin_amdgcn_sched_barrier(0);
             lsum += ps;
         }
         if (nn) {
-            if (!interior(j + 1)) mask_tile(sn, qi, (j + 1) * C::BN, hh, W);
-            update_ref(sn);
+            // Edge tiles are masked, and their max taken again, here.
+            if (!interior(j + 1)) {
+                mask_tile(sn, qi, (j + 1) * C::BN, hh, W);
+                mxn = tile_max(sn);
+            }
+            raise_ref(mxn);
         }
         publish();   // V(j+1) and K(j+2), needed by the next step, have landed
     };
