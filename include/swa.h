@@ -76,6 +76,34 @@ int swa_forward(const void* q, const void* k, const void* v, void* out,
                 int dtype, void* stream);
 
 /*
+ * Prefill with arbitrary strides and an optional score scale: the layouts of
+ * "Implementation: Sliding Window Attention", Step 2 (queries, keys and
+ * values as (batch, seq_len, num_heads, head_dim), and its scale argument
+ * that defaults to 1 / sqrt(head_dim)) and of "25. Sliding-Window Causal
+ * Attention for Streaming Inference" ((batch, seq_len, d_model), one head),
+ * without copies.  The computation is that of swa_forward with the scores
+ * multiplied by `scale` instead of divided by sqrt(D).
+ *
+ *   q, k, v, out : logical [B, H, T, D]; element (b, h, t, d) of tensor X
+ *                  sits at X + b * sb + h * sh + t * st + d, elements of dtype
+ *   strides      : host int64[12] = {q_sb, q_sh, q_st, k_sb, k_sh, k_st,
+ *                  v_sb, v_sh, v_st, out_sb, out_sh, out_st}, in elements,
+ *                  each >= 0 (0 broadcasts, e.g. one key/value head shared
+ *                  by all query heads).  Read during the call only.
+ *   scale        : finite; 0 selects 1 / sqrt(D)
+ *   dtype        : as swa_forward.  bf16 with 16-byte aligned pointers,
+ *                  strides that are multiples of 8, k/v row strides >= D and
+ *                  k/v (batch, head) slabs under 2 GiB runs on the matrix
+ *                  cores; other bf16 layouts run on the row-wise kernel.
+ *   out must not overlap itself or an input.
+ * Returns SWA_ERR_INVALID_ARG also for a null `strides`, a negative stride
+ * or a non-finite scale.
+ */
+int swa_forward_strided(const void* q, const void* k, const void* v, void* out, int64_t B,
+                        int64_t H, int64_t T, int64_t D, int64_t W, const int64_t* strides,
+                        double scale, int dtype, void* stream);
+
+/*
  * Decode: one query per stream against a bounded W-slot ring of keys/values
  * (the bounded cache that drops anything older than the window,
  * "25. Sliding-Window Causal Attention for Streaming Inference", Problem; a

@@ -100,13 +100,26 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def swa_dense(q, k, v, W: int, return_weights: bool = False):
+def _scores(qk, D: int, scale):
+    """Raw dot products to scores: divided by sqrt(D) [P1 step 1; P2 step 1;
+    P5 code], or multiplied by an explicit ``scale`` [P3 Step 2, whose
+    ``scale`` argument defaults to 1 / sqrt(head_dim)]."""
+    if scale is None:
+        return qk / math.sqrt(D)
+    scale = float(scale)
+    if not math.isfinite(scale):
+        raise ValueError("scale must be finite")
+    return qk * scale
+
+
+def swa_dense(q, k, v, W: int, return_weights: bool = False, scale=None):
     """The pages' dense recipe in float64.
 
     q, k: (..., T, D); v: (..., T, Dv); any leading dims (P1 and P4 use
     (B, H, T, D), P2 uses (B, T, D), P5 uses (H, T, Dh)).
 
     1. scores = q @ k^T / sqrt(D)          [P1 step 1; P2 step 1; P5 code]
+       (or q @ k^T * scale                 [P3 Step 2])
     2. band mask, select -inf outside it   [P1 steps 2-3; P5 "Mask before softmax"]
     3. stable softmax over keys            [P3 Step 2: subtract the row max,
                                             exponentiate, divide by the sum]
@@ -119,7 +132,7 @@ def swa_dense(q, k, v, W: int, return_weights: bool = False):
     T, D = q.shape[-2], q.shape[-1]
     if k.shape[-2] != T or v.shape[-2] != T or k.shape[-1] != D:
         raise ValueError("q, k, v must share T, and q, k must share D")
-    scores = np.matmul(q, np.swapaxes(k, -1, -2)) / math.sqrt(D)
+    scores = _scores(np.matmul(q, np.swapaxes(k, -1, -2)), D, scale)
     mask = band_mask(T, W)
     scores = np.where(mask, scores, -np.inf)
     row_max = scores.max(axis=-1, keepdims=True)
@@ -131,13 +144,14 @@ def swa_dense(q, k, v, W: int, return_weights: bool = False):
     return out
 
 
-def swa_rows(q, k, v, W: int, rows: Iterable[int]):
+def swa_rows(q, k, v, W: int, rows: Iterable[int], scale=None):
     """Output rows ``rows`` computed one by one from the definition.
 
     For query i the visible keys are j in [max(0, i - W + 1), i] (the same set
     as ``band_mask``: j <= i and i - j < W, P1 step 2, P5 "Build the band by
-    index difference").  Over that set: s_j = q_i . k_j / sqrt(D), then a
-    stable softmax and the weighted sum of v_j (P3 Step 2).  Only the band is
+    index difference").  Over that set: s_j = q_i . k_j / sqrt(D) (or times
+    ``scale``, P3 Step 2), then a stable softmax and the weighted sum of v_j
+    (P3 Step 2).  Only the band is
     touched, so this works at full size for a sample of rows.
 
     q, k: (..., T, D); v: (..., T, Dv) (float arrays of any float dtype).
@@ -155,7 +169,6 @@ def swa_rows(q, k, v, W: int, rows: Iterable[int]):
     V = v.reshape(-1, T, Dv)
     rows = [int(r) for r in rows]
     out = np.empty((Q.shape[0], len(rows), Dv), dtype=np.float64)
-    root_d = math.sqrt(D)
     for r, i in enumerate(rows):
         if not 0 <= i < T:
             raise IndexError(f"row {i} outside [0, {T})")
@@ -163,7 +176,7 @@ def swa_rows(q, k, v, W: int, rows: Iterable[int]):
         kk = K[:, lo:i + 1, :].astype(np.float64)              # (N, n, D)
         vv = V[:, lo:i + 1, :].astype(np.float64)              # (N, n, Dv)
         qi = Q[:, i, :].astype(np.float64)                     # (N, D)
-        s = np.matmul(kk, qi[:, :, None])[:, :, 0] / root_d     # (N, n)
+        s = _scores(np.matmul(kk, qi[:, :, None])[:, :, 0], D, scale)   # (N, n)
         m = s.max(axis=1, keepdims=True)
         e = np.exp(s - m)
         w = e / e.sum(axis=1, keepdims=True)

@@ -7,6 +7,8 @@ no CPU fallback: if ``libswa.so`` is missing every entry point raises.
 
 Entry points (same names as the C ABI):
   swa_forward(q, k, v, out, window_size)        prefill, [B, H, T, D]
+  swa_forward_strided(q, k, v, out, window_size, scale=None)
+                                                 prefill over strided [B, H, T, D] views
   swa_decode(q, kring, vring, pos, out)          decode against a W-slot ring
   swa_ring_append(knew, vnew, kring, vring, pos) write position pos into slot pos mod W
   swa_chunk_forward(q, kc, vc, kring, vring, pos0, out)
@@ -14,7 +16,7 @@ Entry points (same names as the C ABI):
   swa_ring_append_chunk(kc, vc, kring, vring, pos0)
                                                  write a chunk's tokens into the ring
 Conveniences that allocate the output with torch:
-  sliding_window_attention(q, k, v, window_size) -> out
+  sliding_window_attention(q, k, v, window_size, scale=None, layout=None) -> out
   decode(q, kring, vring, pos) -> out
   chunk_attention(q, kc, vc, kring, vring, pos0) -> out
 """
@@ -29,7 +31,7 @@ import torch
 __all__ = [
     "LIB_PATH", "SWA_F32", "SWA_BF16", "SWA_OK", "SWA_ERR_INVALID_ARG",
     "SWA_ERR_UNSUPPORTED", "SWA_ERR_LAUNCH", "SWAError", "lib", "abi_version",
-    "status_string", "swa_forward", "swa_decode", "swa_ring_append", "swa_chunk_forward",
+    "status_string", "swa_forward", "swa_forward_strided", "swa_decode", "swa_ring_append", "swa_chunk_forward",
     "swa_ring_append_chunk", "sliding_window_attention", "decode", "chunk_attention",
 ]
 
@@ -65,6 +67,9 @@ def lib() -> ctypes.CDLL:
     L.swa_status_string.restype = ctypes.c_char_p
     L.swa_forward.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i32, p]
     L.swa_forward.restype = i32
+    L.swa_forward_strided.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, p, ctypes.c_double,
+                                      i32, p]
+    L.swa_forward_strided.restype = i32
     L.swa_decode.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, p]
     L.swa_decode.restype = i32
     L.swa_ring_append.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, p]
@@ -106,7 +111,7 @@ def _dtype_code(*ts: torch.Tensor) -> int:
     return _DTYPES[dt]
 
 
-def _check_device(*ts: torch.Tensor) -> None:
+def _check_device(*ts: torch.Tensor, contiguous: bool = True) -> None:
     dev = ts[0].device
     for t in ts:
         if not isinstance(t, torch.Tensor):
@@ -115,7 +120,7 @@ def _check_device(*ts: torch.Tensor) -> None:
             raise ValueError("tensors must be on a GPU device (no CPU fallback)")
         if t.device != dev:
             raise ValueError("tensors must be on one device")
-        if not t.is_contiguous():
+        if contiguous and not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
 
 
@@ -141,6 +146,29 @@ def swa_forward(q, k, v, out, window_size: int, stream=None) -> None:
     B, H, T, D = q.shape
     _check(lib().swa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, T, D, W, code,
                              _stream(q, stream)))
+
+
+def swa_forward_strided(q, k, v, out, window_size: int, scale=None, stream=None) -> None:
+    """Prefill into ``out`` for [B, H, T, D] views of any strides whose last
+    axis is contiguous (e.g. a (B, T, H, D) tensor seen through
+    ``permute(0, 2, 1, 3)``); ``scale`` multiplies the scores (None: 1/sqrt(D))."""
+    W = _window(window_size)
+    _check_device(q, k, v, out, contiguous=False)
+    code = _dtype_code(q, k, v, out)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or out.shape != q.shape:
+        raise ValueError("q, k, v, out must all be [B, H, T, D] views of one shape")
+    if any(t.stride(3) != 1 for t in (q, k, v, out)):
+        raise ValueError("the head-size axis must be contiguous")
+    if scale is None:
+        scale = 0.0                       # the library's code for 1 / sqrt(D)
+    elif isinstance(scale, bool) or not isinstance(scale, (int, float)):
+        raise TypeError("scale must be a number")
+    elif scale == 0 or scale != scale or abs(scale) == float("inf"):
+        raise ValueError("scale must be finite and non-zero")
+    B, H, T, D = q.shape
+    st = (ctypes.c_int64 * 12)(*[x for t in (q, k, v, out) for x in t.stride()[:3]])
+    _check(lib().swa_forward_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, T, D, W, st,
+                                     float(scale), code, _stream(q, stream)))
 
 
 def swa_decode(q, kring, vring, pos, out, stream=None) -> None:
@@ -214,14 +242,36 @@ def chunk_attention(q, kc, vc, kring, vring, pos0):
     return out
 
 
-def sliding_window_attention(q, k, v, window_size: int):
-    """Prefill returning a new tensor.  [B, H, T, D], or [B, T, D] as one head."""
-    squeeze = q.dim() == 3
-    if squeeze:
-        q, k, v = q.unsqueeze(1), k.unsqueeze(1), v.unsqueeze(1)
+_LAYOUTS = ("bhtd", "bshd", "btd")
+
+
+def sliding_window_attention(q, k, v, window_size: int, scale=None, layout: str = None):
+    """Prefill returning a new tensor in the layout of ``q``.
+
+    layout "bhtd": [B, H, T, D];  "bshd": [B, T, H, D];  "btd": [B, T, D], one
+    head.  Default: "bhtd" for 4-D inputs, "btd" for 3-D.  ``scale`` multiplies
+    the scores (None: 1/sqrt(D)).  Contiguous [B, H, T, D] inputs with the
+    default scale go through swa_forward; everything else through
+    swa_forward_strided, reading the tensors in place.
+    """
+    if layout is None:
+        layout = "btd" if q.dim() == 3 else "bhtd"
+    if layout not in _LAYOUTS:
+        raise ValueError(f"layout must be one of {_LAYOUTS}")
+    if q.dim() != (3 if layout == "btd" else 4):
+        raise ValueError(f"layout {layout!r} needs {3 if layout == 'btd' else 4}-D tensors")
     out = torch.empty_like(q)
-    swa_forward(q, k, v, out, window_size)
-    return out.squeeze(1) if squeeze else out
+    if layout == "btd":
+        views = [t.unsqueeze(1) for t in (q, k, v, out)]
+    elif layout == "bshd":
+        views = [t.permute(0, 2, 1, 3) for t in (q, k, v, out)]
+    else:
+        views = [q, k, v, out]
+    if scale is None and all(t.is_contiguous() for t in views):
+        swa_forward(*views, window_size)
+    else:
+        swa_forward_strided(*views, window_size, scale=scale)
+    return out
 
 
 def decode(q, kring, vring, pos):

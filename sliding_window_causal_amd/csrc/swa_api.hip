@@ -4,6 +4,8 @@
 #include "../../include/swa.h"
 #include "swa_internal.h"
 
+#include <cmath>
+
 namespace {
 
 constexpr int kAbiVersion = 1;
@@ -24,6 +26,33 @@ bool fits(int64_t a, int64_t b, int64_t c, int64_t d) {
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH; }
+
+// Prefill dispatch once arguments are known to be non-null and positive.
+// scale == 0 selects 1 / sqrt(D).
+int forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H,
+            int64_t T, int64_t D, int64_t W, const swa::Layout& L, double scale, int dtype,
+            hipStream_t st) {
+    if (B * H * T >= ((int64_t)1 << 31)) return SWA_ERR_UNSUPPORTED;
+    const float sc = scale == 0.0 ? 1.0f / sqrtf((float)D) : (float)scale;
+    if (dtype == SWA_BF16) {
+        if (D != 64 && D != 128) return SWA_ERR_UNSUPPORTED;
+        const swa::bf16 *qb = (const swa::bf16*)q, *kb = (const swa::bf16*)k,
+                        *vb = (const swa::bf16*)v;
+        if (swa::prefill_bf16_supports(q, k, v, out, T, D, L))
+            return from_hip(swa::launch_prefill_bf16(qb, kb, vb, (swa::bf16*)out, B, H, T, (int)D,
+                                                     W, L, sc, st));
+        // alignment or offsets the matrix-core kernel does not take
+        return from_hip(swa::launch_rowwise_prefill<swa::bf16>(qb, kb, vb, (swa::bf16*)out, B, H,
+                                                               T, (int)D, W, L, sc, st));
+    }
+    if (dtype == SWA_F32) {
+        if (D > kMaxRowD) return SWA_ERR_UNSUPPORTED;
+        return from_hip(swa::launch_rowwise_prefill<float>((const float*)q, (const float*)k,
+                                                           (const float*)v, (float*)out, B, H, T,
+                                                           (int)D, W, L, sc, st));
+    }
+    return SWA_ERR_UNSUPPORTED;
+}
 
 }  // namespace
 
@@ -46,23 +75,25 @@ int swa_forward(const void* q, const void* k, const void* v, void* out, int64_t 
     if (!q || !k || !v || !out) return SWA_ERR_INVALID_ARG;
     if (!positive(B) || !positive(H) || !positive(T) || !positive(D) || !positive(W))
         return SWA_ERR_INVALID_ARG;
-    if (!fits(B, H, T, D) || B * H * T >= ((int64_t)1 << 31)) return SWA_ERR_UNSUPPORTED;
-    hipStream_t st = (hipStream_t)stream;
-    if (dtype == SWA_BF16) {
-        // the bf16 kernel indexes one (batch, head) slab with 32-bit offsets
-        if ((D == 64 || D == 128) && T * D < ((int64_t)1 << 31))
-            return from_hip(swa::launch_prefill_bf16((const swa::bf16*)q, (const swa::bf16*)k,
-                                                     (const swa::bf16*)v, (swa::bf16*)out, B, H, T,
-                                                     (int)D, W, st));
-        return SWA_ERR_UNSUPPORTED;
-    }
-    if (dtype == SWA_F32) {
-        if (D > kMaxRowD) return SWA_ERR_UNSUPPORTED;
-        return from_hip(swa::launch_rowwise_prefill<float>((const float*)q, (const float*)k,
-                                                           (const float*)v, (float*)out, B, H, T,
-                                                           (int)D, W, st));
-    }
-    return SWA_ERR_UNSUPPORTED;
+    if (!fits(B, H, T, D)) return SWA_ERR_UNSUPPORTED;
+    return forward(q, k, v, out, B, H, T, D, W, swa::contiguous_layout(H, T, D), 0.0, dtype,
+                   (hipStream_t)stream);
+}
+
+int swa_forward_strided(const void* q, const void* k, const void* v, void* out, int64_t B,
+                        int64_t H, int64_t T, int64_t D, int64_t W, const int64_t* strides,
+                        double scale, int dtype, void* stream) {
+    if (!q || !k || !v || !out || !strides) return SWA_ERR_INVALID_ARG;
+    if (!positive(B) || !positive(H) || !positive(T) || !positive(D) || !positive(W))
+        return SWA_ERR_INVALID_ARG;
+    for (int i = 0; i < 12; ++i)
+        if (strides[i] < 0) return SWA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return SWA_ERR_INVALID_ARG;
+    if (!fits(B, H, T, D)) return SWA_ERR_UNSUPPORTED;
+    swa::Layout L;
+    swa::Strides* dst[4] = {&L.q, &L.k, &L.v, &L.o};
+    for (int i = 0; i < 4; ++i) *dst[i] = {strides[3 * i], strides[3 * i + 1], strides[3 * i + 2]};
+    return forward(q, k, v, out, B, H, T, D, W, L, scale, dtype, (hipStream_t)stream);
 }
 
 int swa_decode(const void* q, const void* kring, const void* vring, const int64_t* pos, void* out,

@@ -17,13 +17,27 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Element strides of a [B, H, T, D] operand whose D axis is contiguous:
+// element (b, h, t, d) sits at b * b + h * h + t * t + d.
+struct Strides {
+    int64_t b, h, t;
+};
+// Strides of q, k, v and out of one prefill call.
+struct Layout {
+    Strides q, k, v, o;
+};
+inline Layout contiguous_layout(int64_t H, int64_t T, int64_t D) {
+    const Strides s = {H * T * D, T * D, D};
+    return {s, s, s, s};
+}
+
 // ---- launchers (each returns the hipError_t of its launch) -----------------
 
 // Generic wavefront-per-row kernels; T is float or bf16; 1 <= D <= 256.
 template <typename T>
 hipError_t launch_rowwise_prefill(const T* q, const T* k, const T* v, T* out,
                                   int64_t B, int64_t H, int64_t Tn, int D, int64_t W,
-                                  hipStream_t stream);
+                                  const Layout& L, float scale, hipStream_t stream);
 template <typename T>
 hipError_t launch_rowwise_decode(const T* q, const T* kring, const T* vring,
                                  const int64_t* pos, T* out, int64_t S, int64_t H, int D,
@@ -35,10 +49,14 @@ hipError_t launch_rowwise_chunk(const T* q, const T* kc, const T* vc, const T* k
                                 const T* vring, const int64_t* pos0, T* out, int64_t S, int64_t H,
                                 int64_t C, int D, int64_t W, hipStream_t stream);
 
-// bf16 MFMA band prefill; D in {64, 128}.
+// bf16 MFMA band prefill; D in {64, 128}.  Every pointer 16-byte aligned,
+// every stride a multiple of 8 elements, row strides >= D, and each
+// (batch, head) slab of k and v within 2^31 bytes (prefill_bf16_supports).
+bool prefill_bf16_supports(const void* q, const void* k, const void* v, const void* out,
+                           int64_t T, int64_t D, const Layout& L);
 hipError_t launch_prefill_bf16(const bf16* q, const bf16* k, const bf16* v, bf16* out,
                                int64_t B, int64_t H, int64_t T, int D, int64_t W,
-                               hipStream_t stream);
+                               const Layout& L, float scale, hipStream_t stream);
 
 // bf16 ring decode; D in {64, 128}, W <= kDecodeMaxW.
 constexpr int64_t kDecodeMaxW = 16384;

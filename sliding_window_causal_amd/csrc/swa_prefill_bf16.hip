@@ -67,12 +67,15 @@ struct Args {
     const bf16* k;
     const bf16* v;
     bf16* out;
+    Layout L;       // element strides (D axis contiguous)
+    int H;
     int T;
     int W;          // min(W, T)
     int nqt;        // query tiles per (b, h)
     int nblocks;    // grid size
     int remap;      // 1: spread consecutive logical tiles over one XCD
-    float c;        // log2(e) / sqrt(D)
+    float c;        // log2(e) * |scale| (scale defaults to 1 / sqrt(D))
+    int qneg;       // 1: scale < 0, applied as -q (exact) times |scale|
 };
 
 __device__ inline float swap_max(float x) {
@@ -99,13 +102,15 @@ template <int D> __device__ inline int vswz(int row) {
     return D == 128 ? 4 * (row & 3) : 4 * (row & 1);
 }
 
-// Buffer resource over rows [k0, T) of one (batch, head) slab: loads past
-// the sequence end return zeros.  Keys past the end lie above every valid
-// query's diagonal, so their scores are masked to -inf and their (zero)
-// values get weight 0.
-__device__ inline __amdgpu_buffer_rsrc_t rows_rsrc(const bf16* slab, int k0, int T, int D) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(slab + k0 * D), 0,
-                                            (T - k0) * D * 2, 0x00020000);
+// Buffer resource over the bytes [off, slab_bytes) of one (batch, head)
+// slab whose rows are at least D elements apart: loads past the sequence
+// end return zeros.  Keys past the end lie above every valid query's
+// diagonal, so their scores are masked to -inf and their (zero) values get
+// weight 0.
+__device__ inline __amdgpu_buffer_rsrc_t rows_rsrc(const bf16* slab, int off, int slab_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(reinterpret_cast<const char*>(slab) + off), 0, slab_bytes - off,
+        0x00020000);
 }
 
 // One 16-byte-per-lane buffer load into LDS: lane l's 16 bytes land at
@@ -126,21 +131,33 @@ __device__ inline uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// Start the HBM -> LDS copy of one tile.  Load n of this wave writes tile
+// Source offsets of one tile's loads.  Load n of this wave writes tile
 // bytes [1024 n, 1024 n + 1024), lane l the 16 bytes at 1024 n + 16 l; it
-// fetches the chunk that the swizzle stores there.
-template <int D, int NW, bool IS_V>
-__device__ inline void dma_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t buf, int wave, int lane) {
+// fetches the chunk that the swizzle stores there, from a row rsb bytes
+// apart from the previous one.
+template <int D, int NW, bool IS_V, int N>
+__device__ inline void tile_offsets(uint32_t (&voff)[N], int wave, int lane, int rsb) {
     using C = Cfg<D, NW>;
+    static_assert(N == C::NLD_W, "one offset per load");
 #pragma unroll
     for (int i = 0; i < C::NLD_W; ++i) {
-        const int n = wave * C::NLD_W + i;
-        const int p = n * 1024 + lane * 16;
+        const int p = (wave * C::NLD_W + i) * 1024 + lane * 16;
         const int row = p / C::ROWB;
         const int phys = (p % C::ROWB) >> 4;
         const int logical = phys ^ (IS_V ? vswz<D>(row) : kswz<D>(row));
-        lds_load16(rsrc, buf + n * 1024, row * C::ROWB + logical * 16);
+        voff[i] = row * rsb + logical * 16;
     }
+}
+
+// Start the HBM -> LDS copy of one tile.
+template <int D, int NW, int N>
+__device__ inline void dma_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t buf, int wave,
+                                const uint32_t (&voff)[N]) {
+    using C = Cfg<D, NW>;
+    static_assert(N == C::NLD_W, "one offset per load");
+#pragma unroll
+    for (int i = 0; i < C::NLD_W; ++i)
+        lds_load16(rsrc, buf + (wave * C::NLD_W + i) * 1024, voff[i]);
 }
 
 // S^T for a 32-key tile: s holds keys 8 (v/4) + 4 hh + v%4 of query lr
@@ -235,10 +252,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int qt = a.nqt - 1 - (logical - bh * a.nqt);
     const int T = a.T, W = a.W;
     const int i0 = qt * C::BM;
-    const int64_t off = (int64_t)bh * T * D;
-    const bf16* __restrict__ Qbh = a.q + off;
-    const bf16* __restrict__ Kbh = a.k + off;
-    const bf16* __restrict__ Vbh = a.v + off;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const bf16* __restrict__ Qbh = a.q + b * a.L.q.b + h * a.L.q.h;
+    const bf16* __restrict__ Kbh = a.k + b * a.L.k.b + h * a.L.k.h;
+    const bf16* __restrict__ Vbh = a.v + b * a.L.v.b + h * a.L.v.h;
+    const int qrs = (int)a.L.q.t, krs = (int)a.L.k.t, vrs = (int)a.L.v.t;
 
     const int qw0 = i0 + 32 * wave;                  // this wave's first query
     const int qi = qw0 + lr;                         // this lane's query
@@ -261,9 +279,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // their outputs are never stored).
     bf16x8 qf[D / 16];
     {
-        const bf16* qp = Qbh + min(qi, T - 1) * D + 8 * hh;
+        const bf16* qp = Qbh + (int64_t)min(qi, T - 1) * qrs + 8 * hh;
 #pragma unroll
         for (int dc = 0; dc < D / 16; ++dc) qf[dc] = *reinterpret_cast<const bf16x8*>(qp + 16 * dc);
+    }
+    if (a.qneg) {
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc) qf[dc] = -qf[dc];
     }
     // Land Q before any tile load is issued: the compiler's own waits for
     // these registers would otherwise count (and drain) the tile loads.
@@ -285,13 +307,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // same number of loads and a fixed vmcnt waits for exactly the oldest.
     auto kslot = [&](int t) { return ring + ((t - t0) % C::R) * C::TILEB; };
     auto vslot = [&](int t) { return ring + (C::R + (t - t0) % C::R) * C::TILEB; };
+    uint32_t koff[C::NLD_W], voff[C::NLD_W];
+    tile_offsets<D, NW, false>(koff, wave, lane, 2 * krs);
+    tile_offsets<D, NW, true>(voff, wave, lane, 2 * vrs);
+    // bytes per key tile and per slab (the last row ends after D elements)
+    const int ktb = C::BN * 2 * krs, vtb = C::BN * 2 * vrs;
+    const int kslab = ((T - 1) * krs + D) * 2, vslab = ((T - 1) * vrs + D) * 2;
     auto load_k = [&](int t) {
-        dma_tile<D, NW, false>(rows_rsrc(Kbh, min(t, t1 - 1) * C::BN, T, D), lds_addr(kslot(t)),
-                               wave, lane);
+        dma_tile<D, NW>(rows_rsrc(Kbh, min(t, t1 - 1) * ktb, kslab), lds_addr(kslot(t)), wave,
+                        koff);
     };
     auto load_v = [&](int t) {
-        dma_tile<D, NW, true>(rows_rsrc(Vbh, min(t, t1 - 1) * C::BN, T, D), lds_addr(vslot(t)),
-                              wave, lane);
+        dma_tile<D, NW>(rows_rsrc(Vbh, min(t, t1 - 1) * vtb, vslab), lds_addr(vslot(t)), wave,
+                        voff);
     };
     // Publish loads: wait until at most VM_WAIT of this wave's loads are in
     // flight and its LDS reads are done, then barrier.  No fence is needed:
@@ -444,7 +472,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const float l = swap_sum(lsum);
     const float inv = 1.f / l;
     if (qi < T) {
-        bf16* orow = a.out + off + (int64_t)qi * D;
+        bf16* orow = a.out + b * a.L.o.b + h * a.L.o.h + (int64_t)qi * a.L.o.t;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -459,32 +487,57 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
 template <int D, int NW>
 hipError_t launch(const bf16* q, const bf16* k, const bf16* v, bf16* out, int64_t B,
-                  int64_t H, int64_t T, int64_t W, hipStream_t stream) {
+                  int64_t H, int64_t T, int64_t W, const Layout& L, float scale,
+                  hipStream_t stream) {
     using C = Cfg<D, NW>;
     Args a;
     a.q = q;
     a.k = k;
     a.v = v;
     a.out = out;
+    a.L = L;
+    a.H = (int)H;
     a.T = (int)T;
     a.W = (int)(W < T ? W : T);
     a.nqt = (int)((T + C::BM - 1) / C::BM);
     const int64_t nblocks = B * H * a.nqt;
     a.nblocks = (int)nblocks;
     a.remap = (nblocks % 8 == 0) ? 1 : 0;
-    a.c = kLog2e / sqrtf((float)D);
+    a.c = kLog2e * fabsf(scale);
+    a.qneg = scale < 0.f ? 1 : 0;
     void* args[] = {(void*)&a};
     return hipLaunchKernel((const void*)prefill_bf16_kernel<D, NW>, dim3((unsigned)nblocks),
                            dim3(C::NT), args, 0, stream);
 }
 
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+bool strides_ok(const Strides& s) {
+    return s.b >= 0 && s.h >= 0 && s.t >= 0 && s.b % 8 == 0 && s.h % 8 == 0 && s.t % 8 == 0 &&
+           s.t < ((int64_t)1 << 30);
+}
+
 }  // namespace
+
+bool prefill_bf16_supports(const void* q, const void* k, const void* v, const void* out,
+                           int64_t T, int64_t D, const Layout& L) {
+    if (D != 64 && D != 128) return false;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return false;
+    if (!strides_ok(L.q) || !strides_ok(L.k) || !strides_ok(L.v) || !strides_ok(L.o)) return false;
+    // rows past T must fall outside the buffer range of a k / v slab, and the
+    // slab must be addressable with 32-bit byte offsets
+    for (const Strides* s : {&L.k, &L.v}) {
+        if (s->t < D) return false;
+        if (((T - 1) * s->t + D) * 2 >= ((int64_t)1 << 31)) return false;
+    }
+    return T < ((int64_t)1 << 31);
+}
 
 hipError_t launch_prefill_bf16(const bf16* q, const bf16* k, const bf16* v, bf16* out,
                                int64_t B, int64_t H, int64_t T, int D, int64_t W,
-                               hipStream_t stream) {
-    if (D == 128) return launch<128, 4>(q, k, v, out, B, H, T, W, stream);
-    return launch<64, 4>(q, k, v, out, B, H, T, W, stream);
+                               const Layout& L, float scale, hipStream_t stream) {
+    if (D == 128) return launch<128, 4>(q, k, v, out, B, H, T, W, L, scale, stream);
+    return launch<64, 4>(q, k, v, out, B, H, T, W, L, scale, stream);
 }
 
 }  // namespace swa

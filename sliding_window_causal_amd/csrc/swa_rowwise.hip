@@ -61,16 +61,16 @@ struct RowAttn {
         __syncthreads();
     }
 
-    // Fold in keys [kbeg, kend) of the [*, D] matrices K, V.
-    __device__ void segment(const T* __restrict__ K, const T* __restrict__ V, int64_t kbeg,
-                            int64_t kend) {
+    // Fold in keys [kbeg, kend) of the matrices K, V (row strides ks, vs).
+    __device__ void segment(const T* __restrict__ K, int64_t ks, const T* __restrict__ V,
+                            int64_t vs, int64_t kbeg, int64_t kend) {
         const int lane = threadIdx.x;
         for (int64_t c0 = kbeg; c0 < kend; c0 += 64) {
             const int64_t j = c0 + lane;
             const bool valid = j < kend;
             float s = -__builtin_inff();
             if (valid) {
-                const T* kr = K + j * (int64_t)D;
+                const T* kr = K + j * ks;
                 float acc = 0.f;
                 for (int d = 0; d < D; ++d) acc = fmaf(qs[d], to_f32(kr[d]), acc);
                 s = acc * scale;
@@ -87,8 +87,8 @@ struct RowAttn {
                 const int d = lane + 64 * r;
                 if (d < D) {
                     float acc = o[r] * alpha;
-                    const T* vc = V + c0 * (int64_t)D + d;
-                    for (int jj = 0; jj < nk; ++jj) acc = fmaf(ps[jj], to_f32(vc[(int64_t)jj * D]), acc);
+                    const T* vc = V + c0 * vs + d;
+                    for (int jj = 0; jj < nk; ++jj) acc = fmaf(ps[jj], to_f32(vc[(int64_t)jj * vs]), acc);
                     o[r] = acc;
                 }
             }
@@ -107,30 +107,32 @@ struct RowAttn {
     }
 };
 
-// Attend query row `qrow` to keys [kbeg, kend) of the [*, D] matrices K, V.
+// Attend query row `qrow` to keys [kbeg, kend) of the matrices K, V (row
+// strides ks, vs).
 template <typename T>
-__device__ void attend_row(const T* __restrict__ qrow, const T* __restrict__ K,
-                           const T* __restrict__ V, int64_t kbeg, int64_t kend, int D,
-                           float scale, T* __restrict__ orow) {
+__device__ void attend_row(const T* __restrict__ qrow, const T* __restrict__ K, int64_t ks,
+                           const T* __restrict__ V, int64_t vs, int64_t kbeg, int64_t kend,
+                           int D, float scale, T* __restrict__ orow) {
     __shared__ float qs[kRowMaxD];
     __shared__ float ps[64];
     RowAttn<T> st;
     st.init(qrow, qs, ps, D, scale);
-    st.segment(K, V, kbeg, kend);
+    st.segment(K, ks, V, vs, kbeg, kend);
     st.finish(orow);
 }
 
 template <typename T>
 __global__ __launch_bounds__(64) void rowwise_prefill_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    T* __restrict__ out, int64_t Tn, int D, int64_t W, float scale) {
+    T* __restrict__ out, int64_t H, int64_t Tn, int D, int64_t W, Layout L, float scale) {
     const int64_t row = blockIdx.x;            // (b*H + h)*T + i
     const int64_t bh = row / Tn;
     const int64_t i = row - bh * Tn;
-    const int64_t base = bh * Tn * D;
+    const int64_t b = bh / H, h = bh - b * H;
     const int64_t kbeg = i - W + 1 > 0 ? i - W + 1 : 0;
-    attend_row<T>(q + base + i * D, k + base, v + base, kbeg, i + 1, D, scale,
-                  out + base + i * D);
+    attend_row<T>(q + b * L.q.b + h * L.q.h + i * L.q.t, k + b * L.k.b + h * L.k.h, L.k.t,
+                  v + b * L.v.b + h * L.v.h, L.v.t, kbeg, i + 1, D, scale,
+                  out + b * L.o.b + h * L.o.h + i * L.o.t);
 }
 
 template <typename T>
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(64) void rowwise_decode_kernel(
     int64_t n = p + 1;
     n = n < 0 ? 0 : (n > W ? W : n);
     const int64_t rbase = sh * W * D;
-    attend_row<T>(q + sh * D, kring + rbase, vring + rbase, 0, n, D, scale, out + sh * D);
+    attend_row<T>(q + sh * D, kring + rbase, D, vring + rbase, D, 0, n, D, scale, out + sh * D);
 }
 
 // Chunk continuation: query c of the chunk sits at absolute position
@@ -173,11 +175,11 @@ __global__ __launch_bounds__(64) void rowwise_chunk_kernel(
         const int64_t n = p0 - lo;             // < W
         const int64_t a = lo % W;
         const int64_t first = a + n <= W ? n : W - a;
-        st.segment(kring + rbase, vring + rbase, a, a + first);
-        if (first < n) st.segment(kring + rbase, vring + rbase, 0, n - first);
+        st.segment(kring + rbase, D, vring + rbase, D, a, a + first);
+        if (first < n) st.segment(kring + rbase, D, vring + rbase, D, 0, n - first);
     }
     const int64_t cb = lo > p0 ? lo - p0 : 0;  // chunk rows [cb, c]
-    st.segment(kc + cbase, vc + cbase, cb, c + 1);
+    st.segment(kc + cbase, D, vc + cbase, D, cb, c + 1);
     st.finish(out + cbase + c * D);
 }
 
@@ -198,12 +200,12 @@ hipError_t launch_rowwise_chunk(const T* q, const T* kc, const T* vc, const T* k
 
 template <typename T>
 hipError_t launch_rowwise_prefill(const T* q, const T* k, const T* v, T* out, int64_t B,
-                                  int64_t H, int64_t Tn, int D, int64_t W,
-                                  hipStream_t stream) {
+                                  int64_t H, int64_t Tn, int D, int64_t W, const Layout& L,
+                                  float scale, hipStream_t stream) {
     const int64_t rows = B * H * Tn;
-    float scale = 1.0f / sqrtf((float)D);
-    void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&out, (void*)&Tn,
-                    (void*)&D, (void*)&W, (void*)&scale};
+    Layout lay = L;
+    void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&out, (void*)&H, (void*)&Tn,
+                    (void*)&D, (void*)&W, (void*)&lay, (void*)&scale};
     return hipLaunchKernel((const void*)rowwise_prefill_kernel<T>, dim3((unsigned)rows),
                            dim3(64), args, 0, stream);
 }
@@ -222,10 +224,10 @@ hipError_t launch_rowwise_decode(const T* q, const T* kring, const T* vring,
 
 template hipError_t launch_rowwise_prefill<float>(const float*, const float*, const float*,
                                                   float*, int64_t, int64_t, int64_t, int,
-                                                  int64_t, hipStream_t);
+                                                  int64_t, const Layout&, float, hipStream_t);
 template hipError_t launch_rowwise_prefill<bf16>(const bf16*, const bf16*, const bf16*, bf16*,
                                                  int64_t, int64_t, int64_t, int, int64_t,
-                                                 hipStream_t);
+                                                 const Layout&, float, hipStream_t);
 template hipError_t launch_rowwise_chunk<float>(const float*, const float*, const float*,
                                                 const float*, const float*, const int64_t*, float*,
                                                 int64_t, int64_t, int64_t, int, int64_t, hipStream_t);

@@ -25,7 +25,8 @@ def _declared_functions():
 def test_header_declares_entry_points():
     names = _declared_functions()
     for n in ("swa_forward", "swa_decode", "swa_ring_append", "swa_status_string",
-              "swa_abi_version", "swa_chunk_forward", "swa_ring_append_chunk"):
+              "swa_abi_version", "swa_chunk_forward", "swa_ring_append_chunk",
+              "swa_forward_strided"):
         assert n in names
 
 
@@ -96,6 +97,52 @@ def test_append_invalid_args(kw):
 
 def test_append_unsupported_dtype():
     assert _app(dt=5) == swa.SWA_ERR_UNSUPPORTED
+
+
+CONTIG = (ctypes.c_int64 * 12)(*([4 * 8 * 64, 8 * 64, 64] * 4))
+
+
+def _fwds(q=DUMMY, k=DUMMY, v=DUMMY, o=DUMMY, B=1, H=4, T=8, D=64, W=4, st=CONTIG, scale=0.0,
+          dt=swa.SWA_BF16):
+    return swa.lib().swa_forward_strided(q, k, v, o, B, H, T, D, W, st, scale, dt, None)
+
+
+def _neg_stride(i):
+    a = list(CONTIG)
+    a[i] = -1
+    return (ctypes.c_int64 * 12)(*a)
+
+
+@pytest.mark.parametrize("kw", [dict(q=None), dict(o=None), dict(st=None), dict(B=0), dict(T=0),
+                                dict(W=0), dict(scale=float("nan")), dict(scale=float("inf")),
+                                dict(scale=-float("inf")), dict(st=_neg_stride(0)),
+                                dict(st=_neg_stride(5)), dict(st=_neg_stride(11))])
+def test_forward_strided_invalid_args(kw):
+    assert _fwds(**kw) == swa.SWA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(dt=5), dict(D=96), dict(D=32), dict(dt=swa.SWA_F32, D=257)])
+def test_forward_strided_unsupported(kw):
+    assert _fwds(**kw) == swa.SWA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("scale,exc", [(0, ValueError), (float("nan"), ValueError),
+                                       (float("inf"), ValueError), ("0.1", TypeError),
+                                       (True, TypeError)])
+def test_binding_rejects_bad_scale(scale, exc, monkeypatch):
+    # device checks are bypassed so that the scale check itself is reached
+    monkeypatch.setattr(swa, "_check_device", lambda *a, **k: None)
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(exc):
+        swa.swa_forward_strided(x, x, x, x.clone(), 4, scale=scale)
+
+
+def test_binding_rejects_bad_layout():
+    x = torch.zeros(1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        swa.sliding_window_attention(x, x, x, 4, layout="tbd")
+    with pytest.raises(ValueError):
+        swa.sliding_window_attention(x, x, x, 4, layout="bshd")
 
 
 def _chunk(q=DUMMY, kc=DUMMY, vc=DUMMY, kr=DUMMY, vr=DUMMY, pos=DUMMY, o=DUMMY, S=1, H=1, C=4,

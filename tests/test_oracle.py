@@ -410,6 +410,80 @@ def test_chunk_continues_ring():
 
 
 # ----------------------------------------------------------------------------
+# Explicit score scale [P3 Step 2: scores = q k^T * scale, default 1/sqrt(D)]
+# ----------------------------------------------------------------------------
+
+def _sdpa_scaled(q, k, v, scale, causal):
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    return torch.nn.functional.scaled_dot_product_attention(
+        t(q), t(k), t(v), is_causal=causal, scale=scale).numpy()
+
+
+@pytest.mark.parametrize("scale", [0.05, 0.7, 2.0])
+def test_scale_reduces_to_library_causal_attention(scale):
+    """W >= T with an explicit scale equals torch's SDPA given that scale
+    (torch's math path mishandles negative scales under its causal mask, so
+    those are pinned by the sign symmetry below)."""
+    r = _rng(21)
+    T, D = 13, 6
+    q, k, v = (r.standard_normal((2, 2, T, D)) for _ in range(3))
+    ref = _sdpa_scaled(q, k, v, scale, causal=True)
+    for fn in (lambda W: so.swa_dense(q, k, v, W, scale=scale),
+               lambda W: so.swa_rows(q, k, v, W, range(T), scale=scale)):
+        for W in (T, 2 * T):
+            assert np.max(np.abs(fn(W) - ref)) <= 1e-12
+
+
+def test_scale_default_is_inverse_sqrt_d_and_band_matches_library():
+    r = _rng(22)
+    T, D = 16, 8
+    q, k, v = (r.standard_normal((3, T, D)) for _ in range(3))
+    for W in (1, 4, 9):
+        a = so.swa_dense(q, k, v, W)
+        b = so.swa_dense(q, k, v, W, scale=1 / math.sqrt(D))
+        assert np.max(np.abs(a - b)) <= 1e-12
+        t = lambda x: torch.from_numpy(x)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            t(q), t(k), t(v), attn_mask=t(so.band_mask(T, W)), scale=0.37).numpy()
+        assert np.max(np.abs(so.swa_dense(q, k, v, W, scale=0.37) - ref)) <= 1e-12
+        rows = so.swa_rows(q, k, v, W, [0, 3, T - 1], scale=0.37)
+        assert np.max(np.abs(rows - ref[:, [0, 3, T - 1]])) <= 1e-12
+
+
+def test_negative_scale_is_negated_queries():
+    """scale = -s scores q . k * (-s) = (-q) . k * s; negating q is exact."""
+    r = _rng(24)
+    T, D = 10, 4
+    q, k, v = (r.standard_normal((2, T, D)) for _ in range(3))
+    for W in (2, 5, 10):
+        a = so.swa_dense(q, k, v, W, scale=-0.4)
+        b = so.swa_dense(-q, k, v, W, scale=0.4)
+        assert np.array_equal(a, b)
+        assert np.max(np.abs(so.swa_rows(q, k, v, W, range(T), scale=-0.4) - a)) <= 1e-12
+
+
+def test_scale_zero_is_trailing_moving_average():
+    """scale = 0 zeroes every score: uniform weights over the window, the
+    closed-form trailing mean of v."""
+    r = _rng(23)
+    T, D = 11, 3
+    q, k, v = (r.standard_normal((1, T, D)) for _ in range(3))
+    C = np.concatenate([np.zeros((1, 1, D)), np.cumsum(v, axis=1)], axis=1)
+    for W in (1, 3, 11):
+        lo = np.maximum(np.arange(T) - W + 1, 0)
+        n = (np.arange(T) - lo + 1)[None, :, None]
+        ref = (C[:, 1:] - C[:, lo]) / n
+        assert np.max(np.abs(so.swa_dense(q, k, v, W, scale=0.0) - ref)) <= 1e-12
+
+
+def test_nonfinite_scale_rejected():
+    x = np.zeros((1, 4, 2))
+    for bad in (float("nan"), float("inf")):
+        with pytest.raises(ValueError):
+            so.swa_dense(x, x, x, 2, scale=bad)
+
+
+# ----------------------------------------------------------------------------
 # Planted mistakes: each must make at least one pin fail
 # ----------------------------------------------------------------------------
 
