@@ -127,6 +127,57 @@ int swa_decode(const void* q, const void* kring, const void* vring,
                int dtype, void* stream);
 
 /*
+ * Bytes of device workspace that swa_decode_split and swa_decode_append need
+ * for these sizes (0: none), or a negative status (-SWA_ERR_INVALID_ARG for
+ * sizes < 1, -SWA_ERR_UNSUPPORTED for sizes too large to address).  The
+ * amount depends on the sizes and dtype only.
+ */
+int64_t swa_decode_workspace_bytes(int64_t S, int64_t H, int64_t D, int64_t W, int dtype);
+
+/*
+ * Decode as swa_decode, for few streams: when S * H workgroups would leave
+ * most of the GPU idle, each (stream, head)'s occupied slots are split over
+ * several workgroups that write partial (max, sum, unnormalised output)
+ * triples to `workspace`, and a second kernel merges them by rescaling each
+ * partial to the largest max (the running-max identity of the stable
+ * softmax in "Implementation: Sliding Window Attention", Step 2, applied to
+ * slot ranges instead of single keys).  Same result as swa_decode up to
+ * rounding order.
+ *
+ *   workspace       : device memory of at least swa_decode_workspace_bytes()
+ *                     bytes, 16-byte aligned, owned by the caller; may be
+ *                     null when that size is 0.  Contents on entry are
+ *                     ignored; concurrent calls need separate workspaces.
+ *   workspace_bytes : its size; too small (or null when needed) returns
+ *                     SWA_ERR_INVALID_ARG.
+ * Other arguments, layouts and dtypes as swa_decode (fp32, and bf16 windows
+ * over 16384 slots, run swa_decode's kernels and use no workspace).
+ */
+int swa_decode_split(const void* q, const void* kring, const void* vring, const int64_t* pos,
+                     void* out, int64_t S, int64_t H, int64_t D, int64_t W, int dtype,
+                     void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Append and decode in one launch: the current token's knew, vnew
+ * ([S, H, D]) go into ring slot pos mod W, as swa_ring_append does, and its
+ * query q attends to the ring including that token, as swa_decode does after
+ * the append (the bounded cache that evicts what falls out of the window,
+ * "25. Sliding-Window Causal Attention for Streaming Inference", Problem).
+ * The attention reads the current token from knew / vnew rather than from
+ * the slot being written, so the result does not depend on write ordering.
+ *
+ *   kring, vring : [S, H, W, D], written at slot pos[s] mod W of each stream
+ *   workspace    : as swa_decode_split
+ * A negative pos[s] writes slot pos mod W reduced into [0, W), as
+ * swa_ring_append does, and gives a zero output (no occupied slots).
+ * fp32, and bf16 windows over 16384 slots, run the append kernel and then
+ * swa_decode's kernels, in stream order.
+ */
+int swa_decode_append(const void* q, const void* knew, const void* vnew, void* kring, void* vring,
+                      const int64_t* pos, void* out, int64_t S, int64_t H, int64_t D, int64_t W,
+                      int dtype, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * Ring append (not part of the timed path): for every stream s and head h,
  * kring[s, h, pos[s] mod W, :] = knew[s, h, :] and the same for v.
  *

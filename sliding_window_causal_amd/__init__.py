@@ -11,13 +11,18 @@ Entry points (same names as the C ABI):
                                                  prefill over strided [B, H, T, D] views
   swa_decode(q, kring, vring, pos, out)          decode against a W-slot ring
   swa_ring_append(knew, vnew, kring, vring, pos) write position pos into slot pos mod W
+  swa_decode_workspace_bytes(S, H, D, W, dtype)  workspace of the two entries below
+  swa_decode_split(q, kring, vring, pos, out)    decode, window split over workgroups
+  swa_decode_append(q, knew, vnew, kring, vring, pos, out)
+                                                 append + decode in one launch
   swa_chunk_forward(q, kc, vc, kring, vring, pos0, out)
                                                  chunk of new tokens continuing a ring
   swa_ring_append_chunk(kc, vc, kring, vring, pos0)
                                                  write a chunk's tokens into the ring
 Conveniences that allocate the output with torch:
   sliding_window_attention(q, k, v, window_size, scale=None, layout=None) -> out
-  decode(q, kring, vring, pos) -> out
+  decode(q, kring, vring, pos, split=False) -> out
+  decode_append(q, knew, vnew, kring, vring, pos) -> out
   chunk_attention(q, kc, vc, kring, vring, pos0) -> out
 """
 
@@ -32,7 +37,8 @@ __all__ = [
     "LIB_PATH", "SWA_F32", "SWA_BF16", "SWA_OK", "SWA_ERR_INVALID_ARG",
     "SWA_ERR_UNSUPPORTED", "SWA_ERR_LAUNCH", "SWAError", "lib", "abi_version",
     "status_string", "swa_forward", "swa_forward_strided", "swa_decode", "swa_ring_append", "swa_chunk_forward",
-    "swa_ring_append_chunk", "sliding_window_attention", "decode", "chunk_attention",
+    "swa_ring_append_chunk", "swa_decode_workspace_bytes", "swa_decode_split",
+    "swa_decode_append", "sliding_window_attention", "decode", "decode_append", "chunk_attention",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa.so")
@@ -74,6 +80,12 @@ def lib() -> ctypes.CDLL:
     L.swa_decode.restype = i32
     L.swa_ring_append.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, p]
     L.swa_ring_append.restype = i32
+    L.swa_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
+    L.swa_decode_workspace_bytes.restype = i64
+    L.swa_decode_split.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, p, i64, p]
+    L.swa_decode_split.restype = i32
+    L.swa_decode_append.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, p, i64, p]
+    L.swa_decode_append.restype = i32
     L.swa_chunk_forward.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i32, p]
     L.swa_chunk_forward.restype = i32
     L.swa_ring_append_chunk.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i32, p]
@@ -187,6 +199,61 @@ def swa_decode(q, kring, vring, pos, out, stream=None) -> None:
                             code, _stream(q, stream)))
 
 
+def swa_decode_workspace_bytes(S: int, H: int, D: int, W: int, dtype) -> int:
+    """Device workspace bytes swa_decode_split / swa_decode_append need (0: none)."""
+    code = _DTYPES.get(dtype, dtype) if not isinstance(dtype, int) else dtype
+    n = int(lib().swa_decode_workspace_bytes(S, H, D, W, code))
+    if n < 0:
+        raise SWAError(-n, status_string(-n))
+    return n
+
+
+def _decode_dims(q, kring, vring, pos, out):
+    if q.dim() != 3 or kring.dim() != 4 or vring.shape != kring.shape or out.shape != q.shape:
+        raise ValueError("q/out must be [S, H, D] and rings [S, H, W, D]")
+    S, H, D = q.shape
+    if kring.shape[0] != S or kring.shape[1] != H or kring.shape[3] != D:
+        raise ValueError("ring shape does not match q")
+    if pos.dtype != torch.int64 or pos.shape != (S,):
+        raise ValueError("pos must be int64 [S]")
+    return S, H, D, kring.shape[2]
+
+
+def _workspace(q, S, H, D, W, workspace):
+    need = swa_decode_workspace_bytes(S, H, D, W, _DTYPES[q.dtype])
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def swa_decode_split(q, kring, vring, pos, out, workspace=None, stream=None) -> None:
+    """swa_decode with the window split over several workgroups when S * H is
+    small; ``workspace`` (bytes from swa_decode_workspace_bytes) is allocated
+    here when not given."""
+    _check_device(q, kring, vring, pos, out)
+    code = _dtype_code(q, kring, vring, out)
+    S, H, D, W = _decode_dims(q, kring, vring, pos, out)
+    ws, nb = _workspace(q, S, H, D, W, workspace)
+    _check(lib().swa_decode_split(_ptr(q), _ptr(kring), _ptr(vring), _ptr(pos), _ptr(out), S, H,
+                                  D, W, code, _ptr(ws), nb, _stream(q, stream)))
+
+
+def swa_decode_append(q, knew, vnew, kring, vring, pos, out, workspace=None, stream=None) -> None:
+    """Write knew, vnew ([S, H, D]) into slot pos mod W and decode q against
+    the ring including them, in one launch."""
+    _check_device(q, knew, vnew, kring, vring, pos, out)
+    code = _dtype_code(q, knew, vnew, kring, vring, out)
+    S, H, D, W = _decode_dims(q, kring, vring, pos, out)
+    if knew.shape != q.shape or vnew.shape != q.shape:
+        raise ValueError("knew, vnew must be [S, H, D] like q")
+    ws, nb = _workspace(q, S, H, D, W, workspace)
+    _check(lib().swa_decode_append(_ptr(q), _ptr(knew), _ptr(vnew), _ptr(kring), _ptr(vring),
+                                   _ptr(pos), _ptr(out), S, H, D, W, code, _ptr(ws), nb,
+                                   _stream(q, stream)))
+
+
 def swa_ring_append(knew, vnew, kring, vring, pos, stream=None) -> None:
     """kring[s, h, pos[s] mod W] = knew[s, h] (and v); knew [S, H, D]."""
     _check_device(knew, vnew, kring, vring, pos)
@@ -274,8 +341,18 @@ def sliding_window_attention(q, k, v, window_size: int, scale=None, layout: str 
     return out
 
 
-def decode(q, kring, vring, pos):
-    """Decode returning a new [S, H, D] tensor."""
+def decode(q, kring, vring, pos, split: bool = False):
+    """Decode returning a new [S, H, D] tensor (split: swa_decode_split)."""
     out = torch.empty_like(q)
-    swa_decode(q, kring, vring, pos, out)
+    if split:
+        swa_decode_split(q, kring, vring, pos, out)
+    else:
+        swa_decode(q, kring, vring, pos, out)
+    return out
+
+
+def decode_append(q, knew, vnew, kring, vring, pos):
+    """Fused append + decode returning a new [S, H, D] tensor."""
+    out = torch.empty_like(q)
+    swa_decode_append(q, knew, vnew, kring, vring, pos, out)
     return out

@@ -107,7 +107,8 @@ int swa_decode(const void* q, const void* kring, const void* vring, const int64_
         if (W <= swa::kDecodeMaxW)
             return from_hip(swa::launch_decode_bf16((const swa::bf16*)q, (const swa::bf16*)kring,
                                                     (const swa::bf16*)vring, pos, (swa::bf16*)out,
-                                                    S, H, (int)D, W, st));
+                                                    S, H, (int)D, W, nullptr, nullptr, nullptr,
+                                                    st));
         return from_hip(swa::launch_rowwise_decode<swa::bf16>(
             (const swa::bf16*)q, (const swa::bf16*)kring, (const swa::bf16*)vring, pos,
             (swa::bf16*)out, S, H, (int)D, W, st));
@@ -119,6 +120,70 @@ int swa_decode(const void* q, const void* kring, const void* vring, const int64_
                                                           H, (int)D, W, st));
     }
     return SWA_ERR_UNSUPPORTED;
+}
+
+int64_t swa_decode_workspace_bytes(int64_t S, int64_t H, int64_t D, int64_t W, int dtype) {
+    if (!positive(S) || !positive(H) || !positive(D) || !positive(W)) return -SWA_ERR_INVALID_ARG;
+    if (!fits(S, H, W, D)) return -SWA_ERR_UNSUPPORTED;
+    if (dtype != SWA_BF16 || (D != 64 && D != 128) || W > swa::kDecodeMaxW) return 0;
+    return swa::decode_workspace_bytes(S, H, D, W);
+}
+
+namespace {
+
+// Shared checks of the workspace-taking decode entries; returns SWA_OK or a
+// status, and sets *split when the split-window bf16 kernel applies.
+int check_decode_ws(int64_t S, int64_t H, int64_t D, int64_t W, int dtype, const void* ws,
+                    int64_t ws_bytes, bool* split) {
+    if (!positive(S) || !positive(H) || !positive(D) || !positive(W)) return SWA_ERR_INVALID_ARG;
+    if (ws_bytes < 0) return SWA_ERR_INVALID_ARG;
+    if (!fits(S, H, W, D) || S * H * swa::kDecMaxSplits >= ((int64_t)1 << 31))
+        return SWA_ERR_UNSUPPORTED;
+    if (dtype != SWA_F32 && dtype != SWA_BF16) return SWA_ERR_UNSUPPORTED;
+    if (dtype == SWA_BF16 && D != 64 && D != 128) return SWA_ERR_UNSUPPORTED;
+    if (dtype == SWA_F32 && D > kMaxRowD) return SWA_ERR_UNSUPPORTED;
+    const int64_t need = swa_decode_workspace_bytes(S, H, D, W, dtype);
+    if (need > 0 && (!ws || ws_bytes < need || ((uintptr_t)ws & 15) != 0))
+        return SWA_ERR_INVALID_ARG;
+    *split = dtype == SWA_BF16 && W <= swa::kDecodeMaxW;
+    return SWA_OK;
+}
+
+}  // namespace
+
+int swa_decode_split(const void* q, const void* kring, const void* vring, const int64_t* pos,
+                     void* out, int64_t S, int64_t H, int64_t D, int64_t W, int dtype,
+                     void* workspace, int64_t workspace_bytes, void* stream) {
+    if (!q || !kring || !vring || !pos || !out) return SWA_ERR_INVALID_ARG;
+    bool split = false;
+    const int rc = check_decode_ws(S, H, D, W, dtype, workspace, workspace_bytes, &split);
+    if (rc != SWA_OK) return rc;
+    if (!split) return swa_decode(q, kring, vring, pos, out, S, H, D, W, dtype, stream);
+    return from_hip(swa::launch_decode_bf16(
+        (const swa::bf16*)q, (const swa::bf16*)kring, (const swa::bf16*)vring, pos,
+        (swa::bf16*)out, S, H, (int)D, W, nullptr, nullptr,
+        swa_decode_workspace_bytes(S, H, D, W, dtype) > 0 ? workspace : nullptr,
+        (hipStream_t)stream));
+}
+
+int swa_decode_append(const void* q, const void* knew, const void* vnew, void* kring, void* vring,
+                      const int64_t* pos, void* out, int64_t S, int64_t H, int64_t D, int64_t W,
+                      int dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (!q || !knew || !vnew || !kring || !vring || !pos || !out) return SWA_ERR_INVALID_ARG;
+    bool split = false;
+    const int rc = check_decode_ws(S, H, D, W, dtype, workspace, workspace_bytes, &split);
+    if (rc != SWA_OK) return rc;
+    if (!split) {
+        // no fused kernel for this shape: append, then decode, in stream order
+        const int r = swa_ring_append(knew, vnew, kring, vring, pos, S, H, D, W, dtype, stream);
+        if (r != SWA_OK) return r;
+        return swa_decode(q, kring, vring, pos, out, S, H, D, W, dtype, stream);
+    }
+    return from_hip(swa::launch_decode_bf16(
+        (const swa::bf16*)q, (const swa::bf16*)kring, (const swa::bf16*)vring, pos,
+        (swa::bf16*)out, S, H, (int)D, W, (const swa::bf16*)knew, (const swa::bf16*)vnew,
+        swa_decode_workspace_bytes(S, H, D, W, dtype) > 0 ? workspace : nullptr,
+        (hipStream_t)stream));
 }
 
 int swa_ring_append(const void* knew, const void* vnew, void* kring, void* vring,

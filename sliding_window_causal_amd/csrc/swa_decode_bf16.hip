@@ -48,10 +48,30 @@ __device__ inline float dot8(const u32x4& k, const u32x4& q, float acc) {
 __device__ inline float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ inline float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
+// Arguments of one decode launch.  A launch has S * H * P workgroups: split
+// sp of (stream, head) sh covers the occupied slots [sp * chunk,
+// min(n, (sp + 1) * chunk)).  With P = 1 the workgroup writes the output;
+// otherwise it writes its unnormalised partial output, max and sum to the
+// workspace and decode_combine_kernel merges the P partials.
+struct DecArgs {
+    const bf16* q;
+    const bf16* kring;
+    const bf16* vring;
+    const int64_t* pos;
+    bf16* out;
+    const bf16* knew;     // fused append: k, v of the current token ([S, H, D]), else null
+    const bf16* vnew;
+    bf16* kring_w;        // the rings again, writable (fused append only)
+    bf16* vring_w;
+    float* ws_o;          // [S * H * P, D] partial outputs (P > 1)
+    float* ws_ml;         // [S * H * P, 2] partial (max, sum) (P > 1)
+    int64_t H, W;
+    int P, chunk;
+    float c;              // log2(e) / sqrt(D)
+};
+
 template <int D>
-__global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ kring, const bf16* __restrict__ vring,
-    const int64_t* __restrict__ pos, bf16* __restrict__ out, int64_t H, int64_t W, float c) {
+__global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a) {
     constexpr int CPL = D / 32;                 // 16-byte chunks per lane per row
     extern __shared__ __attribute__((aligned(16))) float sm[];
     float* sc = sm;                             // scores / probabilities, later partial outputs
@@ -60,31 +80,60 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(
     const int tid = threadIdx.x;
     const int quad = tid >> 2, sig = tid & 3;
     const int wave = tid >> 6, lane = tid & 63;
-    const int64_t sh = blockIdx.x;
-    const int64_t s = sh / H;
-    const int64_t p = pos[s];
+    const int64_t bid = blockIdx.x;
+    const int64_t sh = bid / a.P;
+    const int sp = (int)(bid - sh * a.P);
+    const int64_t s = sh / a.H;
+    const int64_t p = a.pos[s];
+    const int64_t W = a.W;
     int64_t n64 = p + 1;
     n64 = n64 < 0 ? 0 : (n64 > W ? W : n64);
     const int n = (int)n64;
-    const bf16* __restrict__ Kr = kring + sh * W * D;
-    const bf16* __restrict__ Vr = vring + sh * W * D;
+    const int lo = sp * a.chunk;
+    const int hi = min(n, lo + a.chunk);       // rows [lo, hi); empty when lo >= hi
+    const int cnt = hi > lo ? hi - lo : 0;
+    const bf16* __restrict__ Kr = a.kring + sh * W * D;
+    const bf16* __restrict__ Vr = a.vring + sh * W * D;
+    // Fused append: slot p mod W holds the current token, read from knew /
+    // vnew instead of the ring (which this launch writes).
+    // The slot is written by the one split that covers it (split 0 for a
+    // negative position, which has no occupied slots: the slot index is
+    // reduced into [0, W) as the plain append does).
+    int wslot = -1;
+    const bf16* __restrict__ Kn = nullptr;
+    const bf16* __restrict__ Vn = nullptr;
+    if (a.knew != nullptr) {
+        int64_t w64 = p % W;
+        w64 = w64 < 0 ? w64 + W : w64;
+        const int wsl = (int)w64;
+        Kn = a.knew + sh * D;
+        Vn = a.vnew + sh * D;
+        if (p >= 0) wslot = wsl;                // always inside [0, n)
+        const bool owner = p >= 0 ? (wsl >= lo && wsl < hi) : sp == 0;
+        if (owner && tid < D / 8) {
+            const int64_t dst = (sh * W + wsl) * D + tid * 8;
+            *reinterpret_cast<u32x4*>(a.kring_w + dst) = *reinterpret_cast<const u32x4*>(Kn + tid * 8);
+            *reinterpret_cast<u32x4*>(a.vring_w + dst) = *reinterpret_cast<const u32x4*>(Vn + tid * 8);
+        }
+    }
 
     // query chunks 4 i + sig
     u32x4 qv[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
-        qv[i] = *reinterpret_cast<const u32x4*>(q + sh * D + (4 * i + sig) * 8);
+        qv[i] = *reinterpret_cast<const u32x4*>(a.q + sh * D + (4 * i + sig) * 8);
 
     // ---- phase 1: scores
-    for (int r0 = 0; r0 < n; r0 += kQuads * kUnroll) {
+    for (int r0 = lo; r0 < hi; r0 += kQuads * kUnroll) {
         u32x4 kv[kUnroll][CPL];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int row = r0 + quad + kQuads * u;
+            const bf16* src = row == wslot ? Kn : Kr + (int64_t)row * D;
 #pragma unroll
             for (int i = 0; i < CPL; ++i)
-                kv[u][i] = row < n ? *reinterpret_cast<const u32x4*>(Kr + (int64_t)row * D + (4 * i + sig) * 8)
-                                   : u32x4{0, 0, 0, 0};
+                kv[u][i] = row < hi ? *reinterpret_cast<const u32x4*>(src + (4 * i + sig) * 8)
+                                    : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
@@ -93,14 +142,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(
 #pragma unroll
             for (int i = 0; i < CPL; ++i) acc = dot8(kv[u][i], qv[i], acc);
             acc = quad_sum(acc);
-            if (sig == 0 && row < n) sc[row] = acc * c;
+            if (sig == 0 && row < hi) sc[row - lo] = acc * a.c;
         }
     }
     __syncthreads();
 
-    // ---- softmax over the n scores: max, then exp2 and sum
+    // ---- softmax over the cnt scores: max, then exp2 and sum
     float mx = -__builtin_inff();
-    for (int r = tid; r < n; r += kDecThreads) mx = fmaxf(mx, sc[r]);
+    for (int r = tid; r < cnt; r += kDecThreads) mx = fmaxf(mx, sc[r]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
     if (lane == 0) red[wave] = mx;
@@ -108,7 +157,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(
     mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     __syncthreads();
     float ls = 0.f;
-    for (int r = tid; r < n; r += kDecThreads) {
+    for (int r = tid; r < cnt; r += kDecThreads) {
         const float e = __builtin_amdgcn_exp2f(sc[r] - mx);
         sc[r] = e;
         ls += e;
@@ -125,20 +174,21 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(
     for (int i = 0; i < CPL; ++i)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
-    for (int r0 = 0; r0 < n; r0 += kQuads * kUnroll) {
+    for (int r0 = lo; r0 < hi; r0 += kQuads * kUnroll) {
         u32x4 vv[kUnroll][CPL];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int row = r0 + quad + kQuads * u;
+            const bf16* src = row == wslot ? Vn : Vr + (int64_t)row * D;
 #pragma unroll
             for (int i = 0; i < CPL; ++i)
-                vv[u][i] = row < n ? *reinterpret_cast<const u32x4*>(Vr + (int64_t)row * D + (4 * i + sig) * 8)
-                                   : u32x4{0, 0, 0, 0};
+                vv[u][i] = row < hi ? *reinterpret_cast<const u32x4*>(src + (4 * i + sig) * 8)
+                                    : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int row = r0 + quad + kQuads * u;
-            const float pr = row < n ? sc[row] : 0.f;
+            const float pr = row < hi ? sc[row - lo] : 0.f;
 #pragma unroll
             for (int i = 0; i < CPL; ++i)
 #pragma unroll
@@ -159,14 +209,50 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(
     if (tid < D) {
         float t = 0.f;
         for (int qd = 0; qd < kQuads; ++qd) t += sm[qd * D + tid];
-        out[sh * D + tid] = (bf16)(n > 0 ? t / l : 0.f);
+        if (a.P == 1) {
+            a.out[sh * D + tid] = (bf16)(cnt > 0 ? t / l : 0.f);
+        } else {
+            a.ws_o[bid * D + tid] = t;
+            if (tid == 0) {
+                a.ws_ml[2 * bid] = mx;          // -inf for an empty split
+                a.ws_ml[2 * bid + 1] = l;
+            }
+        }
     }
 }
 
+// Merge the P partials of each (stream, head): with M the largest partial
+// max, o = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.  Empty splits
+// (m_p = -inf) get weight 0; a stream with no occupied slot gets 0.
 template <int D>
-hipError_t launch(const bf16* q, const bf16* kring, const bf16* vring, const int64_t* pos,
-                  bf16* out, int64_t S, int64_t H, int64_t W, hipStream_t stream) {
-    const int64_t floats = W > (int64_t)kQuads * D ? W : (int64_t)kQuads * D;
+__global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ ws_o,
+                                                            const float* __restrict__ ws_ml,
+                                                            bf16* __restrict__ out, int P) {
+    const int64_t sh = blockIdx.x;
+    const float* ml = ws_ml + 2 * sh * P;
+    float M = -__builtin_inff();
+    for (int p = 0; p < P; ++p) M = fmaxf(M, ml[2 * p]);
+    float L = 0.f;
+    float o[D / 64];
+#pragma unroll
+    for (int r = 0; r < D / 64; ++r) o[r] = 0.f;
+    for (int p = 0; p < P; ++p) {
+        const float m = ml[2 * p];
+        if (m == -__builtin_inff()) continue;
+        const float w = __builtin_amdgcn_exp2f(m - M);
+        L = fmaf(w, ml[2 * p + 1], L);
+#pragma unroll
+        for (int r = 0; r < D / 64; ++r)
+            o[r] = fmaf(w, ws_o[(sh * P + p) * D + threadIdx.x + 64 * r], o[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < D / 64; ++r)
+        out[sh * D + threadIdx.x + 64 * r] = (bf16)(L > 0.f ? o[r] / L : 0.f);
+}
+
+template <int D>
+hipError_t launch(DecArgs a, int64_t S, hipStream_t stream) {
+    const int64_t floats = a.chunk > kQuads * D ? (int64_t)a.chunk : (int64_t)kQuads * D;
     const unsigned lds = (unsigned)(floats * sizeof(float));
     static bool attr_set = false;
     if (!attr_set) {
@@ -176,11 +262,18 @@ hipError_t launch(const bf16* q, const bf16* kring, const bf16* vring, const int
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    float c = kLog2e / sqrtf((float)D);
-    void* args[] = {(void*)&q, (void*)&kring, (void*)&vring, (void*)&pos, (void*)&out,
-                    (void*)&H, (void*)&W, (void*)&c};
-    return hipLaunchKernel((const void*)decode_bf16_kernel<D>, dim3((unsigned)(S * H)),
-                           dim3(kDecThreads), args, lds, stream);
+    a.c = kLog2e / sqrtf((float)D);
+    void* args[] = {(void*)&a};
+    hipError_t e = hipLaunchKernel((const void*)decode_bf16_kernel<D>,
+                                   dim3((unsigned)(S * a.H * a.P)), dim3(kDecThreads), args, lds,
+                                   stream);
+    if (e != hipSuccess || a.P == 1) return e;
+    const float* wo = a.ws_o;
+    const float* wml = a.ws_ml;
+    int P = a.P;
+    void* cargs[] = {(void*)&wo, (void*)&wml, (void*)&a.out, (void*)&P};
+    return hipLaunchKernel((const void*)decode_combine_kernel<D>, dim3((unsigned)(S * a.H)),
+                           dim3(64), cargs, 0, stream);
 }
 
 // ---- ring append -----------------------------------------------------------
@@ -251,11 +344,49 @@ hipError_t launch_ring_append_chunk(const void* kc, const void* vc, void* kring,
                            stream);
 }
 
+int decode_splits(int64_t S, int64_t H, int64_t W) {
+    // Splitting pays while S * H workgroups leave most compute units idle
+    // (measured at D = 128, W = 4096: 2.3x at S * H = 32, 1.7x at 64, none
+    // from 128 on).  Aim for kDecSplitTargetWGs workgroups with at least
+    // kDecSplitMinSlots slots each (smaller splits measured slower).
+    const int64_t sh = S * H;
+    if (sh >= kDecSplitTargetWGs / 4) return 1;
+    int64_t p = (kDecSplitTargetWGs + sh - 1) / sh;
+    const int64_t pmax = (W + kDecSplitMinSlots - 1) / kDecSplitMinSlots;
+    p = p < pmax ? p : pmax;
+    p = p < kDecMaxSplits ? p : kDecMaxSplits;
+    return p < 1 ? 1 : (int)p;
+}
+
+int64_t decode_workspace_bytes(int64_t S, int64_t H, int64_t D, int64_t W) {
+    const int P = decode_splits(S, H, W);
+    return P == 1 ? 0 : S * H * P * (D + 2) * (int64_t)sizeof(float);
+}
+
 hipError_t launch_decode_bf16(const bf16* q, const bf16* kring, const bf16* vring,
                               const int64_t* pos, bf16* out, int64_t S, int64_t H, int D,
-                              int64_t W, hipStream_t stream) {
-    if (D == 128) return launch<128>(q, kring, vring, pos, out, S, H, W, stream);
-    return launch<64>(q, kring, vring, pos, out, S, H, W, stream);
+                              int64_t W, const bf16* knew, const bf16* vnew, void* workspace,
+                              hipStream_t stream) {
+    DecArgs a = {};
+    a.q = q;
+    a.kring = kring;
+    a.vring = vring;
+    a.pos = pos;
+    a.out = out;
+    a.knew = knew;
+    a.vnew = vnew;
+    a.kring_w = const_cast<bf16*>(kring);
+    a.vring_w = const_cast<bf16*>(vring);
+    a.H = H;
+    a.W = W;
+    a.P = workspace ? decode_splits(S, H, W) : 1;
+    a.chunk = (int)((W + a.P - 1) / a.P);
+    if (a.P > 1) {
+        a.ws_o = (float*)workspace;
+        a.ws_ml = a.ws_o + S * H * a.P * D;
+    }
+    if (D == 128) return launch<128>(a, S, stream);
+    return launch<64>(a, S, stream);
 }
 
 hipError_t launch_ring_append(const void* knew, const void* vnew, void* kring, void* vring,

@@ -58,11 +58,21 @@ hipError_t launch_prefill_bf16(const bf16* q, const bf16* k, const bf16* v, bf16
                                int64_t B, int64_t H, int64_t T, int D, int64_t W,
                                const Layout& L, float scale, hipStream_t stream);
 
-// bf16 ring decode; D in {64, 128}, W <= kDecodeMaxW.
+// bf16 ring decode; D in {64, 128}, W <= kDecodeMaxW.  With a workspace of
+// decode_workspace_bytes(S, H, D, W) bytes the window may be split over
+// decode_splits(S, H, W) workgroups per (stream, head) and merged by a second
+// kernel; with knew / vnew the current token's k, v are read from there and
+// written into slot pos mod W by the same launch.
 constexpr int64_t kDecodeMaxW = 16384;
+constexpr int64_t kDecSplitTargetWGs = 512;
+constexpr int64_t kDecSplitMinSlots = 256;
+constexpr int64_t kDecMaxSplits = 64;
+int decode_splits(int64_t S, int64_t H, int64_t W);
+int64_t decode_workspace_bytes(int64_t S, int64_t H, int64_t D, int64_t W);
 hipError_t launch_decode_bf16(const bf16* q, const bf16* kring, const bf16* vring,
                               const int64_t* pos, bf16* out, int64_t S, int64_t H, int D,
-                              int64_t W, hipStream_t stream);
+                              int64_t W, const bf16* knew, const bf16* vnew, void* workspace,
+                              hipStream_t stream);
 
 // Chunk append into the ring; any D >= 1; elem_bytes is 2 or 4.
 hipError_t launch_ring_append_chunk(const void* kc, const void* vc, void* kring, void* vring,

@@ -26,7 +26,8 @@ def test_header_declares_entry_points():
     names = _declared_functions()
     for n in ("swa_forward", "swa_decode", "swa_ring_append", "swa_status_string",
               "swa_abi_version", "swa_chunk_forward", "swa_ring_append_chunk",
-              "swa_forward_strided"):
+              "swa_forward_strided", "swa_decode_workspace_bytes", "swa_decode_split",
+              "swa_decode_append"):
         assert n in names
 
 
@@ -143,6 +144,42 @@ def test_binding_rejects_bad_layout():
         swa.sliding_window_attention(x, x, x, 4, layout="tbd")
     with pytest.raises(ValueError):
         swa.sliding_window_attention(x, x, x, 4, layout="bshd")
+
+
+def _dsplit(ws=DUMMY, nb=1 << 30, S=1, H=4, D=128, W=4096, dt=swa.SWA_BF16, q=DUMMY):
+    return swa.lib().swa_decode_split(q, DUMMY, DUMMY, DUMMY, DUMMY, S, H, D, W, dt, ws, nb, None)
+
+
+def _dapp(ws=DUMMY, nb=1 << 30, S=1, H=4, D=128, W=4096, dt=swa.SWA_BF16, kn=DUMMY):
+    return swa.lib().swa_decode_append(DUMMY, kn, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, S, H, D, W,
+                                       dt, ws, nb, None)
+
+
+def test_decode_workspace_bytes():
+    L = swa.lib()
+    need = L.swa_decode_workspace_bytes(1, 4, 128, 4096, swa.SWA_BF16)
+    assert need > 0 and need % 4 == 0
+    assert L.swa_decode_workspace_bytes(1024, 4, 128, 4096, swa.SWA_BF16) == 0
+    assert L.swa_decode_workspace_bytes(1, 4, 128, 4096, swa.SWA_F32) == 0
+    assert L.swa_decode_workspace_bytes(0, 4, 128, 4096, swa.SWA_BF16) == -swa.SWA_ERR_INVALID_ARG
+    assert L.swa_decode_workspace_bytes(1, 4, 128, -1, swa.SWA_BF16) == -swa.SWA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("fn", [_dsplit, _dapp])
+@pytest.mark.parametrize("kw", [dict(ws=None), dict(nb=16), dict(nb=-1),
+                                dict(ws=ctypes.c_void_p(0x1004)), dict(S=0), dict(W=0)])
+def test_decode_workspace_entries_reject(fn, kw):
+    assert fn(**kw) == swa.SWA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("fn", [_dsplit, _dapp])
+@pytest.mark.parametrize("kw", [dict(dt=3), dict(D=96), dict(dt=swa.SWA_F32, D=300)])
+def test_decode_workspace_entries_unsupported(fn, kw):
+    assert fn(**kw) == swa.SWA_ERR_UNSUPPORTED
+
+
+def test_decode_append_rejects_null_token():
+    assert _dapp(kn=None) == swa.SWA_ERR_INVALID_ARG
 
 
 def _chunk(q=DUMMY, kc=DUMMY, vc=DUMMY, kr=DUMMY, vr=DUMMY, pos=DUMMY, o=DUMMY, S=1, H=1, C=4,
