@@ -59,6 +59,22 @@ def decode_bytes(S, H, D, n, elem=2) -> int:
     return 2 * S * H * n * D * elem + 2 * S * H * D * elem
 
 
+def time_launches(fn, stream, reps: int, warmup: int = 10) -> float:
+    """Mean ms of one fn() call over reps back-to-back calls (HIP events on
+    the launching stream)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def source_sha(paths) -> str:
     h = hashlib.sha256()
     for p in paths:
@@ -253,6 +269,26 @@ def main() -> int:
         }
         if not do_p:
             res["value"], res["unit"] = gbs, "GB/s"
+        # Latency of one decode token for a single stream (32 heads, full
+        # 4096-slot rings): one workgroup per head, the window split over
+        # workgroups, and the fused append + split decode.
+        q1, kr1, vr1, pos1 = si.decode_inputs(1, wd.H, wd.D, wd.W, torch.bfloat16, wd.seed, dev)
+        o1 = torch.empty_like(q1)
+        kn1, vn1 = q1.clone(), q1.clone()
+        nws = swa.swa_decode_workspace_bytes(1, wd.H, wd.D, wd.W, torch.bfloat16)
+        ws1 = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+        b1 = decode_bytes(1, wd.H, wd.D, wd.W)
+        t_plain = time_launches(lambda: swa.swa_decode(q1, kr1, vr1, pos1, o1, stream=stream),
+                                stream, 100)
+        t_split = time_launches(lambda: swa.swa_decode_split(q1, kr1, vr1, pos1, o1, ws1,
+                                                             stream=stream), stream, 100)
+        t_fused = time_launches(lambda: swa.swa_decode_append(q1, kn1, vn1, kr1, vr1, pos1, o1,
+                                                              ws1, stream=stream), stream, 100)
+        res["decode"]["single_stream"] = {
+            "S": 1, "H": wd.H, "D": wd.D, "W": wd.W, "workspace_bytes": nws,
+            "us_one_wg_per_head": t_plain * 1e3, "us_split": t_split * 1e3,
+            "us_fused_append_split": t_fused * 1e3,
+            "GBs_split": b1 / (t_split * 1e-3) / 1e9}
     if do_p and args.only == "all" and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(q, k, v, wp.W, args.cpu_seconds)
     res["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
