@@ -289,6 +289,25 @@ def main() -> int:
             "us_one_wg_per_head": t_plain * 1e3, "us_split": t_split * 1e3,
             "us_fused_append_split": t_fused * 1e3,
             "GBs_split": b1 / (t_split * 1e-3) / 1e9}
+    if do_p and args.only == "all":
+        # Chunked prefill continuing full 4096-slot rings (the streaming
+        # path): 2048 new tokens of one stream, and 512 of four, 32 heads,
+        # D = 128; every query sees W keys.
+        res["chunk"] = []
+        for S, Cn in ((1, 2048), (4, 512)):
+            gc = si.generator(wp.seed, dev)
+            qc, kc, vc = (si.normal((S, wp.H, Cn, wp.D), gc, torch.bfloat16, dev) for _ in range(3))
+            krc = si.normal((S, wp.H, wp.W, wp.D), gc, torch.bfloat16, dev)
+            vrc = si.normal((S, wp.H, wp.W, wp.D), gc, torch.bfloat16, dev)
+            p0c = torch.full((S,), 5 * wp.W + 123, dtype=torch.int64, device=dev)
+            oc = torch.empty_like(qc)
+            tc = time_launches(lambda: swa.swa_chunk_forward(qc, kc, vc, krc, vrc, p0c, oc,
+                                                             stream=stream), stream, 50, 20)
+            fl = 4 * S * wp.H * wp.D * Cn * wp.W
+            res["chunk"].append({"S": S, "C": Cn, "H": wp.H, "D": wp.D, "W": wp.W,
+                                 "kernel_ms_mean": tc, "useful_flop_per_launch": fl,
+                                 "TFLOPs": fl / (tc * 1e-3) / 1e12})
+            del qc, kc, vc, krc, vrc, oc
     if do_p and args.only == "all" and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(q, k, v, wp.W, args.cpu_seconds)
     res["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),

@@ -207,6 +207,12 @@ int swa_chunk_forward(const void* q, const void* kc, const void* vc, const void*
         return SWA_ERR_UNSUPPORTED;
     if (D > kMaxRowD) return SWA_ERR_UNSUPPORTED;
     hipStream_t st = (hipStream_t)stream;
+    if (dtype == SWA_BF16 && swa::chunk_bf16_supports(q, kc, vc, kring, vring, out, C, D, W) &&
+        S * H * ((C + 127) / 128) < ((int64_t)1 << 31))
+        return from_hip(swa::launch_chunk_bf16(
+            (const swa::bf16*)q, (const swa::bf16*)kc, (const swa::bf16*)vc,
+            (const swa::bf16*)kring, (const swa::bf16*)vring, pos0, (swa::bf16*)out, S, H, C,
+            (int)D, W, st));
     if (dtype == SWA_BF16)
         return from_hip(swa::launch_rowwise_chunk<swa::bf16>(
             (const swa::bf16*)q, (const swa::bf16*)kc, (const swa::bf16*)vc,

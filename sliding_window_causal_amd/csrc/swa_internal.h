@@ -58,6 +58,15 @@ hipError_t launch_prefill_bf16(const bf16* q, const bf16* k, const bf16* v, bf16
                                int64_t B, int64_t H, int64_t T, int D, int64_t W,
                                const Layout& L, float scale, hipStream_t stream);
 
+// bf16 MFMA chunk continuation of a ring (q, kc, vc, out contiguous
+// [S, H, C, D], rings [S, H, W, D]); D in {64, 128}, 16-byte aligned
+// pointers, slabs under 2 GiB (chunk_bf16_supports).
+bool chunk_bf16_supports(const void* q, const void* kc, const void* vc, const void* kring,
+                         const void* vring, const void* out, int64_t C, int64_t D, int64_t W);
+hipError_t launch_chunk_bf16(const bf16* q, const bf16* kc, const bf16* vc, const bf16* kring,
+                             const bf16* vring, const int64_t* pos0, bf16* out, int64_t S,
+                             int64_t H, int64_t C, int D, int64_t W, hipStream_t stream);
+
 // bf16 ring decode; D in {64, 128}, W <= kDecodeMaxW.  With a workspace of
 // decode_workspace_bytes(S, H, D, W) bytes the window may be split over
 // decode_splits(S, H, W) workgroups per (stream, head) and merged by a second

@@ -76,6 +76,13 @@ struct Args {
     int remap;      // 1: spread consecutive logical tiles over one XCD
     float c;        // log2(e) * |scale| (scale defaults to 1 / sqrt(D))
     int qneg;       // 1: scale < 0, applied as -q (exact) times |scale|
+    // chunk continuation only: q, k, v, out are the chunk [S, H, C, D]
+    // (contiguous), the W-slot rings hold the earlier tokens, pos0[s] is the
+    // chunk's first position
+    const bf16* kring;
+    const bf16* vring;
+    const int64_t* pos0;
+    int C;
 };
 
 __device__ inline float swap_max(float x) {
@@ -147,6 +154,15 @@ __device__ inline void tile_offsets(uint32_t (&voff)[N], int wave, int lane, int
         const int logical = phys ^ (IS_V ? vswz<D>(row) : kswz<D>(row));
         voff[i] = row * rsb + logical * 16;
     }
+}
+
+// One 16-byte-per-lane global load into LDS (per-lane source addresses),
+// written as asm for the same reason as lds_load16.
+__device__ inline void lds_load16_global(uint32_t lds_base, const void* src) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_base), "v"(src)
+                 : "memory", "m0");
 }
 
 // Start the HBM -> LDS copy of one tile.
@@ -233,7 +249,15 @@ __device__ inline void read_v_chunk(const char* Vt, int ch, int lane, bf16x8 (&v
 // reference.
 constexpr float kRescaleLog2 = 8.0f;
 
-template <int D, int NW>
+// CHUNK = false: prefill of [B, H, T, D].  CHUNK = true: the chunk
+// continuation of a ring ("27. Sliding-Window Attention", Problem, the
+// rolling buffer; "25. Sliding-Window Causal Attention for Streaming
+// Inference", Problem).  Stream b's chunk holds positions p0 .. p0 + C - 1;
+// keys before p0 live in ring slot (position mod W).  Positions are taken
+// relative to an origin (a multiple of 32 at least W + 32 below p0), so the
+// kernel sees a sequence of length p0r + C whose queries are its last C rows
+// and whose key tiles come from the ring below p0r and from the chunk above.
+template <int D, int NW, bool CHUNK>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_bf16_kernel(Args a) {
     using C = Cfg<D, NW>;
     // Tile t lives in slot (t - t0) % R of the K ring and of the V ring.
@@ -250,9 +274,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int logical = a.remap ? (bid & 7) * (a.nblocks >> 3) + (bid >> 3) : bid;
     const int bh = logical / a.nqt;
     const int qt = a.nqt - 1 - (logical - bh * a.nqt);
-    const int T = a.T, W = a.W;
-    const int i0 = qt * C::BM;
+    const int W = a.W;
     const int b = bh / a.H, h = bh - b * a.H;
+    int T = a.T;                    // sequence length (relative positions)
+    int p0r = 0;                    // first query position (relative)
+    int omod = 0;                   // origin mod W (ring slot of relative position 0)
+    if constexpr (CHUNK) {
+        int64_t p0 = a.pos0[b];
+        p0 = p0 < 0 ? 0 : p0;
+        const int64_t origin = p0 >= (int64_t)W + 32 ? ((p0 - W - 32) & ~(int64_t)31) : 0;
+        p0r = (int)(p0 - origin);
+        omod = (int)(origin % W);
+        T = p0r + a.C;
+    }
+    const int nrow = CHUNK ? a.C : T;   // rows of q and out
+    const int i0 = p0r + qt * C::BM;
     const bf16* __restrict__ Qbh = a.q + b * a.L.q.b + h * a.L.q.h;
     const bf16* __restrict__ Kbh = a.k + b * a.L.k.b + h * a.L.k.h;
     const bf16* __restrict__ Vbh = a.v + b * a.L.v.b + h * a.L.v.h;
@@ -279,7 +315,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // their outputs are never stored).
     bf16x8 qf[D / 16];
     {
-        const bf16* qp = Qbh + (int64_t)min(qi, T - 1) * qrs + 8 * hh;
+        const bf16* qp = Qbh + (int64_t)min(qi - p0r, nrow - 1) * qrs + 8 * hh;
 #pragma unroll
         for (int dc = 0; dc < D / 16; ++dc) qf[dc] = *reinterpret_cast<const bf16x8*>(qp + 16 * dc);
     }
@@ -312,14 +348,64 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     tile_offsets<D, NW, true>(voff, wave, lane, 2 * vrs);
     // bytes per key tile and per slab (the last row ends after D elements)
     const int ktb = C::BN * 2 * krs, vtb = C::BN * 2 * vrs;
-    const int kslab = ((T - 1) * krs + D) * 2, vslab = ((T - 1) * vrs + D) * 2;
+    const int kslab = ((nrow - 1) * krs + D) * 2, vslab = ((nrow - 1) * vrs + D) * 2;
+    // Chunk continuation: the ring slot of relative position x (x < 3 W
+    // whenever W >= 64, which the two subtractions cover).
+    auto ring_slot = [&](int x) {
+        if (W < 64) return x % W;
+        x -= x >= W ? W : 0;
+        x -= x >= W ? W : 0;
+        return x;
+    };
+    const int rslab = W * D * 2;
+    const bf16* Krh = nullptr;
+    const bf16* Vrh = nullptr;
+    if constexpr (CHUNK) {
+        Krh = a.kring + (int64_t)bh * W * D;
+        Vrh = a.vring + (int64_t)bh * W * D;
+    }
+    // A tile of the chunk continuation: all chunk rows (zero-filled past
+    // the chunk), all ring rows in consecutive slots, or (the tile holding
+    // position p0r, or the one where the ring wraps) one source address per
+    // lane, with rows past the chunk clamped to its last row: those keys lie
+    // above every query's diagonal and get weight 0.
+    auto load_chunk_tile = [&](int t, const bf16* Cbh, const bf16* Rbh, int tb, int cslab,
+                               const uint32_t (&off)[C::NLD_W], uint32_t lds, bool isv) {
+        const int k0 = min(t, t1 - 1) * C::BN;
+        if (k0 >= p0r) {
+            dma_tile<D, NW>(rows_rsrc(Cbh, (k0 - p0r) * (tb / C::BN), cslab), lds, wave, off);
+            return;
+        }
+        const int s0 = ring_slot(k0 + omod);
+        if (k0 + C::BN <= p0r && s0 + C::BN <= W) {
+            dma_tile<D, NW>(rows_rsrc(Rbh, s0 * 2 * D, rslab), lds, wave, off);
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < C::NLD_W; ++i) {
+            const int pb = (wave * C::NLD_W + i) * 1024 + lane * 16;
+            const int row = pb / C::ROWB;
+            const int phys = (pb % C::ROWB) >> 4;
+            const int logical = phys ^ (isv ? vswz<D>(row) : kswz<D>(row));
+            const int pos = k0 + row;
+            const bf16* src = pos < p0r ? Rbh + (int64_t)ring_slot(pos + omod) * D
+                                        : Cbh + (int64_t)min(pos - p0r, a.C - 1) * D;
+            lds_load16_global(lds + (wave * C::NLD_W + i) * 1024, src + logical * 8);
+        }
+    };
     auto load_k = [&](int t) {
-        dma_tile<D, NW>(rows_rsrc(Kbh, min(t, t1 - 1) * ktb, kslab), lds_addr(kslot(t)), wave,
-                        koff);
+        if constexpr (CHUNK)
+            load_chunk_tile(t, Kbh, Krh, ktb, kslab, koff, lds_addr(kslot(t)), false);
+        else
+            dma_tile<D, NW>(rows_rsrc(Kbh, min(t, t1 - 1) * ktb, kslab), lds_addr(kslot(t)), wave,
+                            koff);
     };
     auto load_v = [&](int t) {
-        dma_tile<D, NW>(rows_rsrc(Vbh, min(t, t1 - 1) * vtb, vslab), lds_addr(vslot(t)), wave,
-                        voff);
+        if constexpr (CHUNK)
+            load_chunk_tile(t, Vbh, Vrh, vtb, vslab, voff, lds_addr(vslot(t)), true);
+        else
+            dma_tile<D, NW>(rows_rsrc(Vbh, min(t, t1 - 1) * vtb, vslab), lds_addr(vslot(t)), wave,
+                            voff);
     };
     // Publish loads: wait until at most VM_WAIT of this wave's loads are in
     // flight and its LDS reads are done, then barrier.  No fence is needed:
@@ -472,7 +558,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const float l = swap_sum(lsum);
     const float inv = 1.f / l;
     if (qi < T) {
-        bf16* orow = a.out + b * a.L.o.b + h * a.L.o.h + (int64_t)qi * a.L.o.t;
+        bf16* orow = a.out + b * a.L.o.b + h * a.L.o.h + (int64_t)(qi - p0r) * a.L.o.t;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -485,29 +571,30 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
 }
 
-template <int D, int NW>
-hipError_t launch(const bf16* q, const bf16* k, const bf16* v, bf16* out, int64_t B,
-                  int64_t H, int64_t T, int64_t W, const Layout& L, float scale,
-                  hipStream_t stream) {
+template <int D, int NW, bool CHUNK>
+hipError_t launch(Args a, int64_t B, int64_t H, int64_t rows, hipStream_t stream) {
     using C = Cfg<D, NW>;
-    Args a;
+    a.H = (int)H;
+    a.nqt = (int)((rows + C::BM - 1) / C::BM);
+    const int64_t nblocks = B * H * a.nqt;
+    a.nblocks = (int)nblocks;
+    a.remap = (nblocks % 8 == 0) ? 1 : 0;
+    void* args[] = {(void*)&a};
+    return hipLaunchKernel((const void*)prefill_bf16_kernel<D, NW, CHUNK>,
+                           dim3((unsigned)nblocks), dim3(C::NT), args, 0, stream);
+}
+
+Args make_args(const bf16* q, const bf16* k, const bf16* v, bf16* out, const Layout& L,
+               float scale) {
+    Args a = {};
     a.q = q;
     a.k = k;
     a.v = v;
     a.out = out;
     a.L = L;
-    a.H = (int)H;
-    a.T = (int)T;
-    a.W = (int)(W < T ? W : T);
-    a.nqt = (int)((T + C::BM - 1) / C::BM);
-    const int64_t nblocks = B * H * a.nqt;
-    a.nblocks = (int)nblocks;
-    a.remap = (nblocks % 8 == 0) ? 1 : 0;
     a.c = kLog2e * fabsf(scale);
     a.qneg = scale < 0.f ? 1 : 0;
-    void* args[] = {(void*)&a};
-    return hipLaunchKernel((const void*)prefill_bf16_kernel<D, NW>, dim3((unsigned)nblocks),
-                           dim3(C::NT), args, 0, stream);
+    return a;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
@@ -536,8 +623,35 @@ bool prefill_bf16_supports(const void* q, const void* k, const void* v, const vo
 hipError_t launch_prefill_bf16(const bf16* q, const bf16* k, const bf16* v, bf16* out,
                                int64_t B, int64_t H, int64_t T, int D, int64_t W,
                                const Layout& L, float scale, hipStream_t stream) {
-    if (D == 128) return launch<128, 4>(q, k, v, out, B, H, T, W, L, scale, stream);
-    return launch<64, 4>(q, k, v, out, B, H, T, W, L, scale, stream);
+    Args a = make_args(q, k, v, out, L, scale);
+    a.T = (int)T;
+    a.W = (int)(W < T ? W : T);
+    if (D == 128) return launch<128, 4, false>(a, B, H, T, stream);
+    return launch<64, 4, false>(a, B, H, T, stream);
+}
+
+bool chunk_bf16_supports(const void* q, const void* kc, const void* vc, const void* kring,
+                         const void* vring, const void* out, int64_t C, int64_t D, int64_t W) {
+    if (D != 64 && D != 128) return false;
+    for (const void* p : {q, kc, vc, kring, vring, out})
+        if (!aligned16(p)) return false;
+    // 32-bit byte offsets inside one chunk slab and one ring slab, and
+    // relative positions (below W + 64 + C) in int
+    return C * D * 2 < ((int64_t)1 << 31) && W * D * 2 < ((int64_t)1 << 31) &&
+           W + C + 64 < ((int64_t)1 << 30);
+}
+
+hipError_t launch_chunk_bf16(const bf16* q, const bf16* kc, const bf16* vc, const bf16* kring,
+                             const bf16* vring, const int64_t* pos0, bf16* out, int64_t S,
+                             int64_t H, int64_t C, int D, int64_t W, hipStream_t stream) {
+    Args a = make_args(q, kc, vc, out, contiguous_layout(H, C, D), 1.0f / sqrtf((float)D));
+    a.kring = kring;
+    a.vring = vring;
+    a.pos0 = pos0;
+    a.C = (int)C;
+    a.W = (int)W;
+    if (D == 128) return launch<128, 4, true>(a, S, H, C, stream);
+    return launch<64, 4, true>(a, S, H, C, stream);
 }
 
 }  // namespace swa

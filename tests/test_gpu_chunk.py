@@ -180,3 +180,61 @@ def test_negative_pos0_is_treated_as_zero():
     b = swa.chunk_attention(qc, kc, vc, kr, vr, torch.tensor([-5], device=DEV))
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ---- the matrix-core chunk kernel (bf16, D in {64, 128}) at larger chunks ----
+
+MFMA_CASES = [
+    # D, W, C, pos0 per stream
+    (128, 256, 300, [0, 100, 256, 1_000_017]),      # W a multiple of the 32-key tile
+    (128, 300, 257, [7, 299, 300, 5 * 300 + 13]),   # ring wraps inside a tile
+    (64, 1000, 700, [0, 999, 4321, 2_000_003]),
+    (128, 40, 200, [0, 3, 41, 999]),                # W < 64
+]
+
+
+@pytest.mark.parametrize("D,W,C,pos0", MFMA_CASES)
+def test_mfma_chunk_matches_oracle(D, W, C, pos0):
+    S, H = len(pos0), 2
+    dtype = torch.bfloat16
+    g = si.generator(90 + W, DEV)
+    qc, kc, vc = (si.normal((S, H, C, D), g, dtype, DEV) for _ in range(3))
+    # rings as the stream left them: full rings of random tokens, except a
+    # stream younger than W, whose slots at and above pos0 are never written
+    kr = si.normal((S, H, W, D), g, dtype, DEV)
+    vr = si.normal((S, H, W, D), g, dtype, DEV)
+    for s in range(S):
+        if pos0[s] < W:
+            kr[s, :, pos0[s]:] = float("nan")
+            vr[s, :, pos0[s]:] = float("nan")
+    p0 = torch.tensor(pos0, dtype=torch.int64, device=DEV)
+    out = swa.chunk_attention(qc, kc, vc, kr, vr, p0)
+    torch.cuda.synchronize()
+    ref = so.swa_chunk(npy(qc), npy(kc), npy(vc), npy(kr), npy(vr), pos0, W)
+    assert_close(out, ref, dtype, "mfma chunk vs oracle")
+
+
+def test_mfma_chunk_stream_matches_mfma_prefill():
+    """Prefill of a 2500-token sequence in chunks of 512 / 1000 / 988 through
+    the matrix-core chunk kernel against one matrix-core prefill."""
+    H, D, W, T = 4, 128, 640, 2500
+    dtype = torch.bfloat16
+    g = si.generator(97, DEV)
+    q, k, v = (si.normal((1, H, T, D), g, dtype, DEV) for _ in range(3))
+    kr = torch.full((1, H, W, D), float("nan"), dtype=dtype, device=DEV)
+    vr = torch.full_like(kr, float("nan"))
+    outs, p = [], 0
+    for C in (512, 1000, 988):
+        sl = slice(p, p + C)
+        qc, kc, vc = (x[:, :, sl].contiguous() for x in (q, k, v))
+        p0 = torch.tensor([p], dtype=torch.int64, device=DEV)
+        outs.append(swa.chunk_attention(qc, kc, vc, kr, vr, p0))
+        swa.swa_ring_append_chunk(kc, vc, kr, vr, p0)
+        p += C
+    out = torch.cat(outs, dim=2)
+    pre = swa.sliding_window_attention(q, k, v, W)
+    torch.cuda.synchronize()
+    assert_close(out, npy(pre).astype(np.float64), dtype, "chunks vs prefill")
+    rows = [0, 511, 512, 513, 1511, 1512, T - 1]
+    ref = so.swa_rows(npy(q[0]), npy(k[0]), npy(v[0]), W, rows)
+    assert_close(out[0][:, rows], ref, dtype, "chunks vs oracle rows")
