@@ -226,6 +226,38 @@ def swa_loop(q, k, v, W: int):
 # Decode against a bounded W-slot ring
 # ----------------------------------------------------------------------------
 
+def mha_forward(x, wq, bq, wk, bk, wv, bv, wo, bo, H: int, W: int):
+    """Multi-head sliding-window self-attention module forward in float64
+    [P5 "A complete example with moving averages", the module's __call__].
+
+    x: (..., T, d_model); w*: (d_model, d_model) kernels applied as x @ w
+    (input features by output features); b*: (d_model,) biases or None (zero).
+    1. q, k, v = x @ wq + bq, x @ wk + bk, x @ wv + bv
+    2. split the feature axis into H heads of width d_model / H
+    3. per head: swa_dense (scores / sqrt(head width), band, softmax, @ v)
+    4. heads concatenated back along the feature axis, then @ wo + bo
+    Returns (..., T, d_model) float64.
+    """
+    x = _f64(x)
+    T, dm = x.shape[-2], x.shape[-1]
+    H = int(H)
+    if H < 1 or dm % H != 0:
+        raise ValueError("d_model must be a positive multiple of the head count")
+    dh = dm // H
+
+    def proj(a, w, b):
+        y = np.matmul(a, _f64(w))
+        return y if b is None else y + _f64(b)
+
+    def heads(y):                                     # (..., T, dm) -> (..., H, T, dh)
+        return np.swapaxes(y.reshape(y.shape[:-1] + (H, dh)), -2, -3)
+
+    q, k, v = (heads(proj(x, w, b)) for w, b in ((wq, bq), (wk, bk), (wv, bv)))
+    o = swa_dense(q, k, v, W)                         # (..., H, T, dh)
+    concat = np.swapaxes(o, -2, -3).reshape(x.shape[:-1] + (dm,))
+    return proj(concat, wo, bo)
+
+
 def ring_slot(p: int, W: int) -> int:
     """Slot of absolute position p in a W-slot ring.
 

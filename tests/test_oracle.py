@@ -484,6 +484,63 @@ def test_nonfinite_scale_rejected():
 
 
 # ----------------------------------------------------------------------------
+# Module forward [P5 "A complete example with moving averages"]
+# ----------------------------------------------------------------------------
+
+def test_mha_forward_reproduces_p5_printed_example():
+    """d_model 2, two heads, zero Q/K kernels, identity V and output kernels,
+    zero biases: the page's printed output, and rows from 3 on unchanged when
+    row 0 is replaced."""
+    W, x, expected, corrupt, unchanged_from = _load_p5()
+    z, eye = np.zeros((2, 2)), np.eye(2)
+    out = so.mha_forward(x, z, None, z, None, eye, None, eye, None, 2, W)
+    assert np.max(np.abs(out - expected)) <= 1e-12
+    x2 = x.copy()
+    x2[0] = corrupt
+    out2 = so.mha_forward(x2, z, None, z, None, eye, None, eye, None, 2, W)
+    assert np.array_equal(out2[unchanged_from:], out[unchanged_from:])
+    assert not np.array_equal(out2[:unchanged_from], out[:unchanged_from])
+
+
+@pytest.mark.parametrize("H,W", [(1, 3), (2, 5), (4, 1), (4, 40)])
+def test_mha_forward_matches_library_multihead_attention(H, W):
+    """torch's multi-head attention (its own projections, head split and
+    output projection) with the band as a boolean mask, in float64."""
+    r = _rng(31 + H + W)
+    T, dm = 17, 8
+    x = r.standard_normal((2, T, dm))
+    ws = [r.standard_normal((dm, dm)) / math.sqrt(dm) for _ in range(4)]
+    bs = [r.standard_normal(dm) for _ in range(4)]
+    out = so.mha_forward(x, ws[0], bs[0], ws[1], bs[1], ws[2], bs[2], ws[3], bs[3], H, W)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    xt = t(np.swapaxes(x, 0, 1))                      # (T, B, dm), torch's default layout
+    in_w = t(np.concatenate([w.T for w in ws[:3]], axis=0))   # torch applies x @ w^T
+    in_b = t(np.concatenate(bs[:3]))
+    masked = t(~so.band_mask(T, W))                   # True = not allowed, in torch's convention
+    ref, _ = torch.nn.functional.multi_head_attention_forward(
+        xt, xt, xt, dm, H, in_w, in_b, None, None, False, 0.0, t(ws[3].T), t(bs[3]),
+        training=False, need_weights=False, attn_mask=masked)
+    ref = np.swapaxes(ref.numpy(), 0, 1)
+    assert np.max(np.abs(out - ref)) <= 1e-12
+
+
+def test_mha_forward_one_head_identity_is_self_attention():
+    """One head with identity kernels and zero biases is the attention of x
+    with itself."""
+    x = _rng(35).standard_normal((9, 4))
+    eye = np.eye(4)
+    out = so.mha_forward(x, eye, None, eye, None, eye, None, eye, None, 1, 4)
+    assert np.max(np.abs(out - so.swa_dense(x, x, x, 4))) <= 1e-12
+
+
+def test_mha_forward_rejects_bad_heads():
+    x = np.zeros((3, 6))
+    w = np.zeros((6, 6))
+    with pytest.raises(ValueError):
+        so.mha_forward(x, w, None, w, None, w, None, w, None, 4, 2)
+
+
+# ----------------------------------------------------------------------------
 # Planted mistakes: each must make at least one pin fail
 # ----------------------------------------------------------------------------
 
