@@ -308,6 +308,27 @@ def main() -> int:
                                  "kernel_ms_mean": tc, "useful_flop_per_launch": fl,
                                  "TFLOPs": fl / (tc * 1e-3) / 1e12})
             del qc, kc, vc, krc, vrc, oc
+    if do_p and args.only == "all":
+        # The whole attention module of one such layer (d_model 4096 = 32
+        # heads x 128): q, k, v, output projections (rocBLAS) around the band.
+        dm = wp.H * wp.D
+        gm = si.generator(wp.seed + 7, dev)
+        xm = si.normal((wp.B, wp.T, dm), gm, torch.bfloat16, dev)
+        wts = [si.normal((dm, dm), gm, torch.float32, dev).mul_(dm ** -0.5).to(torch.bfloat16)
+               for _ in range(4)]
+        bss = [torch.zeros(dm, dtype=torch.bfloat16, device=dev) for _ in range(4)]
+        om = torch.empty_like(xm)
+        wsm = torch.empty(swa.swa_mha_workspace_bytes(wp.B, wp.T, dm, torch.bfloat16),
+                          dtype=torch.uint8, device=dev)
+        tm = time_launches(lambda: swa.swa_mha_forward(
+            xm, wts[0], bss[0], wts[1], bss[1], wts[2], bss[2], wts[3], bss[3], om, wp.H, wp.W,
+            workspace=wsm, stream=stream), stream, 20, 5)
+        proj = 4 * 2 * wp.B * wp.T * dm * dm
+        att = prefill_flops(wp.B, wp.H, wp.T, wp.D, wp.W)
+        res["module"] = {"B": wp.B, "T": wp.T, "d_model": dm, "H": wp.H, "W": wp.W,
+                         "ms_mean": tm, "projection_flop": proj, "attention_flop": att,
+                         "TFLOPs": (proj + att) / (tm * 1e-3) / 1e12}
+        del xm, wts, om, wsm
     if do_p and args.only == "all" and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(q, k, v, wp.W, args.cpu_seconds)
     res["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),

@@ -225,6 +225,33 @@ int swa_ring_append_chunk(const void* kc, const void* vc, void* kring, void* vri
                           const int64_t* pos0, int64_t S, int64_t H, int64_t C, int64_t D,
                           int64_t W, int dtype, void* stream);
 
+/*
+ * Multi-head sliding-window self-attention module, forward ("NNX
+ * Sliding-Window Attention", A complete example with moving averages):
+ *   q = x wq + bq, k = x wk + bk, v = x wv + bv   (x: [B, T, d_model])
+ *   heads h of width Dh = d_model / H: o_h = swa(q_h, k_h, v_h, W) with
+ *   scores divided by sqrt(Dh) (the computation of swa_forward)
+ *   out = concat_h(o_h) wo + bo
+ * The projections are plain GEMMs (rocBLAS, fp32 accumulation).
+ *
+ *   x, out          : [B, T, d_model]
+ *   wq, wk, wv, wo  : [d_model, d_model], applied as x @ w (rows = input
+ *                     features), row-major
+ *   bq, bk, bv, bo  : [d_model] or NULL for a zero bias
+ *   H               : heads, d_model % H == 0 (else SWA_ERR_INVALID_ARG);
+ *                     bf16 needs Dh in {64, 128}, fp32 Dh <= 256
+ *   workspace       : device memory of swa_mha_workspace_bytes() bytes,
+ *                     16-byte aligned, owned by the caller (q, k, v and the
+ *                     attention output live there)
+ * All device pointers; dtype SWA_F32 or SWA_BF16 for every tensor.  Returns
+ * SWA_ERR_LAUNCH also when rocBLAS fails.
+ */
+int64_t swa_mha_workspace_bytes(int64_t B, int64_t T, int64_t d_model, int dtype);
+int swa_mha_forward(const void* x, const void* wq, const void* bq, const void* wk, const void* bk,
+                    const void* wv, const void* bv, const void* wo, const void* bo, void* out,
+                    int64_t B, int64_t T, int64_t d_model, int64_t H, int64_t W, int dtype,
+                    void* workspace, int64_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,11 +19,14 @@ Entry points (same names as the C ABI):
                                                  chunk of new tokens continuing a ring
   swa_ring_append_chunk(kc, vc, kring, vring, pos0)
                                                  write a chunk's tokens into the ring
+  swa_mha_forward(x, wq, bq, wk, bk, wv, bv, wo, bo, out, num_heads, window)
+                                                 module forward with projections
 Conveniences that allocate the output with torch:
   sliding_window_attention(q, k, v, window_size, scale=None, layout=None) -> out
   decode(q, kring, vring, pos, split=False) -> out
   decode_append(q, knew, vnew, kring, vring, pos) -> out
   chunk_attention(q, kc, vc, kring, vring, pos0) -> out
+  SlidingWindowMHA(d_model, num_heads)(x, window) -> out
 """
 
 from __future__ import annotations
@@ -38,7 +41,8 @@ __all__ = [
     "SWA_ERR_UNSUPPORTED", "SWA_ERR_LAUNCH", "SWAError", "lib", "abi_version",
     "status_string", "swa_forward", "swa_forward_strided", "swa_decode", "swa_ring_append", "swa_chunk_forward",
     "swa_ring_append_chunk", "swa_decode_workspace_bytes", "swa_decode_split",
-    "swa_decode_append", "sliding_window_attention", "decode", "decode_append", "chunk_attention",
+    "swa_decode_append", "swa_mha_workspace_bytes", "swa_mha_forward", "SlidingWindowMHA",
+    "sliding_window_attention", "decode", "decode_append", "chunk_attention",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa.so")
@@ -80,6 +84,10 @@ def lib() -> ctypes.CDLL:
     L.swa_decode.restype = i32
     L.swa_ring_append.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, p]
     L.swa_ring_append.restype = i32
+    L.swa_mha_workspace_bytes.argtypes = [i64, i64, i64, i32]
+    L.swa_mha_workspace_bytes.restype = i64
+    L.swa_mha_forward.argtypes = [p] * 10 + [i64, i64, i64, i64, i64, i32, p, i64, p]
+    L.swa_mha_forward.restype = i32
     L.swa_decode_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
     L.swa_decode_workspace_bytes.restype = i64
     L.swa_decode_split.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, p, i64, p]
@@ -307,6 +315,68 @@ def chunk_attention(q, kc, vc, kring, vring, pos0):
     out = torch.empty_like(q)
     swa_chunk_forward(q, kc, vc, kring, vring, pos0, out)
     return out
+
+
+def swa_mha_workspace_bytes(B: int, T: int, d_model: int, dtype) -> int:
+    code = _DTYPES.get(dtype, dtype) if not isinstance(dtype, int) else dtype
+    n = int(lib().swa_mha_workspace_bytes(B, T, d_model, code))
+    if n < 0:
+        raise SWAError(-n, status_string(-n))
+    return n
+
+
+def swa_mha_forward(x, wq, bq, wk, bk, wv, bv, wo, bo, out, num_heads: int, window_size: int,
+                    workspace=None, stream=None) -> None:
+    """Module forward into ``out``: x, out [B, T, d_model]; w* [d_model, d_model]
+    applied as x @ w; b* [d_model] or None (zero)."""
+    W = _window(window_size)
+    ws = [t for t in (x, wq, wk, wv, wo, out, bq, bk, bv, bo) if t is not None]
+    _check_device(*ws)
+    code = _dtype_code(*ws)
+    if x.dim() != 3 or out.shape != x.shape:
+        raise ValueError("x and out must be [B, T, d_model]")
+    B, T, dm = x.shape
+    for w in (wq, wk, wv, wo):
+        if w.shape != (dm, dm):
+            raise ValueError("projection kernels must be [d_model, d_model]")
+    for b in (bq, bk, bv, bo):
+        if b is not None and b.shape != (dm,):
+            raise ValueError("biases must be [d_model]")
+    need = swa_mha_workspace_bytes(B, T, dm, x.dtype)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ptr = lambda t: None if t is None else _ptr(t)
+    _check(lib().swa_mha_forward(_ptr(x), _ptr(wq), ptr(bq), _ptr(wk), ptr(bk), _ptr(wv), ptr(bv),
+                                 _ptr(wo), ptr(bo), _ptr(out), B, T, dm, int(num_heads), W, code,
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(x, stream)))
+
+
+class SlidingWindowMHA:
+    """Multi-head sliding-window self-attention with q, k, v and output
+    projections (the module of the NNX exercise), forward only.  Weights are
+    plain tensors: kernels [d_model, d_model] applied as x @ w, biases
+    [d_model]; by default kernels ~ N(0, 1/d_model) and zero biases."""
+
+    def __init__(self, d_model: int, num_heads: int, dtype=torch.bfloat16, device="cuda",
+                 generator=None):
+        if num_heads < 1 or d_model % num_heads:
+            raise ValueError("d_model must be a positive multiple of num_heads")
+        self.d_model, self.num_heads = d_model, num_heads
+        std = d_model ** -0.5
+        mk = lambda: (torch.randn(d_model, d_model, generator=generator, device=device) * std
+                      ).to(dtype)
+        self.wq, self.wk, self.wv, self.wo = mk(), mk(), mk(), mk()
+        z = lambda: torch.zeros(d_model, dtype=dtype, device=device)
+        self.bq, self.bk, self.bv, self.bo = z(), z(), z(), z()
+
+    def __call__(self, x, window: int):
+        squeeze = x.dim() == 2                        # the exercise's (T, d_model)
+        xb = x.unsqueeze(0) if squeeze else x
+        out = torch.empty_like(xb)
+        swa_mha_forward(xb, self.wq, self.bq, self.wk, self.bk, self.wv, self.bv, self.wo,
+                        self.bo, out, self.num_heads, window)
+        return out[0] if squeeze else out
 
 
 _LAYOUTS = ("bhtd", "bshd", "btd")

@@ -23,6 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libswa.so")
 ARCH = "gfx950"
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
@@ -81,7 +82,9 @@ def build(verbose: bool = False) -> str:
         for f in futs:
             f.result()
     tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    # rocBLAS carries the module forward's projection GEMMs
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp,
+          f"-L{ROCM}/lib", "-lrocblas", f"-Wl,-rpath,{ROCM}/lib"], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -27,7 +27,7 @@ def test_header_declares_entry_points():
     for n in ("swa_forward", "swa_decode", "swa_ring_append", "swa_status_string",
               "swa_abi_version", "swa_chunk_forward", "swa_ring_append_chunk",
               "swa_forward_strided", "swa_decode_workspace_bytes", "swa_decode_split",
-              "swa_decode_append"):
+              "swa_decode_append", "swa_mha_forward", "swa_mha_workspace_bytes"):
         assert n in names
 
 
@@ -180,6 +180,34 @@ def test_decode_workspace_entries_unsupported(fn, kw):
 
 def test_decode_append_rejects_null_token():
     assert _dapp(kn=None) == swa.SWA_ERR_INVALID_ARG
+
+
+def _mha(x=DUMMY, wq=DUMMY, out=DUMMY, ws=DUMMY, nb=1 << 40, B=1, T=16, dm=256, H=2, W=8,
+         dt=swa.SWA_BF16):
+    return swa.lib().swa_mha_forward(x, wq, None, DUMMY, None, DUMMY, None, DUMMY, None, out, B,
+                                     T, dm, H, W, dt, ws, nb, None)
+
+
+def test_mha_workspace_bytes():
+    L = swa.lib()
+    assert L.swa_mha_workspace_bytes(2, 16, 256, swa.SWA_BF16) == 2 * 16 * 4 * 256 * 2
+    assert L.swa_mha_workspace_bytes(2, 16, 256, swa.SWA_F32) == 2 * 16 * 4 * 256 * 4
+    assert L.swa_mha_workspace_bytes(0, 16, 256, swa.SWA_F32) == -swa.SWA_ERR_INVALID_ARG
+    assert L.swa_mha_workspace_bytes(1, 16, 256, 7) == -swa.SWA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(x=None), dict(wq=None), dict(out=None), dict(ws=None),
+                                dict(B=0), dict(T=0), dict(dm=0), dict(H=0), dict(W=0),
+                                dict(H=3), dict(nb=100), dict(nb=-1),
+                                dict(ws=ctypes.c_void_p(0x1008))])
+def test_mha_invalid_args(kw):
+    assert _mha(**kw) == swa.SWA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(dt=4), dict(dm=192, H=2), dict(dm=64, H=2),
+                                dict(dt=swa.SWA_F32, dm=1024, H=2)])
+def test_mha_unsupported(kw):
+    assert _mha(**kw) == swa.SWA_ERR_UNSUPPORTED
 
 
 def _chunk(q=DUMMY, kc=DUMMY, vc=DUMMY, kr=DUMMY, vr=DUMMY, pos=DUMMY, o=DUMMY, S=1, H=1, C=4,
