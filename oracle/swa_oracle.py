@@ -226,6 +226,36 @@ def swa_loop(q, k, v, W: int):
 # Decode against a bounded W-slot ring
 # ----------------------------------------------------------------------------
 
+def swa_backward(q, k, v, W: int, dout, scale=None):
+    """Gradients of the band attention output with respect to q, k and v,
+    in float64, by the chain rule through the dense recipe of ``swa_dense``
+    (the pages define the forward only; gradients are named by P5, "Mask
+    before softmax": masked weights are zero and gradients stay defined for
+    finite allowed scores).
+
+    With S = q k^T * scale (scale = 1/sqrt(D) by default), P = softmax of S
+    over the band (0 outside it) and out = P v:
+      dV = P^T dout
+      dP = dout v^T
+      dS = P * (dP - rowsum(P * dP))        (softmax Jacobian, per row)
+      dQ = dS k * scale,  dK = dS^T q * scale
+    Entries outside the band have P = 0 and hence dS = 0.
+
+    q, k: (..., T, D); v, dout: (..., T, Dv).  Returns (dq, dk, dv) float64.
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    T, D = q.shape[-2], q.shape[-1]
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _, P = swa_dense(q, k, v, W, return_weights=True, scale=scale)
+    tr = lambda a: np.swapaxes(a, -1, -2)
+    dv = np.matmul(tr(P), dout)
+    dP = np.matmul(dout, tr(v))
+    dS = P * (dP - np.sum(P * dP, axis=-1, keepdims=True))
+    dq = np.matmul(dS, k) * sc
+    dk = np.matmul(tr(dS), q) * sc
+    return dq, dk, dv
+
+
 def mha_forward(x, wq, bq, wk, bk, wv, bv, wo, bo, H: int, W: int):
     """Multi-head sliding-window self-attention module forward in float64
     [P5 "A complete example with moving averages", the module's __call__].

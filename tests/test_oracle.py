@@ -484,6 +484,71 @@ def test_nonfinite_scale_rejected():
 
 
 # ----------------------------------------------------------------------------
+# Backward (gradients of the band attention)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("W", [1, 3, 8, 30])
+@pytest.mark.parametrize("scale", [None, 0.4])
+def test_backward_matches_library_autograd(W, scale):
+    """torch autograd through its own scaled dot-product attention (band as a
+    boolean mask), float64 on the CPU."""
+    r = _rng(41 + W)
+    T, D = 19, 6
+    q, k, v, do = (r.standard_normal((2, T, D)) for _ in range(4))
+    dq, dk, dv = so.swa_backward(q, k, v, W, do, scale=scale)
+    t = lambda a: torch.from_numpy(a.copy()).requires_grad_(True)
+    qt, kt, vt = t(q), t(k), t(v)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, attn_mask=torch.from_numpy(so.band_mask(T, W)), scale=scale)
+    out.backward(torch.from_numpy(do))
+    for mine, ref in ((dq, qt.grad), (dk, kt.grad), (dv, vt.grad)):
+        assert np.max(np.abs(mine - ref.numpy())) <= 1e-12
+
+
+def test_backward_matches_finite_differences():
+    """Central differences of sum(dout * out) on a tiny case (step 1e-6)."""
+    r = _rng(42)
+    T, D, W = 6, 3, 3
+    q, k, v, do = (r.standard_normal((T, D)) for _ in range(4))
+    grads = so.swa_backward(q, k, v, W, do)
+    f = lambda a, b, c: float(np.sum(do * so.swa_dense(a, b, c, W)))
+    h = 1e-6
+    for which in range(3):
+        args = [q, k, v]
+        num = np.zeros_like(args[which])
+        for idx in np.ndindex(num.shape):
+            plus = [a.copy() for a in args]
+            minus = [a.copy() for a in args]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            num[idx] = (f(*plus) - f(*minus)) / (2 * h)
+        assert np.max(np.abs(num - grads[which])) <= 1e-7
+
+
+def test_backward_window_one_closed_form():
+    """W = 1: out = v, so dv = dout and dq = dk = 0 exactly."""
+    r = _rng(43)
+    q, k, v, do = (r.standard_normal((4, 7, 5)) for _ in range(4))
+    dq, dk, dv = so.swa_backward(q, k, v, 1, do)
+    assert np.array_equal(dv, do)
+    assert not np.any(dq) and not np.any(dk)
+
+
+def test_backward_gradient_support_is_the_window():
+    """dk_j and dv_j come only from queries i in [j, j + W - 1]: zeroing dout
+    there zeroes them."""
+    r = _rng(44)
+    T, D, W, j = 20, 4, 5, 7
+    q, k, v, do = (r.standard_normal((T, D)) for _ in range(4))
+    do2 = do.copy()
+    do2[j:j + W] = 0.0
+    _, dk, dv = so.swa_backward(q, k, v, W, do2)
+    assert not np.any(dk[j]) and not np.any(dv[j])
+    _, dk, dv = so.swa_backward(q, k, v, W, do)
+    assert np.any(dk[j]) and np.any(dv[j])
+
+
+# ----------------------------------------------------------------------------
 # Module forward [P5 "A complete example with moving averages"]
 # ----------------------------------------------------------------------------
 
