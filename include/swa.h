@@ -226,6 +226,30 @@ int swa_ring_append_chunk(const void* kc, const void* vc, void* kring, void* vri
                           int64_t W, int dtype, void* stream);
 
 /*
+ * Backward of the prefill: gradients dq, dk, dv of a loss with respect to
+ * q, k, v, given dout = d loss / d out.  The pages define the forward only;
+ * "NNX Sliding-Window Attention", Mask before softmax, notes that masked
+ * weights are zero and gradients stay well defined for finite allowed
+ * scores.  With P = softmax over the band of S = q k^T * scale:
+ *   dv = P^T dout, dS = P * (dout v^T - rowsum(dout * out)),
+ *   dq = dS k * scale, dk = dS^T q * scale.
+ *
+ *   q, k, v, out, dout, dq, dk, dv : [B, H, T, D] contiguous, one dtype;
+ *                    out must be swa_forward's output for q, k, v, W, scale
+ *   scale          : finite; 0 selects 1 / sqrt(D)
+ *   dtype          : SWA_F32 or SWA_BF16 (fp32 accumulation), 1 <= D <= 256
+ *   workspace      : device memory of swa_backward_workspace_bytes() bytes
+ *                    (per-row log-sum-exp and rowsum(dout * out)), 4-byte
+ *                    aligned, owned by the caller
+ * Row-wise kernels (one wavefront per query row, then per key row).
+ */
+int64_t swa_backward_workspace_bytes(int64_t B, int64_t H, int64_t T);
+int swa_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t T, int64_t D,
+                 int64_t W, double scale, int dtype, void* workspace, int64_t workspace_bytes,
+                 void* stream);
+
+/*
  * Multi-head sliding-window self-attention module, forward ("NNX
  * Sliding-Window Attention", A complete example with moving averages):
  *   q = x wq + bq, k = x wk + bk, v = x wv + bv   (x: [B, T, d_model])

@@ -19,6 +19,8 @@ Entry points (same names as the C ABI):
                                                  chunk of new tokens continuing a ring
   swa_ring_append_chunk(kc, vc, kring, vring, pos0)
                                                  write a chunk's tokens into the ring
+  swa_backward(q, k, v, out, dout, dq, dk, dv, window_size, scale=None)
+                                                 gradients of the prefill
   swa_mha_forward(x, wq, bq, wk, bk, wv, bv, wo, bo, out, num_heads, window)
                                                  module forward with projections
 Conveniences that allocate the output with torch:
@@ -41,7 +43,7 @@ __all__ = [
     "SWA_ERR_UNSUPPORTED", "SWA_ERR_LAUNCH", "SWAError", "lib", "abi_version",
     "status_string", "swa_forward", "swa_forward_strided", "swa_decode", "swa_ring_append", "swa_chunk_forward",
     "swa_ring_append_chunk", "swa_decode_workspace_bytes", "swa_decode_split",
-    "swa_decode_append", "swa_mha_workspace_bytes", "swa_mha_forward", "SlidingWindowMHA",
+    "swa_decode_append", "swa_backward", "swa_mha_workspace_bytes", "swa_mha_forward", "SlidingWindowMHA",
     "sliding_window_attention", "decode", "decode_append", "chunk_attention",
 ]
 
@@ -84,6 +86,10 @@ def lib() -> ctypes.CDLL:
     L.swa_decode.restype = i32
     L.swa_ring_append.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, p]
     L.swa_ring_append.restype = i32
+    L.swa_backward_workspace_bytes.argtypes = [i64, i64, i64]
+    L.swa_backward_workspace_bytes.restype = i64
+    L.swa_backward.argtypes = [p] * 8 + [i64, i64, i64, i64, i64, ctypes.c_double, i32, p, i64, p]
+    L.swa_backward.restype = i32
     L.swa_mha_workspace_bytes.argtypes = [i64, i64, i64, i32]
     L.swa_mha_workspace_bytes.restype = i64
     L.swa_mha_forward.argtypes = [p] * 10 + [i64, i64, i64, i64, i64, i32, p, i64, p]
@@ -189,6 +195,33 @@ def swa_forward_strided(q, k, v, out, window_size: int, scale=None, stream=None)
     st = (ctypes.c_int64 * 12)(*[x for t in (q, k, v, out) for x in t.stride()[:3]])
     _check(lib().swa_forward_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, T, D, W, st,
                                      float(scale), code, _stream(q, stream)))
+
+
+def swa_backward(q, k, v, out, dout, dq, dk, dv, window_size: int, scale=None, workspace=None,
+                 stream=None) -> None:
+    """Gradients dq, dk, dv ([B, H, T, D]) of the prefill given its output
+    ``out`` and dout; ``scale`` None means 1/sqrt(D)."""
+    W = _window(window_size)
+    ts = (q, k, v, out, dout, dq, dk, dv)
+    _check_device(*ts)
+    code = _dtype_code(*ts)
+    if q.dim() != 4 or any(t.shape != q.shape for t in ts):
+        raise ValueError("all tensors must be [B, H, T, D] of one shape")
+    if scale is None:
+        scale = 0.0
+    elif isinstance(scale, bool) or not isinstance(scale, (int, float)):
+        raise TypeError("scale must be a number")
+    elif scale == 0 or scale != scale or abs(scale) == float("inf"):
+        raise ValueError("scale must be finite and non-zero")
+    B, H, T, D = q.shape
+    need = int(lib().swa_backward_workspace_bytes(B, H, T))
+    if need < 0:
+        raise SWAError(-need, status_string(-need))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib().swa_backward(*[_ptr(t) for t in ts], B, H, T, D, W, float(scale), code,
+                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(q, stream)))
 
 
 def swa_decode(q, kring, vring, pos, out, stream=None) -> None:

@@ -122,6 +122,41 @@ int swa_decode(const void* q, const void* kring, const void* vring, const int64_
     return SWA_ERR_UNSUPPORTED;
 }
 
+int64_t swa_backward_workspace_bytes(int64_t B, int64_t H, int64_t T) {
+    if (!positive(B) || !positive(H) || !positive(T)) return -SWA_ERR_INVALID_ARG;
+    if (!fits(B, H, T, 8)) return -SWA_ERR_UNSUPPORTED;
+    return B * H * T * 2 * (int64_t)sizeof(float);
+}
+
+int swa_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t T, int64_t D,
+                 int64_t W, double scale, int dtype, void* workspace, int64_t workspace_bytes,
+                 void* stream) {
+    if (!q || !k || !v || !out || !dout || !dq || !dk || !dv || !workspace)
+        return SWA_ERR_INVALID_ARG;
+    if (!positive(B) || !positive(H) || !positive(T) || !positive(D) || !positive(W))
+        return SWA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || workspace_bytes < 0) return SWA_ERR_INVALID_ARG;
+    if (!fits(B, H, T, D) || B * H * T >= ((int64_t)1 << 31)) return SWA_ERR_UNSUPPORTED;
+    if (dtype != SWA_F32 && dtype != SWA_BF16) return SWA_ERR_UNSUPPORTED;
+    if (D > kMaxRowD) return SWA_ERR_UNSUPPORTED;
+    const int64_t need = swa_backward_workspace_bytes(B, H, T);
+    if (workspace_bytes < need || ((uintptr_t)workspace & 3) != 0) return SWA_ERR_INVALID_ARG;
+    const float sc = scale == 0.0 ? 1.0f / sqrtf((float)D) : (float)scale;
+    float* lse = (float*)workspace;
+    float* delta = lse + B * H * T;
+    hipStream_t st = (hipStream_t)stream;
+    if (dtype == SWA_BF16) {
+        using bf = swa::bf16;
+        return from_hip(swa::launch_rowwise_backward<bf>(
+            (const bf*)q, (const bf*)k, (const bf*)v, (const bf*)out, (const bf*)dout, (bf*)dq,
+            (bf*)dk, (bf*)dv, lse, delta, B, H, T, (int)D, W, sc, st));
+    }
+    return from_hip(swa::launch_rowwise_backward<float>(
+        (const float*)q, (const float*)k, (const float*)v, (const float*)out, (const float*)dout,
+        (float*)dq, (float*)dk, (float*)dv, lse, delta, B, H, T, (int)D, W, sc, st));
+}
+
 int64_t swa_decode_workspace_bytes(int64_t S, int64_t H, int64_t D, int64_t W, int dtype) {
     if (!positive(S) || !positive(H) || !positive(D) || !positive(W)) return -SWA_ERR_INVALID_ARG;
     if (!fits(S, H, W, D)) return -SWA_ERR_UNSUPPORTED;

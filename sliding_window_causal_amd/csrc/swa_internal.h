@@ -43,6 +43,14 @@ hipError_t launch_rowwise_decode(const T* q, const T* kring, const T* vring,
                                  const int64_t* pos, T* out, int64_t S, int64_t H, int D,
                                  int64_t W, hipStream_t stream);
 
+// Band attention backward, wavefront per query row (dq, log-sum-exp and
+// delta into lse / delta, B*H*T floats each), then per key row (dk, dv).
+template <typename T>
+hipError_t launch_rowwise_backward(const T* q, const T* k, const T* v, const T* o, const T* dout,
+                                   T* dq, T* dk, T* dv, float* lse, float* delta, int64_t B,
+                                   int64_t H, int64_t Tn, int D, int64_t W, float scale,
+                                   hipStream_t stream);
+
 // Chunk continuation of a ring, wavefront per row; T is float or bf16.
 template <typename T>
 hipError_t launch_rowwise_chunk(const T* q, const T* kc, const T* vc, const T* kring,

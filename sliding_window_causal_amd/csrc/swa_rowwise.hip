@@ -183,7 +183,180 @@ __global__ __launch_bounds__(64) void rowwise_chunk_kernel(
     st.finish(out + cbase + c * D);
 }
 
+// ---- backward ---------------------------------------------------------------
+//
+// Gradients of out = P v with P = softmax over the band of S = q k^T * scale:
+//   dV = P^T dout, dP = dout v^T, dS = P (dP - delta), delta_i = dout_i . out_i
+//   (= sum_j P_ij dP_ij), dQ = dS k * scale, dK = dS^T q * scale.
+// bwd_query_kernel: one wavefront per query row i: the row's log-sum-exp of
+// the scores (one online pass over its band), delta_i, then a second pass
+// accumulating dQ_i.  bwd_key_kernel: one wavefront per key row j, over the
+// queries i in [j, j + W - 1] that see it, accumulating dK_j and dV_j from
+// the per-row log-sum-exp and delta the first kernel left in the workspace.
+
+template <typename T>
+__global__ __launch_bounds__(64) void bwd_query_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ o, const T* __restrict__ dout, T* __restrict__ dq,
+    float* __restrict__ lse, float* __restrict__ delta, int64_t Tn, int D, int64_t W,
+    float scale) {
+    __shared__ float qs[kRowMaxD];
+    __shared__ float ds_[kRowMaxD];
+    __shared__ float ps[64];
+    const int lane = threadIdx.x;
+    const int64_t row = blockIdx.x;            // (b*H + h)*T + i
+    const int64_t bh = row / Tn;
+    const int64_t i = row - bh * Tn;
+    const int64_t base = bh * Tn * D;
+    const T* K = k + base;
+    const T* V = v + base;
+    float dl = 0.f;
+    for (int d = lane; d < D; d += 64) {
+        qs[d] = to_f32(q[base + i * D + d]);
+        ds_[d] = to_f32(dout[base + i * D + d]);
+        dl = fmaf(ds_[d], to_f32(o[base + i * D + d]), dl);
+    }
+    dl = wave_sum(dl);
+    __syncthreads();
+    const int64_t kbeg = i - W + 1 > 0 ? i - W + 1 : 0, kend = i + 1;
+    auto score = [&](int64_t j) {
+        const T* kr = K + j * D;
+        float acc = 0.f;
+        for (int d = 0; d < D; ++d) acc = fmaf(qs[d], to_f32(kr[d]), acc);
+        return acc * scale;
+    };
+    // pass 1: log-sum-exp of the row's scores
+    float m = -__builtin_inff(), l = 0.f;
+    for (int64_t c0 = kbeg; c0 < kend; c0 += 64) {
+        const int64_t j = c0 + lane;
+        const float s = j < kend ? score(j) : -__builtin_inff();
+        const float mn = fmaxf(m, wave_max(s));      // finite: key c0 is valid
+        l = l * expf(m - mn) + wave_sum(j < kend ? expf(s - mn) : 0.f);
+        m = mn;
+    }
+    const float L = m + logf(l);
+    // pass 2: dQ_i = scale * sum_j dS_ij k_j (lanes own columns d = lane + 64 r)
+    float acc[kRowDPL];
+#pragma unroll
+    for (int r = 0; r < kRowDPL; ++r) acc[r] = 0.f;
+    for (int64_t c0 = kbeg; c0 < kend; c0 += 64) {
+        const int64_t j = c0 + lane;
+        float dsv = 0.f;
+        if (j < kend) {
+            const float p = expf(score(j) - L);
+            const T* vr = V + j * D;
+            float dp = 0.f;
+            for (int d = 0; d < D; ++d) dp = fmaf(ds_[d], to_f32(vr[d]), dp);
+            dsv = p * (dp - dl);
+        }
+        ps[lane] = dsv;
+        __syncthreads();
+        const int nk = (int)((kend - c0) < 64 ? (kend - c0) : 64);
+#pragma unroll
+        for (int r = 0; r < kRowDPL; ++r) {
+            const int d = lane + 64 * r;
+            if (d < D)
+                for (int jj = 0; jj < nk; ++jj)
+                    acc[r] = fmaf(ps[jj], to_f32(K[(c0 + jj) * D + d]), acc[r]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < kRowDPL; ++r) {
+        const int d = lane + 64 * r;
+        if (d < D) dq[base + i * D + d] = from_f32<T>(acc[r] * scale);
+    }
+    if (lane == 0) {
+        lse[row] = L;
+        delta[row] = dl;
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void bwd_key_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dout, T* __restrict__ dk, T* __restrict__ dv,
+    const float* __restrict__ lse, const float* __restrict__ delta, int64_t Tn, int D, int64_t W,
+    float scale) {
+    __shared__ float ks[kRowMaxD];
+    __shared__ float vs[kRowMaxD];
+    __shared__ float pp[64];
+    __shared__ float dd[64];
+    const int lane = threadIdx.x;
+    const int64_t row = blockIdx.x;            // (b*H + h)*T + j
+    const int64_t bh = row / Tn;
+    const int64_t j = row - bh * Tn;
+    const int64_t base = bh * Tn * D;
+    const T* Q = q + base;
+    const T* DO = dout + base;
+    for (int d = lane; d < D; d += 64) {
+        ks[d] = to_f32(k[base + j * D + d]);
+        vs[d] = to_f32(v[base + j * D + d]);
+    }
+    __syncthreads();
+    const int64_t qbeg = j, qend = j + W < Tn ? j + W : Tn;
+    float ak[kRowDPL], av[kRowDPL];
+#pragma unroll
+    for (int r = 0; r < kRowDPL; ++r) ak[r] = av[r] = 0.f;
+    for (int64_t c0 = qbeg; c0 < qend; c0 += 64) {
+        const int64_t i = c0 + lane;
+        float p = 0.f, dsv = 0.f;
+        if (i < qend) {
+            const T* qr = Q + i * D;
+            const T* dr = DO + i * D;
+            float s = 0.f, dp = 0.f;
+            for (int d = 0; d < D; ++d) {
+                s = fmaf(ks[d], to_f32(qr[d]), s);
+                dp = fmaf(vs[d], to_f32(dr[d]), dp);
+            }
+            p = expf(s * scale - lse[bh * Tn + i]);
+            dsv = p * (dp - delta[bh * Tn + i]);
+        }
+        pp[lane] = p;
+        dd[lane] = dsv;
+        __syncthreads();
+        const int nq = (int)((qend - c0) < 64 ? (qend - c0) : 64);
+#pragma unroll
+        for (int r = 0; r < kRowDPL; ++r) {
+            const int d = lane + 64 * r;
+            if (d < D)
+                for (int ii = 0; ii < nq; ++ii) {
+                    av[r] = fmaf(pp[ii], to_f32(DO[(c0 + ii) * D + d]), av[r]);
+                    ak[r] = fmaf(dd[ii], to_f32(Q[(c0 + ii) * D + d]), ak[r]);
+                }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int r = 0; r < kRowDPL; ++r) {
+        const int d = lane + 64 * r;
+        if (d < D) {
+            dk[base + j * D + d] = from_f32<T>(ak[r] * scale);
+            dv[base + j * D + d] = from_f32<T>(av[r]);
+        }
+    }
+}
+
 }  // namespace
+
+template <typename T>
+hipError_t launch_rowwise_backward(const T* q, const T* k, const T* v, const T* o, const T* dout,
+                                   T* dq, T* dk, T* dv, float* lse, float* delta, int64_t B,
+                                   int64_t H, int64_t Tn, int D, int64_t W, float scale,
+                                   hipStream_t stream) {
+    const int64_t rows = B * H * Tn;
+    void* a1[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&o, (void*)&dout, (void*)&dq,
+                  (void*)&lse, (void*)&delta, (void*)&Tn, (void*)&D, (void*)&W, (void*)&scale};
+    hipError_t e = hipLaunchKernel((const void*)bwd_query_kernel<T>, dim3((unsigned)rows),
+                                   dim3(64), a1, 0, stream);
+    if (e != hipSuccess) return e;
+    const float* lc = lse;
+    const float* dc = delta;
+    void* a2[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&dout, (void*)&dk, (void*)&dv,
+                  (void*)&lc, (void*)&dc, (void*)&Tn, (void*)&D, (void*)&W, (void*)&scale};
+    return hipLaunchKernel((const void*)bwd_key_kernel<T>, dim3((unsigned)rows), dim3(64), a2, 0,
+                           stream);
+}
 
 template <typename T>
 hipError_t launch_rowwise_chunk(const T* q, const T* kc, const T* vc, const T* kring,
@@ -234,6 +407,14 @@ template hipError_t launch_rowwise_chunk<float>(const float*, const float*, cons
 template hipError_t launch_rowwise_chunk<bf16>(const bf16*, const bf16*, const bf16*, const bf16*,
                                                const bf16*, const int64_t*, bf16*, int64_t, int64_t,
                                                int64_t, int, int64_t, hipStream_t);
+template hipError_t launch_rowwise_backward<float>(const float*, const float*, const float*,
+                                                   const float*, const float*, float*, float*,
+                                                   float*, float*, float*, int64_t, int64_t,
+                                                   int64_t, int, int64_t, float, hipStream_t);
+template hipError_t launch_rowwise_backward<bf16>(const bf16*, const bf16*, const bf16*,
+                                                  const bf16*, const bf16*, bf16*, bf16*, bf16*,
+                                                  float*, float*, int64_t, int64_t, int64_t, int,
+                                                  int64_t, float, hipStream_t);
 template hipError_t launch_rowwise_decode<float>(const float*, const float*, const float*,
                                                  const int64_t*, float*, int64_t, int64_t,
                                                  int, int64_t, hipStream_t);

@@ -27,7 +27,8 @@ def test_header_declares_entry_points():
     for n in ("swa_forward", "swa_decode", "swa_ring_append", "swa_status_string",
               "swa_abi_version", "swa_chunk_forward", "swa_ring_append_chunk",
               "swa_forward_strided", "swa_decode_workspace_bytes", "swa_decode_split",
-              "swa_decode_append", "swa_mha_forward", "swa_mha_workspace_bytes"):
+              "swa_decode_append", "swa_mha_forward", "swa_mha_workspace_bytes",
+              "swa_backward", "swa_backward_workspace_bytes"):
         assert n in names
 
 
@@ -208,6 +209,29 @@ def test_mha_invalid_args(kw):
                                 dict(dt=swa.SWA_F32, dm=1024, H=2)])
 def test_mha_unsupported(kw):
     assert _mha(**kw) == swa.SWA_ERR_UNSUPPORTED
+
+
+def _bwd(q=DUMMY, dq=DUMMY, ws=DUMMY, nb=1 << 40, B=1, H=1, T=8, D=64, W=4, scale=0.0,
+         dt=swa.SWA_F32):
+    return swa.lib().swa_backward(q, DUMMY, DUMMY, DUMMY, DUMMY, dq, DUMMY, DUMMY, B, H, T, D, W,
+                                  scale, dt, ws, nb, None)
+
+
+def test_backward_workspace_bytes():
+    assert swa.lib().swa_backward_workspace_bytes(2, 3, 5) == 2 * 3 * 5 * 8
+    assert swa.lib().swa_backward_workspace_bytes(0, 3, 5) == -swa.SWA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(q=None), dict(dq=None), dict(ws=None), dict(B=0), dict(T=0),
+                                dict(W=0), dict(nb=8), dict(nb=-1), dict(scale=float("nan")),
+                                dict(ws=ctypes.c_void_p(0x1002))])
+def test_backward_invalid_args(kw):
+    assert _bwd(**kw) == swa.SWA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(dt=2), dict(D=300)])
+def test_backward_unsupported(kw):
+    assert _bwd(**kw) == swa.SWA_ERR_UNSUPPORTED
 
 
 def _chunk(q=DUMMY, kc=DUMMY, vc=DUMMY, kr=DUMMY, vr=DUMMY, pos=DUMMY, o=DUMMY, S=1, H=1, C=4,
