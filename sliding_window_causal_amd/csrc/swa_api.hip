@@ -146,6 +146,13 @@ int swa_backward(const void* q, const void* k, const void* v, const void* out, c
     float* lse = (float*)workspace;
     float* delta = lse + B * H * T;
     hipStream_t st = (hipStream_t)stream;
+    if (dtype == SWA_BF16 && swa::backward_bf16_supports(q, k, v, out, dout, T, D, scale) &&
+        B * H * ((T + 127) / 128) < ((int64_t)1 << 31)) {
+        using bf = swa::bf16;
+        return from_hip(swa::launch_backward_bf16(
+            (const bf*)q, (const bf*)k, (const bf*)v, (const bf*)out, (const bf*)dout, (bf*)dq,
+            (bf*)dk, (bf*)dv, lse, delta, B, H, T, (int)D, W, sc, st));
+    }
     if (dtype == SWA_BF16) {
         using bf = swa::bf16;
         return from_hip(swa::launch_rowwise_backward<bf>(

@@ -51,6 +51,17 @@ hipError_t launch_rowwise_backward(const T* q, const T* k, const T* v, const T* 
                                    int64_t H, int64_t Tn, int D, int64_t W, float scale,
                                    hipStream_t stream);
 
+// bf16 matrix-core backward (contiguous [B, H, T, D], D in {64, 128},
+// 16-byte aligned, scale > 0): the forward again for the per-row log2
+// normalisers (into lse; its output goes to dq), then dq (and delta), dv,
+// dk kernels.
+bool backward_bf16_supports(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, int64_t T, int64_t D, double scale);
+hipError_t launch_backward_bf16(const bf16* q, const bf16* k, const bf16* v, const bf16* o,
+                                const bf16* dout, bf16* dq, bf16* dk, bf16* dv, float* lse,
+                                float* delta, int64_t B, int64_t H, int64_t T, int D, int64_t W,
+                                float scale, hipStream_t stream);
+
 // Chunk continuation of a ring, wavefront per row; T is float or bf16.
 template <typename T>
 hipError_t launch_rowwise_chunk(const T* q, const T* kc, const T* vc, const T* kring,
@@ -62,9 +73,12 @@ hipError_t launch_rowwise_chunk(const T* q, const T* kc, const T* vc, const T* k
 // (batch, head) slab of k and v within 2^31 bytes (prefill_bf16_supports).
 bool prefill_bf16_supports(const void* q, const void* k, const void* v, const void* out,
                            int64_t T, int64_t D, const Layout& L);
+// With lse non-null, row i of (batch, head) bh also gets log2 of its softmax
+// normaliser, log2(sum_j exp2(s_ij * log2(e) * scale)), at lse[bh * T + i].
 hipError_t launch_prefill_bf16(const bf16* q, const bf16* k, const bf16* v, bf16* out,
                                int64_t B, int64_t H, int64_t T, int D, int64_t W,
-                               const Layout& L, float scale, hipStream_t stream);
+                               const Layout& L, float scale, hipStream_t stream,
+                               float* lse = nullptr);
 
 // bf16 MFMA chunk continuation of a ring (q, kc, vc, out contiguous
 // [S, H, C, D], rings [S, H, W, D]); D in {64, 128}, 16-byte aligned

@@ -33,15 +33,10 @@
 // the softmax of tile j, then O += V(j)^T P(j)^T.  The LDS layouts are XOR
 // swizzled on 16-byte chunks so every LDS read is bank-conflict free.
 
-#include "swa_internal.h"
+#include "swa_mfma.h"
 
 namespace swa {
 namespace {
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 template <int D, int NW>
 struct Cfg {
@@ -83,98 +78,10 @@ struct Args {
     const bf16* vring;
     const int64_t* pos0;
     int C;
+    // prefill only, optional: log2 of each row's softmax normaliser,
+    // log2(sum_j exp2(s_ij * c)), at lse[bh * T + i] (for the backward)
+    float* lse;
 };
-
-__device__ inline float swap_max(float x) {
-    // v_permlane32_swap exchanges the two 32-lane halves between its two
-    // outputs; max over both outputs is the max over lanes l and l ^ 32.
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ inline float swap_sum(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// K tile: 16-byte chunk c of row r is stored at chunk c ^ kswz(r), so the 16
-// lanes that read one chunk column of 16 consecutive rows (the S MFMA A
-// operand) touch 16 different bank groups.
-template <int D> __device__ inline int kswz(int row) {
-    return D == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-// V tile: chunk c of row r is stored at c ^ vswz(r).  A transposing read
-// covers 4 consecutive rows x 32 bytes per 16 lanes; XOR with 4 (r & 3)
-// spreads the two 16-lane groups of a pass over 16 distinct chunks.
-template <int D> __device__ inline int vswz(int row) {
-    return D == 128 ? 4 * (row & 3) : 4 * (row & 1);
-}
-
-// Buffer resource over the bytes [off, slab_bytes) of one (batch, head)
-// slab whose rows are at least D elements apart: loads past the sequence
-// end return zeros.  Keys past the end lie above every valid query's
-// diagonal, so their scores are masked to -inf and their (zero) values get
-// weight 0.
-__device__ inline __amdgpu_buffer_rsrc_t rows_rsrc(const bf16* slab, int off, int slab_bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(reinterpret_cast<const char*>(slab) + off), 0, slab_bytes - off,
-        0x00020000);
-}
-
-// One 16-byte-per-lane buffer load into LDS: lane l's 16 bytes land at
-// lds_base + 16 l (lds_base goes to M0).  Written as asm so the compiler
-// does not see an LDS write: otherwise it cannot tell later LDS reads of
-// other ring slots apart from the loads still streaming in and drains all
-// in-flight loads before them.  The kernel orders these loads itself
-// (counted vmcnt waits and a barrier before a slot is read).  No register
-// is written, so nothing is left in flight into a VGPR.
-__device__ inline void lds_load16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_base, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds_base), "v"(voff), "s"(rsrc)
-                 : "memory", "m0");
-}
-
-__device__ inline uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
-// Source offsets of one tile's loads.  Load n of this wave writes tile
-// bytes [1024 n, 1024 n + 1024), lane l the 16 bytes at 1024 n + 16 l; it
-// fetches the chunk that the swizzle stores there, from a row rsb bytes
-// apart from the previous one.
-template <int D, int NW, bool IS_V, int N>
-__device__ inline void tile_offsets(uint32_t (&voff)[N], int wave, int lane, int rsb) {
-    using C = Cfg<D, NW>;
-    static_assert(N == C::NLD_W, "one offset per load");
-#pragma unroll
-    for (int i = 0; i < C::NLD_W; ++i) {
-        const int p = (wave * C::NLD_W + i) * 1024 + lane * 16;
-        const int row = p / C::ROWB;
-        const int phys = (p % C::ROWB) >> 4;
-        const int logical = phys ^ (IS_V ? vswz<D>(row) : kswz<D>(row));
-        voff[i] = row * rsb + logical * 16;
-    }
-}
-
-// One 16-byte-per-lane global load into LDS (per-lane source addresses),
-// written as asm for the same reason as lds_load16.
-__device__ inline void lds_load16_global(uint32_t lds_base, const void* src) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :
-                 : "s"(lds_base), "v"(src)
-                 : "memory", "m0");
-}
-
-// Start the HBM -> LDS copy of one tile.
-template <int D, int NW, int N>
-__device__ inline void dma_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t buf, int wave,
-                                const uint32_t (&voff)[N]) {
-    using C = Cfg<D, NW>;
-    static_assert(N == C::NLD_W, "one offset per load");
-#pragma unroll
-    for (int i = 0; i < C::NLD_W; ++i)
-        lds_load16(rsrc, buf + (wave * C::NLD_W + i) * 1024, voff[i]);
-}
 
 // S^T for a 32-key tile: s holds keys 8 (v/4) + 4 hh + v%4 of query lr
 // (v = register index).
@@ -187,60 +94,6 @@ __device__ inline void qk_tile(const char* Kt, const bf16x8 (&qf)[D / 16], int l
     for (int dc = 0; dc < D / 16; ++dc) {
         const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(r0 + (((2 * dc + hh) ^ ksw) << 4));
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[dc], s, 0, 0, 0);
-    }
-}
-
-// Band mask of a tile starting at key k0: key j is visible to query qi iff
-// 0 <= qi - j < W (one unsigned compare).
-__device__ inline void mask_tile(f32x16& s, int qi, int k0, int hh, int W) {
-    const int base = qi - k0 - 4 * hh;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int kof = 8 * (v >> 2) + (v & 3);
-        s[v] = (unsigned)(base - kof) < (unsigned)W ? s[v] : -__builtin_inff();
-    }
-}
-
-__device__ inline void exp_block(f32x16& s, float c, float mc) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], c, -mc));
-}
-
-// Eight probabilities as the bf16 B operand; their sum is added to acc with
-// v_dot2 against ones, so l sums exactly the weights the MFMA applies.
-__device__ inline bf16x8 pack_p(const f32x16& s, int e0, float& acc) {
-    bf16x8 pf;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pf[e] = (bf16)s[e0 + e];
-    const u32x4 pw = __builtin_bit_cast(u32x4, pf);
-    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t w = pw[j];   // scalar copy: bit_cast of a vector element reads element 0
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, acc, false);
-    }
-    return pf;
-}
-
-// A operands of O^T += V^T P^T for the 16-key chunk ch.  Lane l (i = l % 16,
-// group half dh = (l / 16) % 2, hh = l / 32) needs, for d = 32 db + l % 32,
-// the keys 16 ch + 8 a + 4 hh + e (a = 0, 1; e = 0..3).  One
-// ds_read_b64_tr_b16 over the 16 lanes of a group hands lane i column
-// (group base + i) of the 4 x 16 block whose row r0 + i/4, columns
-// 4 (i % 4) .. + 3, lane i addresses.
-template <int D>
-__device__ inline void read_v_chunk(const char* Vt, int ch, int lane, bf16x8 (&va)[D / 32]) {
-    const int i = lane & 15, hh = lane >> 5, dh = (lane >> 4) & 1;
-    const int row = 16 * ch + 4 * hh + (i >> 2);           // + 8 a
-    const int vsw = vswz<D>(i >> 2);                        // row + 8 a keeps the swizzle
-    const char* rp = Vt + row * (2 * D) + 8 * (i & 1);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-        const int chunk = (4 * db + 2 * dh + ((i & 3) >> 1)) ^ vsw;
-        const char* p0 = rp + (chunk << 4);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)p0);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p0 + 8 * 2 * D));
-        va[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 }
 
@@ -344,8 +197,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     auto kslot = [&](int t) { return ring + ((t - t0) % C::R) * C::TILEB; };
     auto vslot = [&](int t) { return ring + (C::R + (t - t0) % C::R) * C::TILEB; };
     uint32_t koff[C::NLD_W], voff[C::NLD_W];
-    tile_offsets<D, NW, false>(koff, wave, lane, 2 * krs);
-    tile_offsets<D, NW, true>(voff, wave, lane, 2 * vrs);
+    tile_offsets<D, NW, kSwzK>(koff, wave, lane, 2 * krs);
+    tile_offsets<D, NW, kSwzV>(voff, wave, lane, 2 * vrs);
     // bytes per key tile and per slab (the last row ends after D elements)
     const int ktb = C::BN * 2 * krs, vtb = C::BN * 2 * vrs;
     const int kslab = ((nrow - 1) * krs + D) * 2, vslab = ((nrow - 1) * vrs + D) * 2;
@@ -373,12 +226,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                                const uint32_t (&off)[C::NLD_W], uint32_t lds, bool isv) {
         const int k0 = min(t, t1 - 1) * C::BN;
         if (k0 >= p0r) {
-            dma_tile<D, NW>(rows_rsrc(Cbh, (k0 - p0r) * (tb / C::BN), cslab), lds, wave, off);
+            dma_tile(rows_rsrc(Cbh, (k0 - p0r) * (tb / C::BN), cslab), lds, wave, off);
             return;
         }
         const int s0 = ring_slot(k0 + omod);
         if (k0 + C::BN <= p0r && s0 + C::BN <= W) {
-            dma_tile<D, NW>(rows_rsrc(Rbh, s0 * 2 * D, rslab), lds, wave, off);
+            dma_tile(rows_rsrc(Rbh, s0 * 2 * D, rslab), lds, wave, off);
             return;
         }
 #pragma unroll
@@ -397,14 +250,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if constexpr (CHUNK)
             load_chunk_tile(t, Kbh, Krh, ktb, kslab, koff, lds_addr(kslot(t)), false);
         else
-            dma_tile<D, NW>(rows_rsrc(Kbh, min(t, t1 - 1) * ktb, kslab), lds_addr(kslot(t)), wave,
+            dma_tile(rows_rsrc(Kbh, min(t, t1 - 1) * ktb, kslab), lds_addr(kslot(t)), wave,
                             koff);
     };
     auto load_v = [&](int t) {
         if constexpr (CHUNK)
             load_chunk_tile(t, Vbh, Vrh, vtb, vslab, voff, lds_addr(vslot(t)), true);
         else
-            dma_tile<D, NW>(rows_rsrc(Vbh, min(t, t1 - 1) * vtb, vslab), lds_addr(vslot(t)), wave,
+            dma_tile(rows_rsrc(Vbh, min(t, t1 - 1) * vtb, vslab), lds_addr(vslot(t)), wave,
                             voff);
     };
     // Publish loads: wait until at most VM_WAIT of this wave's loads are in
@@ -557,6 +410,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // ---- finalise: O / l, bf16, store (lane holds d = 32 db + 8 g + 4 hh + 0..3)
     const float l = swap_sum(lsum);
     const float inv = 1.f / l;
+    if (!CHUNK && a.lse != nullptr && qi < T && hh == 0)
+        a.lse[(int64_t)bh * T + qi] = m * c + __builtin_amdgcn_logf(l);
     if (qi < T) {
         bf16* orow = a.out + b * a.L.o.b + h * a.L.o.h + (int64_t)(qi - p0r) * a.L.o.t;
 #pragma unroll
@@ -622,8 +477,9 @@ bool prefill_bf16_supports(const void* q, const void* k, const void* v, const vo
 
 hipError_t launch_prefill_bf16(const bf16* q, const bf16* k, const bf16* v, bf16* out,
                                int64_t B, int64_t H, int64_t T, int D, int64_t W,
-                               const Layout& L, float scale, hipStream_t stream) {
+                               const Layout& L, float scale, hipStream_t stream, float* lse) {
     Args a = make_args(q, k, v, out, L, scale);
+    a.lse = lse;
     a.T = (int)T;
     a.W = (int)(W < T ? W : T);
     if (D == 128) return launch<128, 4, false>(a, B, H, T, stream);

@@ -61,6 +61,21 @@ def test_backward_matches_oracle(dtype, D, T, W):
     _check(dv, rv, dtype, "dv")
 
 
+@pytest.mark.parametrize("B,H,T,D,W", [(2, 2, 1000, 128, 200), (1, 3, 700, 64, 64),
+                                       (1, 2, 513, 128, 1000)])
+def test_bf16_matrix_core_backward_mid_size(B, H, T, D, W):
+    """Several 128-row workgroups, ragged tails, W < T and W > T."""
+    dtype = torch.bfloat16
+    g = si.generator(170 + T, DEV)
+    q, k, v, do = (si.normal((B, H, T, D), g, dtype, DEV) for _ in range(4))
+    dq, dk, dv = _run(q, k, v, W, do)
+    for b in range(B):
+        rq, rk, rv = so.swa_backward(npy(q[b]), npy(k[b]), npy(v[b]), W, npy(do[b]))
+        _check(dq[b], rq, dtype, f"dq[{b}]")
+        _check(dk[b], rk, dtype, f"dk[{b}]")
+        _check(dv[b], rv, dtype, f"dv[{b}]")
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_backward_with_explicit_scale(dtype):
     B, H, T, D, W = 1, 2, 120, 64, 30
