@@ -329,6 +329,22 @@ def main() -> int:
                          "ms_mean": tm, "projection_flop": proj, "attention_flop": att,
                          "TFLOPs": (proj + att) / (tm * 1e-3) / 1e12}
         del xm, wts, om, wsm
+    if do_p and args.only == "all":
+        # Backward of the same layer: dq, dk, dv given dout (includes the
+        # forward rerun that rebuilds the per-row softmax normalisers).
+        gb = si.generator(wp.seed + 11, dev)
+        dob = si.normal(tuple(q.shape), gb, torch.bfloat16, dev)
+        gq, gk, gv = (torch.empty_like(q) for _ in range(3))
+        wsb = torch.empty(int(swa.lib().swa_backward_workspace_bytes(wp.B, wp.H, wp.T)),
+                          dtype=torch.uint8, device=dev)
+        tb = time_launches(lambda: swa.swa_backward(q, k, v, out, dob, gq, gk, gv, wp.W,
+                                                    workspace=wsb, stream=stream), stream, 10, 3)
+        bf = 10 * wp.B * wp.H * wp.D * band_pairs(wp.T, wp.W)
+        res["backward"] = {"ms_mean": tb, "band_product_flop": bf,
+                           "TFLOPs": bf / (tb * 1e-3) / 1e12,
+                           "note": "five band products (S, dP, dV, dK, dQ) counted; the "
+                                   "forward rerun and the extra S products are not"}
+        del dob, gq, gk, gv, wsb
     if do_p and args.only == "all" and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(q, k, v, wp.W, args.cpu_seconds)
     res["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
