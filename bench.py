@@ -38,6 +38,7 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 PREFILL_SOURCES = ["sliding_window_causal_amd/csrc/swa_prefill_bf16.hip",
+                   "sliding_window_causal_amd/csrc/swa_mfma.h",
                    "sliding_window_causal_amd/csrc/swa_internal.h"]
 DECODE_SOURCES = ["sliding_window_causal_amd/csrc/swa_decode_bf16.hip",
                   "sliding_window_causal_amd/csrc/swa_internal.h"]
