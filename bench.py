@@ -340,12 +340,19 @@ def main() -> int:
                           dtype=torch.uint8, device=dev)
         tb = time_launches(lambda: swa.swa_backward(q, k, v, out, dob, gq, gk, gv, wp.W,
                                                     workspace=wsb, stream=stream), stream, 10, 3)
+        # training order: the forward keeps its row log-sum-exp for the backward
+        lse = torch.empty((wp.B, wp.H, wp.T), dtype=torch.float32, device=dev)
+        swa.swa_forward_lse(q, k, v, out, lse, wp.W, stream=stream)
+        tl = time_launches(lambda: swa.swa_backward(q, k, v, out, dob, gq, gk, gv, wp.W, lse=lse,
+                                                    workspace=wsb, stream=stream), stream, 10, 3)
         bf = 10 * wp.B * wp.H * wp.D * band_pairs(wp.T, wp.W)
-        res["backward"] = {"ms_mean": tb, "band_product_flop": bf,
+        res["backward"] = {"ms_mean": tb, "ms_mean_given_lse": tl, "band_product_flop": bf,
                            "TFLOPs": bf / (tb * 1e-3) / 1e12,
+                           "TFLOPs_given_lse": bf / (tl * 1e-3) / 1e12,
                            "note": "five band products (S, dP, dV, dK, dQ) counted; the "
-                                   "forward rerun and the extra S products are not"}
-        del dob, gq, gk, gv, wsb
+                                   "forward rerun (absent given lse) and the recomputed S "
+                                   "products are not"}
+        del dob, gq, gk, gv, wsb, lse
     if do_p and args.only == "all" and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(q, k, v, wp.W, args.cpu_seconds)
     res["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),

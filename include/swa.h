@@ -76,6 +76,21 @@ int swa_forward(const void* q, const void* k, const void* v, void* out,
                 int dtype, void* stream);
 
 /*
+ * Prefill as swa_forward, with an explicit scale (0 selects 1 / sqrt(D)),
+ * also writing each row's log-sum-exp of its scaled scores,
+ *   lse[(b * H + h) * T + i] = ln(sum over the row's band of exp(s_ij)),
+ * s_ij = q_i . k_j * scale: the softmax normaliser of "Implementation:
+ * Sliding Window Attention", Step 2, that swa_backward can take instead of
+ * recomputing it.
+ *
+ *   lse : device float[B * H * T], written; other arguments as swa_forward
+ * Returns SWA_ERR_INVALID_ARG also for a null lse or a non-finite scale.
+ */
+int swa_forward_lse(const void* q, const void* k, const void* v, void* out, float* lse,
+                    int64_t B, int64_t H, int64_t T, int64_t D, int64_t W, double scale,
+                    int dtype, void* stream);
+
+/*
  * Prefill with arbitrary strides and an optional score scale: the layouts of
  * "Implementation: Sliding Window Attention", Step 2 (queries, keys and
  * values as (batch, seq_len, num_heads, head_dim), and its scale argument
@@ -236,6 +251,8 @@ int swa_ring_append_chunk(const void* kc, const void* vc, void* kring, void* vri
  *
  *   q, k, v, out, dout, dq, dk, dv : [B, H, T, D] contiguous, one dtype;
  *                    out must be swa_forward's output for q, k, v, W, scale
+ *   lse            : NULL, or swa_forward_lse's lse for the same call; the
+ *                    matrix-core path then skips rerunning the forward
  *   scale          : finite; 0 selects 1 / sqrt(D)
  *   dtype          : SWA_F32 or SWA_BF16 (fp32 accumulation), 1 <= D <= 256
  *   workspace      : device memory of swa_backward_workspace_bytes() bytes
@@ -245,9 +262,9 @@ int swa_ring_append_chunk(const void* kc, const void* vc, void* kring, void* vri
  */
 int64_t swa_backward_workspace_bytes(int64_t B, int64_t H, int64_t T);
 int swa_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                 void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t T, int64_t D,
-                 int64_t W, double scale, int dtype, void* workspace, int64_t workspace_bytes,
-                 void* stream);
+                 const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                 int64_t T, int64_t D, int64_t W, double scale, int dtype, void* workspace,
+                 int64_t workspace_bytes, void* stream);
 
 /*
  * Multi-head sliding-window self-attention module, forward ("NNX

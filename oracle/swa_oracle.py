@@ -226,6 +226,19 @@ def swa_loop(q, k, v, W: int):
 # Decode against a bounded W-slot ring
 # ----------------------------------------------------------------------------
 
+def swa_lse(q, k, W: int, scale=None):
+    """Each row's log-sum-exp of its scaled in-band scores, ln(sum_j exp(s_ij))
+    over j in the band of i, in float64: the normaliser of the stable
+    softmax of P3 Step 2 (weights = exp(s - lse)).  q, k: (..., T, D);
+    returns (..., T)."""
+    q, k = _f64(q), _f64(k)
+    T, D = q.shape[-2], q.shape[-1]
+    s = _scores(np.matmul(q, np.swapaxes(k, -1, -2)), D, scale)
+    s = np.where(band_mask(T, W), s, -np.inf)
+    m = s.max(axis=-1, keepdims=True)
+    return (m + np.log(np.exp(s - m).sum(axis=-1, keepdims=True)))[..., 0]
+
+
 def swa_backward(q, k, v, W: int, dout, scale=None):
     """Gradients of the band attention output with respect to q, k and v,
     in float64, by the chain rule through the dense recipe of ``swa_dense``

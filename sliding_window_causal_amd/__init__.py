@@ -19,7 +19,9 @@ Entry points (same names as the C ABI):
                                                  chunk of new tokens continuing a ring
   swa_ring_append_chunk(kc, vc, kring, vring, pos0)
                                                  write a chunk's tokens into the ring
-  swa_backward(q, k, v, out, dout, dq, dk, dv, window_size, scale=None)
+  swa_forward_lse(q, k, v, out, lse, window_size, scale=None)
+                                                 prefill that also writes the row log-sum-exp
+  swa_backward(q, k, v, out, dout, dq, dk, dv, window_size, scale=None, lse=None)
                                                  gradients of the prefill
   swa_mha_forward(x, wq, bq, wk, bk, wv, bv, wo, bo, out, num_heads, window)
                                                  module forward with projections
@@ -43,7 +45,7 @@ __all__ = [
     "SWA_ERR_UNSUPPORTED", "SWA_ERR_LAUNCH", "SWAError", "lib", "abi_version",
     "status_string", "swa_forward", "swa_forward_strided", "swa_decode", "swa_ring_append", "swa_chunk_forward",
     "swa_ring_append_chunk", "swa_decode_workspace_bytes", "swa_decode_split",
-    "swa_decode_append", "swa_backward", "swa_mha_workspace_bytes", "swa_mha_forward", "SlidingWindowMHA",
+    "swa_decode_append", "swa_forward_lse", "swa_backward", "swa_mha_workspace_bytes", "swa_mha_forward", "SlidingWindowMHA",
     "sliding_window_attention", "decode", "decode_append", "chunk_attention",
 ]
 
@@ -88,7 +90,9 @@ def lib() -> ctypes.CDLL:
     L.swa_ring_append.restype = i32
     L.swa_backward_workspace_bytes.argtypes = [i64, i64, i64]
     L.swa_backward_workspace_bytes.restype = i64
-    L.swa_backward.argtypes = [p] * 8 + [i64, i64, i64, i64, i64, ctypes.c_double, i32, p, i64, p]
+    L.swa_backward.argtypes = [p] * 9 + [i64, i64, i64, i64, i64, ctypes.c_double, i32, p, i64, p]
+    L.swa_forward_lse.argtypes = [p] * 5 + [i64, i64, i64, i64, i64, ctypes.c_double, i32, p]
+    L.swa_forward_lse.restype = i32
     L.swa_backward.restype = i32
     L.swa_mha_workspace_bytes.argtypes = [i64, i64, i64, i32]
     L.swa_mha_workspace_bytes.restype = i64
@@ -197,29 +201,59 @@ def swa_forward_strided(q, k, v, out, window_size: int, scale=None, stream=None)
                                      float(scale), code, _stream(q, stream)))
 
 
-def swa_backward(q, k, v, out, dout, dq, dk, dv, window_size: int, scale=None, workspace=None,
-                 stream=None) -> None:
+def _scale_code(scale) -> float:
+    if scale is None:
+        return 0.0                        # the library's code for 1 / sqrt(D)
+    if isinstance(scale, bool) or not isinstance(scale, (int, float)):
+        raise TypeError("scale must be a number")
+    if scale == 0 or scale != scale or abs(scale) == float("inf"):
+        raise ValueError("scale must be finite and non-zero")
+    return float(scale)
+
+
+def _check_lse(lse, q):
+    B, H, T, _ = q.shape
+    if lse.dtype != torch.float32 or lse.shape != (B, H, T):
+        raise ValueError("lse must be float32 [B, H, T]")
+    _check_device(q, lse)
+
+
+def swa_forward_lse(q, k, v, out, lse, window_size: int, scale=None, stream=None) -> None:
+    """Prefill into ``out`` ([B, H, T, D], contiguous) and each row's
+    log-sum-exp of its scaled scores into ``lse`` (float32 [B, H, T])."""
+    W = _window(window_size)
+    _check_device(q, k, v, out)
+    code = _dtype_code(q, k, v, out)
+    if q.dim() != 4 or k.shape != q.shape or v.shape != q.shape or out.shape != q.shape:
+        raise ValueError("q, k, v, out must all be [B, H, T, D] of one shape")
+    _check_lse(lse, q)
+    B, H, T, D = q.shape
+    _check(lib().swa_forward_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, T, D, W,
+                                 _scale_code(scale), code, _stream(q, stream)))
+
+
+def swa_backward(q, k, v, out, dout, dq, dk, dv, window_size: int, scale=None, lse=None,
+                 workspace=None, stream=None) -> None:
     """Gradients dq, dk, dv ([B, H, T, D]) of the prefill given its output
-    ``out`` and dout; ``scale`` None means 1/sqrt(D)."""
+    ``out`` and dout; ``scale`` None means 1/sqrt(D); ``lse`` optionally the
+    forward's log-sum-exp (swa_forward_lse)."""
     W = _window(window_size)
     ts = (q, k, v, out, dout, dq, dk, dv)
     _check_device(*ts)
     code = _dtype_code(*ts)
     if q.dim() != 4 or any(t.shape != q.shape for t in ts):
         raise ValueError("all tensors must be [B, H, T, D] of one shape")
-    if scale is None:
-        scale = 0.0
-    elif isinstance(scale, bool) or not isinstance(scale, (int, float)):
-        raise TypeError("scale must be a number")
-    elif scale == 0 or scale != scale or abs(scale) == float("inf"):
-        raise ValueError("scale must be finite and non-zero")
+    scale = _scale_code(scale)
+    if lse is not None:
+        _check_lse(lse, q)
     B, H, T, D = q.shape
     need = int(lib().swa_backward_workspace_bytes(B, H, T))
     if need < 0:
         raise SWAError(-need, status_string(-need))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    _check(lib().swa_backward(*[_ptr(t) for t in ts], B, H, T, D, W, float(scale), code,
+    _check(lib().swa_backward(*[_ptr(t) for t in ts[:5]], None if lse is None else _ptr(lse),
+                              *[_ptr(t) for t in ts[5:]], B, H, T, D, W, scale, code,
                               _ptr(workspace), workspace.numel() * workspace.element_size(),
                               _stream(q, stream)))
 

@@ -31,7 +31,7 @@ int from_hip(hipError_t e) { return e == hipSuccess ? SWA_OK : SWA_ERR_LAUNCH; }
 // scale == 0 selects 1 / sqrt(D).
 int forward(const void* q, const void* k, const void* v, void* out, int64_t B, int64_t H,
             int64_t T, int64_t D, int64_t W, const swa::Layout& L, double scale, int dtype,
-            hipStream_t st) {
+            hipStream_t st, float* lse = nullptr) {
     if (B * H * T >= ((int64_t)1 << 31)) return SWA_ERR_UNSUPPORTED;
     const float sc = scale == 0.0 ? 1.0f / sqrtf((float)D) : (float)scale;
     if (dtype == SWA_BF16) {
@@ -40,16 +40,16 @@ int forward(const void* q, const void* k, const void* v, void* out, int64_t B, i
                         *vb = (const swa::bf16*)v;
         if (swa::prefill_bf16_supports(q, k, v, out, T, D, L))
             return from_hip(swa::launch_prefill_bf16(qb, kb, vb, (swa::bf16*)out, B, H, T, (int)D,
-                                                     W, L, sc, st));
+                                                     W, L, sc, st, lse));
         // alignment or offsets the matrix-core kernel does not take
         return from_hip(swa::launch_rowwise_prefill<swa::bf16>(qb, kb, vb, (swa::bf16*)out, B, H,
-                                                               T, (int)D, W, L, sc, st));
+                                                               T, (int)D, W, L, sc, st, lse));
     }
     if (dtype == SWA_F32) {
         if (D > kMaxRowD) return SWA_ERR_UNSUPPORTED;
         return from_hip(swa::launch_rowwise_prefill<float>((const float*)q, (const float*)k,
                                                            (const float*)v, (float*)out, B, H, T,
-                                                           (int)D, W, L, sc, st));
+                                                           (int)D, W, L, sc, st, lse));
     }
     return SWA_ERR_UNSUPPORTED;
 }
@@ -78,6 +78,18 @@ int swa_forward(const void* q, const void* k, const void* v, void* out, int64_t 
     if (!fits(B, H, T, D)) return SWA_ERR_UNSUPPORTED;
     return forward(q, k, v, out, B, H, T, D, W, swa::contiguous_layout(H, T, D), 0.0, dtype,
                    (hipStream_t)stream);
+}
+
+int swa_forward_lse(const void* q, const void* k, const void* v, void* out, float* lse,
+                    int64_t B, int64_t H, int64_t T, int64_t D, int64_t W, double scale,
+                    int dtype, void* stream) {
+    if (!q || !k || !v || !out || !lse) return SWA_ERR_INVALID_ARG;
+    if (!positive(B) || !positive(H) || !positive(T) || !positive(D) || !positive(W))
+        return SWA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return SWA_ERR_INVALID_ARG;
+    if (!fits(B, H, T, D)) return SWA_ERR_UNSUPPORTED;
+    return forward(q, k, v, out, B, H, T, D, W, swa::contiguous_layout(H, T, D), scale, dtype,
+                   (hipStream_t)stream, lse);
 }
 
 int swa_forward_strided(const void* q, const void* k, const void* v, void* out, int64_t B,
@@ -129,9 +141,9 @@ int64_t swa_backward_workspace_bytes(int64_t B, int64_t H, int64_t T) {
 }
 
 int swa_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                 void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t T, int64_t D,
-                 int64_t W, double scale, int dtype, void* workspace, int64_t workspace_bytes,
-                 void* stream) {
+                 const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                 int64_t T, int64_t D, int64_t W, double scale, int dtype, void* workspace,
+                 int64_t workspace_bytes, void* stream) {
     if (!q || !k || !v || !out || !dout || !dq || !dk || !dv || !workspace)
         return SWA_ERR_INVALID_ARG;
     if (!positive(B) || !positive(H) || !positive(T) || !positive(D) || !positive(W))
@@ -143,25 +155,25 @@ int swa_backward(const void* q, const void* k, const void* v, const void* out, c
     const int64_t need = swa_backward_workspace_bytes(B, H, T);
     if (workspace_bytes < need || ((uintptr_t)workspace & 3) != 0) return SWA_ERR_INVALID_ARG;
     const float sc = scale == 0.0 ? 1.0f / sqrtf((float)D) : (float)scale;
-    float* lse = (float*)workspace;
-    float* delta = lse + B * H * T;
+    float* lse_ws = (float*)workspace;
+    float* delta = lse_ws + B * H * T;
     hipStream_t st = (hipStream_t)stream;
     if (dtype == SWA_BF16 && swa::backward_bf16_supports(q, k, v, out, dout, T, D, scale) &&
         B * H * ((T + 127) / 128) < ((int64_t)1 << 31)) {
         using bf = swa::bf16;
         return from_hip(swa::launch_backward_bf16(
             (const bf*)q, (const bf*)k, (const bf*)v, (const bf*)out, (const bf*)dout, (bf*)dq,
-            (bf*)dk, (bf*)dv, lse, delta, B, H, T, (int)D, W, sc, st));
+            (bf*)dk, (bf*)dv, lse, lse_ws, delta, B, H, T, (int)D, W, sc, st));
     }
     if (dtype == SWA_BF16) {
         using bf = swa::bf16;
         return from_hip(swa::launch_rowwise_backward<bf>(
             (const bf*)q, (const bf*)k, (const bf*)v, (const bf*)out, (const bf*)dout, (bf*)dq,
-            (bf*)dk, (bf*)dv, lse, delta, B, H, T, (int)D, W, sc, st));
+            (bf*)dk, (bf*)dv, lse_ws, delta, B, H, T, (int)D, W, sc, st));
     }
     return from_hip(swa::launch_rowwise_backward<float>(
         (const float*)q, (const float*)k, (const float*)v, (const float*)out, (const float*)dout,
-        (float*)dq, (float*)dk, (float*)dv, lse, delta, B, H, T, (int)D, W, sc, st));
+        (float*)dq, (float*)dk, (float*)dv, lse_ws, delta, B, H, T, (int)D, W, sc, st));
 }
 
 int64_t swa_decode_workspace_bytes(int64_t S, int64_t H, int64_t D, int64_t W, int dtype) {

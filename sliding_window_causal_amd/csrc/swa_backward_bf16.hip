@@ -7,8 +7,8 @@
 // gradients stay defined):
 //   dV = P^T dout, dP = dout v^T, dS = P (dP - delta), delta_i = dout_i . out_i,
 //   dQ = dS k * scale, dK = dS^T q * scale.
-// P is rebuilt tile by tile as exp2(s * c - L_i) from the forward's per-row
-// log2 normaliser L_i (c = log2(e) * scale), so no T x T array exists.
+// P is rebuilt tile by tile as exp2(s * c - L_i log2(e)) from the forward's
+// per-row log-sum-exp L_i (c = log2(e) * scale), so no T x T array exists.
 //
 // Three kernels share one skeleton: a workgroup of 4 wavefronts owns 128
 // "row" items (32 per wavefront) and walks 32-item "column" tiles of its band
@@ -56,7 +56,7 @@ struct BArgs {
     const bf16* o;        // forward output (DQ: delta)
     const bf16* dout;
     bf16* grad;           // dq, dk or dv, [B, H, T, D]
-    float* lse;           // [B * H * T] log2 normalisers (forward)
+    const float* lse;     // [B * H * T] log-sum-exp of the scaled scores (forward)
     float* delta;         // [B * H * T] dout . out (written by DQ)
     int T, W, nrt, nblocks, remap;
     float c;              // log2(e) * scale
@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // for the DK kernel)
     float Lrow = 0.f, drow = 0.f;
     if (ROWQ) {
-        Lrow = a.lse[(int64_t)bh * T + rc];
+        Lrow = a.lse[(int64_t)bh * T + rc] * kLog2e;
         const bf16* po = a.o + off + (int64_t)rc * D + 8 * hh;
         float d = 0.f;
 #pragma unroll
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // write the same bytes); past the sequence end the buffer range check
     // gives 0.
     const __amdgpu_buffer_rsrc_t lse_rs = __builtin_amdgcn_make_buffer_rsrc(
-        a.lse + (int64_t)bh * T, 0, T * 4, 0x00020000);
+        const_cast<float*>(a.lse) + (int64_t)bh * T, 0, T * 4, 0x00020000);
     const __amdgpu_buffer_rsrc_t del_rs = __builtin_amdgcn_make_buffer_rsrc(
         a.delta + (int64_t)bh * T, 0, T * 4, 0x00020000);
     auto load = [&](int t) {
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // P and (DQ, DK) dS
 #pragma unroll
             for (int vv = 0; vv < 16; ++vv) {
-                const float L = ROWQ ? Lrow : Ls[vv];
+                const float L = ROWQ ? Lrow : Ls[vv] * kLog2e;
                 const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[vv], c, -L));
                 if (MODE == kDV) s[vv] = p;
                 else s[vv] = p * (dp[vv] - (ROWQ ? drow : Ds[vv]));
@@ -328,21 +328,25 @@ bool backward_bf16_supports(const void* q, const void* k, const void* v, const v
 }
 
 hipError_t launch_backward_bf16(const bf16* q, const bf16* k, const bf16* v, const bf16* o,
-                                const bf16* dout, bf16* dq, bf16* dk, bf16* dv, float* lse,
-                                float* delta, int64_t B, int64_t H, int64_t T, int D, int64_t W,
-                                float scale, hipStream_t stream) {
-    // the forward again, for the per-row log2 normalisers; its output goes to
-    // dq, which the DQ kernel overwrites
-    hipError_t e = launch_prefill_bf16(q, k, v, dq, B, H, T, D, W, contiguous_layout(H, T, D),
-                                       scale, stream, lse);
-    if (e != hipSuccess) return e;
+                                const bf16* dout, bf16* dq, bf16* dk, bf16* dv,
+                                const float* lse_in, float* lse, float* delta, int64_t B,
+                                int64_t H, int64_t T, int D, int64_t W, float scale,
+                                hipStream_t stream) {
+    if (lse_in == nullptr) {
+        // the forward again, for the per-row log-sum-exp; its output goes to
+        // dq, which the DQ kernel overwrites
+        hipError_t e = launch_prefill_bf16(q, k, v, dq, B, H, T, D, W,
+                                           contiguous_layout(H, T, D), scale, stream, lse);
+        if (e != hipSuccess) return e;
+        lse_in = lse;
+    }
     BArgs a = {};
     a.q = q;
     a.k = k;
     a.v = v;
     a.o = o;
     a.dout = dout;
-    a.lse = lse;
+    a.lse = lse_in;
     a.delta = delta;
     a.T = (int)T;
     a.W = (int)(W < T ? W : T);

@@ -19,6 +19,8 @@
 
 #include "swa_internal.h"
 
+#include <atomic>
+
 namespace swa {
 namespace {
 
@@ -254,13 +256,17 @@ template <int D>
 hipError_t launch(DecArgs a, int64_t S, hipStream_t stream) {
     const int64_t floats = a.chunk > kQuads * D ? (int64_t)a.chunk : (int64_t)kQuads * D;
     const unsigned lds = (unsigned)(floats * sizeof(float));
-    static bool attr_set = false;
-    if (!attr_set) {
+    // the dynamic-LDS limit is raised once per device (bit dev of attr_done)
+    static std::atomic<uint64_t> attr_done{0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    const uint64_t bit = 1ull << (dev & 63);
+    if (!(attr_done.load(std::memory_order_acquire) & bit)) {
         hipError_t e = hipFuncSetAttribute((const void*)decode_bf16_kernel<D>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize,
                                            (int)(kDecodeMaxW * sizeof(float)));
         if (e != hipSuccess) return e;
-        attr_set = true;
+        attr_done.fetch_or(bit, std::memory_order_release);
     }
     a.c = kLog2e / sqrtf((float)D);
     void* args[] = {(void*)&a};

@@ -16,6 +16,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 // Element strides of a [B, H, T, D] operand whose D axis is contiguous:
 // element (b, h, t, d) sits at b * b + h * h + t * t + d.
@@ -37,7 +38,8 @@ inline Layout contiguous_layout(int64_t H, int64_t T, int64_t D) {
 template <typename T>
 hipError_t launch_rowwise_prefill(const T* q, const T* k, const T* v, T* out,
                                   int64_t B, int64_t H, int64_t Tn, int D, int64_t W,
-                                  const Layout& L, float scale, hipStream_t stream);
+                                  const Layout& L, float scale, hipStream_t stream,
+                                  float* lse = nullptr);
 template <typename T>
 hipError_t launch_rowwise_decode(const T* q, const T* kring, const T* vring,
                                  const int64_t* pos, T* out, int64_t S, int64_t H, int D,
@@ -52,15 +54,16 @@ hipError_t launch_rowwise_backward(const T* q, const T* k, const T* v, const T* 
                                    hipStream_t stream);
 
 // bf16 matrix-core backward (contiguous [B, H, T, D], D in {64, 128},
-// 16-byte aligned, scale > 0): the forward again for the per-row log2
-// normalisers (into lse; its output goes to dq), then dq (and delta), dv,
-// dk kernels.
+// 16-byte aligned, scale > 0): unless lse_in is given, the forward again for
+// the per-row log-sum-exp (into lse; its output goes to dq); then dq (and
+// delta), dv, dk kernels.
 bool backward_bf16_supports(const void* q, const void* k, const void* v, const void* o,
                             const void* dout, int64_t T, int64_t D, double scale);
 hipError_t launch_backward_bf16(const bf16* q, const bf16* k, const bf16* v, const bf16* o,
-                                const bf16* dout, bf16* dq, bf16* dk, bf16* dv, float* lse,
-                                float* delta, int64_t B, int64_t H, int64_t T, int D, int64_t W,
-                                float scale, hipStream_t stream);
+                                const bf16* dout, bf16* dq, bf16* dk, bf16* dv,
+                                const float* lse_in, float* lse, float* delta, int64_t B,
+                                int64_t H, int64_t T, int D, int64_t W, float scale,
+                                hipStream_t stream);
 
 // Chunk continuation of a ring, wavefront per row; T is float or bf16.
 template <typename T>
@@ -73,8 +76,8 @@ hipError_t launch_rowwise_chunk(const T* q, const T* kc, const T* vc, const T* k
 // (batch, head) slab of k and v within 2^31 bytes (prefill_bf16_supports).
 bool prefill_bf16_supports(const void* q, const void* k, const void* v, const void* out,
                            int64_t T, int64_t D, const Layout& L);
-// With lse non-null, row i of (batch, head) bh also gets log2 of its softmax
-// normaliser, log2(sum_j exp2(s_ij * log2(e) * scale)), at lse[bh * T + i].
+// With lse non-null, row i of (batch, head) bh also gets the log-sum-exp of
+// its scaled scores, ln(sum_j exp(s_ij * scale)), at lse[bh * T + i].
 hipError_t launch_prefill_bf16(const bf16* q, const bf16* k, const bf16* v, bf16* out,
                                int64_t B, int64_t H, int64_t T, int D, int64_t W,
                                const Layout& L, float scale, hipStream_t stream,

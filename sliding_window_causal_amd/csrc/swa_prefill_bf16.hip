@@ -78,8 +78,8 @@ struct Args {
     const bf16* vring;
     const int64_t* pos0;
     int C;
-    // prefill only, optional: log2 of each row's softmax normaliser,
-    // log2(sum_j exp2(s_ij * c)), at lse[bh * T + i] (for the backward)
+    // prefill only, optional: each row's log-sum-exp of its scaled scores,
+    // ln(sum_j exp(s_ij * scale)), at lse[bh * T + i] (for the backward)
     float* lse;
 };
 
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const float l = swap_sum(lsum);
     const float inv = 1.f / l;
     if (!CHUNK && a.lse != nullptr && qi < T && hh == 0)
-        a.lse[(int64_t)bh * T + qi] = m * c + __builtin_amdgcn_logf(l);
+        a.lse[(int64_t)bh * T + qi] = (m * c + __builtin_amdgcn_logf(l)) * kLn2;
     if (qi < T) {
         bf16* orow = a.out + b * a.L.o.b + h * a.L.o.h + (int64_t)(qi - p0r) * a.L.o.t;
 #pragma unroll

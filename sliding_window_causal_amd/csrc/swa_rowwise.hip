@@ -97,6 +97,9 @@ struct RowAttn {
         }
     }
 
+    // ln(sum_j exp(s_j)) of the scaled scores seen (-inf if none)
+    __device__ float lse() const { return m + logf(l); }
+
     __device__ void finish(T* __restrict__ orow) const {
         const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
@@ -124,15 +127,20 @@ __device__ void attend_row(const T* __restrict__ qrow, const T* __restrict__ K, 
 template <typename T>
 __global__ __launch_bounds__(64) void rowwise_prefill_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    T* __restrict__ out, int64_t H, int64_t Tn, int D, int64_t W, Layout L, float scale) {
+    T* __restrict__ out, int64_t H, int64_t Tn, int D, int64_t W, Layout L, float scale,
+    float* __restrict__ lse) {
     const int64_t row = blockIdx.x;            // (b*H + h)*T + i
     const int64_t bh = row / Tn;
     const int64_t i = row - bh * Tn;
     const int64_t b = bh / H, h = bh - b * H;
     const int64_t kbeg = i - W + 1 > 0 ? i - W + 1 : 0;
-    attend_row<T>(q + b * L.q.b + h * L.q.h + i * L.q.t, k + b * L.k.b + h * L.k.h, L.k.t,
-                  v + b * L.v.b + h * L.v.h, L.v.t, kbeg, i + 1, D, scale,
-                  out + b * L.o.b + h * L.o.h + i * L.o.t);
+    __shared__ float qs[kRowMaxD];
+    __shared__ float ps[64];
+    RowAttn<T> st;
+    st.init(q + b * L.q.b + h * L.q.h + i * L.q.t, qs, ps, D, scale);
+    st.segment(k + b * L.k.b + h * L.k.h, L.k.t, v + b * L.v.b + h * L.v.h, L.v.t, kbeg, i + 1);
+    st.finish(out + b * L.o.b + h * L.o.h + i * L.o.t);
+    if (lse != nullptr && threadIdx.x == 0) lse[row] = st.lse();
 }
 
 template <typename T>
@@ -374,11 +382,11 @@ hipError_t launch_rowwise_chunk(const T* q, const T* kc, const T* vc, const T* k
 template <typename T>
 hipError_t launch_rowwise_prefill(const T* q, const T* k, const T* v, T* out, int64_t B,
                                   int64_t H, int64_t Tn, int D, int64_t W, const Layout& L,
-                                  float scale, hipStream_t stream) {
+                                  float scale, hipStream_t stream, float* lse) {
     const int64_t rows = B * H * Tn;
     Layout lay = L;
     void* args[] = {(void*)&q, (void*)&k, (void*)&v, (void*)&out, (void*)&H, (void*)&Tn,
-                    (void*)&D, (void*)&W, (void*)&lay, (void*)&scale};
+                    (void*)&D, (void*)&W, (void*)&lay, (void*)&scale, (void*)&lse};
     return hipLaunchKernel((const void*)rowwise_prefill_kernel<T>, dim3((unsigned)rows),
                            dim3(64), args, 0, stream);
 }
@@ -397,10 +405,11 @@ hipError_t launch_rowwise_decode(const T* q, const T* kring, const T* vring,
 
 template hipError_t launch_rowwise_prefill<float>(const float*, const float*, const float*,
                                                   float*, int64_t, int64_t, int64_t, int,
-                                                  int64_t, const Layout&, float, hipStream_t);
+                                                  int64_t, const Layout&, float, hipStream_t,
+                                                  float*);
 template hipError_t launch_rowwise_prefill<bf16>(const bf16*, const bf16*, const bf16*, bf16*,
                                                  int64_t, int64_t, int64_t, int, int64_t,
-                                                 const Layout&, float, hipStream_t);
+                                                 const Layout&, float, hipStream_t, float*);
 template hipError_t launch_rowwise_chunk<float>(const float*, const float*, const float*,
                                                 const float*, const float*, const int64_t*, float*,
                                                 int64_t, int64_t, int64_t, int, int64_t, hipStream_t);

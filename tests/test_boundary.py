@@ -28,7 +28,7 @@ def test_header_declares_entry_points():
               "swa_abi_version", "swa_chunk_forward", "swa_ring_append_chunk",
               "swa_forward_strided", "swa_decode_workspace_bytes", "swa_decode_split",
               "swa_decode_append", "swa_mha_forward", "swa_mha_workspace_bytes",
-              "swa_backward", "swa_backward_workspace_bytes"):
+              "swa_backward", "swa_backward_workspace_bytes", "swa_forward_lse"):
         assert n in names
 
 
@@ -213,8 +213,23 @@ def test_mha_unsupported(kw):
 
 def _bwd(q=DUMMY, dq=DUMMY, ws=DUMMY, nb=1 << 40, B=1, H=1, T=8, D=64, W=4, scale=0.0,
          dt=swa.SWA_F32):
-    return swa.lib().swa_backward(q, DUMMY, DUMMY, DUMMY, DUMMY, dq, DUMMY, DUMMY, B, H, T, D, W,
-                                  scale, dt, ws, nb, None)
+    return swa.lib().swa_backward(q, DUMMY, DUMMY, DUMMY, DUMMY, None, dq, DUMMY, DUMMY, B, H, T,
+                                  D, W, scale, dt, ws, nb, None)
+
+
+def _flse(q=DUMMY, lse=DUMMY, B=1, H=1, T=8, D=64, W=4, scale=0.0, dt=swa.SWA_BF16):
+    return swa.lib().swa_forward_lse(q, DUMMY, DUMMY, DUMMY, lse, B, H, T, D, W, scale, dt, None)
+
+
+@pytest.mark.parametrize("kw", [dict(q=None), dict(lse=None), dict(T=0), dict(W=0),
+                                dict(scale=float("inf"))])
+def test_forward_lse_invalid_args(kw):
+    assert _flse(**kw) == swa.SWA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(dt=3), dict(D=96)])
+def test_forward_lse_unsupported(kw):
+    assert _flse(**kw) == swa.SWA_ERR_UNSUPPORTED
 
 
 def test_backward_workspace_bytes():

@@ -100,3 +100,33 @@ def test_key_gradient_support_is_its_window():
     do2[:, :, j + W:] = -5.0
     _, dk2, dv2 = _run(q, k, v, W, do2)
     assert torch.equal(dk[:, :, j], dk2[:, :, j]) and torch.equal(dv[:, :, j], dv2[:, :, j])
+
+
+@pytest.mark.parametrize("dtype,D,T,W,scale", [(torch.bfloat16, 128, 300, 64, None),
+                                               (torch.bfloat16, 64, 200, 500, 0.2),
+                                               (torch.float32, 48, 120, 17, None)])
+def test_forward_lse_and_backward_reusing_it(dtype, D, T, W, scale):
+    """swa_forward_lse's row log-sum-exp against the oracle (fp32 bar 1e-5 on
+    values of order 1-10 for both dtypes: it is an fp32 output), and the
+    backward fed that lse equals the backward that recomputes it, bitwise."""
+    B, H = 2, 2
+    g = si.generator(180 + D, DEV)
+    q, k, v, do = (si.normal((B, H, T, D), g, dtype, DEV) for _ in range(4))
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=DEV)
+    swa.swa_forward_lse(q, k, v, out, lse, W, scale=scale)
+    ref = so.swa_lse(npy(q), npy(k), W, scale=scale)
+    torch.cuda.synchronize()
+    err = np.abs(npy(lse).astype(np.float64) - ref).max()
+    tol = 1e-5 * max(1.0, np.abs(ref).max()) if dtype == torch.float32 else 2e-2
+    assert err <= tol, f"lse max err {err:.3e}"
+    base = swa.sliding_window_attention(q, k, v, W, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, base)
+    g1 = [torch.empty_like(q) for _ in range(3)]
+    g2 = [torch.empty_like(q) for _ in range(3)]
+    swa.swa_backward(q, k, v, out, do, *g1, W, scale=scale)
+    swa.swa_backward(q, k, v, out, do, *g2, W, scale=scale, lse=lse)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)

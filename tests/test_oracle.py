@@ -505,6 +505,22 @@ def test_backward_matches_library_autograd(W, scale):
         assert np.max(np.abs(mine - ref.numpy())) <= 1e-12
 
 
+@pytest.mark.parametrize("W,scale", [(1, None), (4, None), (11, 0.3), (40, None)])
+def test_lse_matches_library_logsumexp(W, scale):
+    """torch.logsumexp over the masked scores, and weights = exp(s - lse)."""
+    r = _rng(45 + W)
+    T, D = 15, 5
+    q, k, v = (r.standard_normal((2, T, D)) for _ in range(3))
+    lse = so.swa_lse(q, k, W, scale=scale)
+    sc = 1 / math.sqrt(D) if scale is None else scale
+    s = torch.from_numpy(q @ np.swapaxes(k, -1, -2) * sc)
+    s = s.masked_fill(~torch.from_numpy(so.band_mask(T, W)), -math.inf)
+    assert np.max(np.abs(lse - torch.logsumexp(s, dim=-1).numpy())) <= 1e-12
+    _, P = so.swa_dense(q, k, v, W, return_weights=True, scale=scale)
+    band = so.band_mask(T, W)
+    assert np.max(np.abs(np.where(band, np.exp(s.numpy() - lse[..., None]), 0.0) - P)) <= 1e-12
+
+
 def test_backward_matches_finite_differences():
     """Central differences of sum(dout * out) on a tiny case (step 1e-6)."""
     r = _rng(42)
