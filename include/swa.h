@@ -229,6 +229,29 @@ int swa_chunk_forward(const void* q, const void* kc, const void* vc,
                       int dtype, void* stream);
 
 /*
+ * Chunk continuation as swa_chunk_forward, for few streams: when the
+ * S * H * ceil(C / 128) workgroups of the matrix-core kernel would leave most
+ * of the GPU idle, each query tile's key range is split over several
+ * workgroups that write partial (max, sum, unnormalised output) rows to
+ * `workspace`, merged by a second kernel (the running-max identity of the
+ * stable softmax, "Implementation: Sliding Window Attention", Step 2).
+ *
+ *   workspace       : device memory of swa_chunk_workspace_bytes() bytes,
+ *                     16-byte aligned, owned by the caller; may be null when
+ *                     that size is 0 (no split applies; then this call is
+ *                     swa_chunk_forward).  Concurrent calls need separate
+ *                     workspaces.
+ *   workspace_bytes : its size; too small returns SWA_ERR_INVALID_ARG.
+ * The size query returns a negative status for invalid or oversized sizes.
+ */
+int64_t swa_chunk_workspace_bytes(int64_t S, int64_t H, int64_t C, int64_t D, int64_t W,
+                                  int dtype);
+int swa_chunk_forward_split(const void* q, const void* kc, const void* vc, const void* kring,
+                            const void* vring, const int64_t* pos0, void* out, int64_t S,
+                            int64_t H, int64_t C, int64_t D, int64_t W, int dtype,
+                            void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * Chunk append (not part of the timed path): the last min(C, W) tokens of
  * the chunk, at positions pos0 + c, go to ring slots (pos0 + c) mod W.
  *

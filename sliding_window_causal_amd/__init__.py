@@ -17,6 +17,8 @@ Entry points (same names as the C ABI):
                                                  append + decode in one launch
   swa_chunk_forward(q, kc, vc, kring, vring, pos0, out)
                                                  chunk of new tokens continuing a ring
+  swa_chunk_forward_split(q, kc, vc, kring, vring, pos0, out)
+                                                 the same, key range split for few streams
   swa_ring_append_chunk(kc, vc, kring, vring, pos0)
                                                  write a chunk's tokens into the ring
   swa_forward_lse(q, k, v, out, lse, window_size, scale=None)
@@ -29,7 +31,7 @@ Conveniences that allocate the output with torch:
   sliding_window_attention(q, k, v, window_size, scale=None, layout=None) -> out
   decode(q, kring, vring, pos, split=False) -> out
   decode_append(q, knew, vnew, kring, vring, pos) -> out
-  chunk_attention(q, kc, vc, kring, vring, pos0) -> out
+  chunk_attention(q, kc, vc, kring, vring, pos0, split=False) -> out
   SlidingWindowMHA(d_model, num_heads)(x, window) -> out
 """
 
@@ -44,7 +46,8 @@ __all__ = [
     "LIB_PATH", "SWA_F32", "SWA_BF16", "SWA_OK", "SWA_ERR_INVALID_ARG",
     "SWA_ERR_UNSUPPORTED", "SWA_ERR_LAUNCH", "SWAError", "lib", "abi_version",
     "status_string", "swa_forward", "swa_forward_strided", "swa_decode", "swa_ring_append", "swa_chunk_forward",
-    "swa_ring_append_chunk", "swa_decode_workspace_bytes", "swa_decode_split",
+    "swa_ring_append_chunk", "swa_chunk_workspace_bytes", "swa_chunk_forward_split",
+    "swa_decode_workspace_bytes", "swa_decode_split",
     "swa_decode_append", "swa_forward_lse", "swa_backward", "swa_mha_workspace_bytes", "swa_mha_forward", "SlidingWindowMHA",
     "sliding_window_attention", "decode", "decode_append", "chunk_attention",
 ]
@@ -106,6 +109,11 @@ def lib() -> ctypes.CDLL:
     L.swa_decode_append.restype = i32
     L.swa_chunk_forward.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i32, p]
     L.swa_chunk_forward.restype = i32
+    L.swa_chunk_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
+    L.swa_chunk_workspace_bytes.restype = i64
+    L.swa_chunk_forward_split.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i32, p,
+                                          i64, p]
+    L.swa_chunk_forward_split.restype = i32
     L.swa_ring_append_chunk.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i64, i32, p]
     L.swa_ring_append_chunk.restype = i32
     _lib = L
@@ -368,6 +376,33 @@ def swa_chunk_forward(q, kc, vc, kring, vring, pos0, out, stream=None) -> None:
                                    _ptr(pos0), _ptr(out), S, H, C, D, W, code, _stream(q, stream)))
 
 
+def swa_chunk_workspace_bytes(S: int, H: int, C: int, D: int, W: int, dtype) -> int:
+    code = _DTYPES.get(dtype, dtype) if not isinstance(dtype, int) else dtype
+    n = int(lib().swa_chunk_workspace_bytes(S, H, C, D, W, code))
+    if n < 0:
+        raise SWAError(-n, status_string(-n))
+    return n
+
+
+def swa_chunk_forward_split(q, kc, vc, kring, vring, pos0, out, workspace=None,
+                            stream=None) -> None:
+    """swa_chunk_forward with the key range split over workgroups for few
+    streams; ``workspace`` is allocated here when not given."""
+    _check_device(q, kc, vc, kring, vring, pos0, out)
+    code = _dtype_code(q, kc, vc, kring, vring, out)
+    S, H, C, D, W = _check_chunk(q, kc, vc, kring, vring, pos0)
+    if out.shape != q.shape:
+        raise ValueError("out must match q")
+    need = swa_chunk_workspace_bytes(S, H, C, D, W, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().swa_chunk_forward_split(_ptr(q), _ptr(kc), _ptr(vc), _ptr(kring), _ptr(vring),
+                                         _ptr(pos0), _ptr(out), S, H, C, D, W, code,
+                                         _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(),
+                                         _stream(q, stream)))
+
+
 def swa_ring_append_chunk(kc, vc, kring, vring, pos0, stream=None) -> None:
     """Write the chunk's last min(C, W) tokens into ring slots (pos0 + c) mod W."""
     _check_device(kc, vc, kring, vring, pos0)
@@ -377,10 +412,14 @@ def swa_ring_append_chunk(kc, vc, kring, vring, pos0, stream=None) -> None:
                                        S, H, C, D, W, code, _stream(kc, stream)))
 
 
-def chunk_attention(q, kc, vc, kring, vring, pos0):
-    """Chunk continuation returning a new [S, H, C, D] tensor."""
+def chunk_attention(q, kc, vc, kring, vring, pos0, split: bool = False):
+    """Chunk continuation returning a new [S, H, C, D] tensor (split:
+    swa_chunk_forward_split)."""
     out = torch.empty_like(q)
-    swa_chunk_forward(q, kc, vc, kring, vring, pos0, out)
+    if split:
+        swa_chunk_forward_split(q, kc, vc, kring, vring, pos0, out)
+    else:
+        swa_chunk_forward(q, kc, vc, kring, vring, pos0, out)
     return out
 
 

@@ -251,9 +251,48 @@ int swa_ring_append(const void* knew, const void* vnew, void* kring, void* vring
                                             dtype == SWA_F32 ? 4 : 2, (hipStream_t)stream));
 }
 
+int64_t swa_chunk_workspace_bytes(int64_t S, int64_t H, int64_t C, int64_t D, int64_t W,
+                                  int dtype) {
+    if (!positive(S) || !positive(H) || !positive(C) || !positive(D) || !positive(W))
+        return -SWA_ERR_INVALID_ARG;
+    if (!fits(S, H, C, D) || !fits(S, H, W, D)) return -SWA_ERR_UNSUPPORTED;
+    if (dtype != SWA_BF16 || (D != 64 && D != 128)) return 0;
+    return swa::chunk_workspace_bytes(S, H, C, D, W);
+}
+
+namespace {
+
+int chunk_forward(const void* q, const void* kc, const void* vc, const void* kring,
+                  const void* vring, const int64_t* pos0, void* out, int64_t S, int64_t H,
+                  int64_t C, int64_t D, int64_t W, int dtype, void* workspace, void* stream);
+
+}  // namespace
+
 int swa_chunk_forward(const void* q, const void* kc, const void* vc, const void* kring,
                       const void* vring, const int64_t* pos0, void* out, int64_t S, int64_t H,
                       int64_t C, int64_t D, int64_t W, int dtype, void* stream) {
+    return chunk_forward(q, kc, vc, kring, vring, pos0, out, S, H, C, D, W, dtype, nullptr,
+                         stream);
+}
+
+int swa_chunk_forward_split(const void* q, const void* kc, const void* vc, const void* kring,
+                            const void* vring, const int64_t* pos0, void* out, int64_t S,
+                            int64_t H, int64_t C, int64_t D, int64_t W, int dtype,
+                            void* workspace, int64_t workspace_bytes, void* stream) {
+    if (workspace_bytes < 0) return SWA_ERR_INVALID_ARG;
+    const int64_t need = swa_chunk_workspace_bytes(S, H, C, D, W, dtype);
+    if (need < 0) return (int)-need;
+    if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15) != 0))
+        return SWA_ERR_INVALID_ARG;
+    return chunk_forward(q, kc, vc, kring, vring, pos0, out, S, H, C, D, W, dtype,
+                         need > 0 ? workspace : nullptr, stream);
+}
+
+namespace {
+
+int chunk_forward(const void* q, const void* kc, const void* vc, const void* kring,
+                  const void* vring, const int64_t* pos0, void* out, int64_t S, int64_t H,
+                  int64_t C, int64_t D, int64_t W, int dtype, void* workspace, void* stream) {
     if (!q || !kc || !vc || !kring || !vring || !pos0 || !out) return SWA_ERR_INVALID_ARG;
     if (!positive(S) || !positive(H) || !positive(C) || !positive(D) || !positive(W))
         return SWA_ERR_INVALID_ARG;
@@ -266,7 +305,7 @@ int swa_chunk_forward(const void* q, const void* kc, const void* vc, const void*
         return from_hip(swa::launch_chunk_bf16(
             (const swa::bf16*)q, (const swa::bf16*)kc, (const swa::bf16*)vc,
             (const swa::bf16*)kring, (const swa::bf16*)vring, pos0, (swa::bf16*)out, S, H, C,
-            (int)D, W, st));
+            (int)D, W, workspace, st));
     if (dtype == SWA_BF16)
         return from_hip(swa::launch_rowwise_chunk<swa::bf16>(
             (const swa::bf16*)q, (const swa::bf16*)kc, (const swa::bf16*)vc,
@@ -279,6 +318,8 @@ int swa_chunk_forward(const void* q, const void* kc, const void* vc, const void*
                                                          H, C, (int)D, W, st));
     return SWA_ERR_UNSUPPORTED;
 }
+
+}  // namespace
 
 int swa_ring_append_chunk(const void* kc, const void* vc, void* kring, void* vring,
                           const int64_t* pos0, int64_t S, int64_t H, int64_t C, int64_t D,

@@ -350,6 +350,14 @@ hipError_t launch_ring_append_chunk(const void* kc, const void* vc, void* kring,
                            stream);
 }
 
+hipError_t launch_combine_bf16(const float* ws_o, const float* ws_ml, bf16* out, int64_t rows,
+                               int P, int D, hipStream_t stream) {
+    void* cargs[] = {(void*)&ws_o, (void*)&ws_ml, (void*)&out, (void*)&P};
+    const void* k = D == 128 ? (const void*)decode_combine_kernel<128>
+                             : (const void*)decode_combine_kernel<64>;
+    return hipLaunchKernel(k, dim3((unsigned)rows), dim3(64), cargs, 0, stream);
+}
+
 int decode_splits(int64_t S, int64_t H, int64_t W) {
     // Splitting pays while S * H workgroups leave most compute units idle
     // (measured at D = 128, W = 4096: 2.3x at S * H = 32, 1.7x at 64, none

@@ -88,9 +88,21 @@ hipError_t launch_prefill_bf16(const bf16* q, const bf16* k, const bf16* v, bf16
 // pointers, slabs under 2 GiB (chunk_bf16_supports).
 bool chunk_bf16_supports(const void* q, const void* kc, const void* vc, const void* kring,
                          const void* vring, const void* out, int64_t C, int64_t D, int64_t W);
+// With a workspace of chunk_workspace_bytes() the key range of each query
+// tile may be split over chunk_splits() workgroups and the partials merged by
+// launch_combine_bf16.
+constexpr int64_t kChunkSplitTargetWGs = 512;
+constexpr int64_t kChunkMaxSplits = 16;
+int chunk_splits(int64_t S, int64_t H, int64_t C, int64_t W);
+int64_t chunk_workspace_bytes(int64_t S, int64_t H, int64_t C, int64_t D, int64_t W);
 hipError_t launch_chunk_bf16(const bf16* q, const bf16* kc, const bf16* vc, const bf16* kring,
                              const bf16* vring, const int64_t* pos0, bf16* out, int64_t S,
-                             int64_t H, int64_t C, int D, int64_t W, hipStream_t stream);
+                             int64_t H, int64_t C, int D, int64_t W, void* workspace,
+                             hipStream_t stream);
+// Merge P partial rows (ws_o [rows * P, D], ws_ml [rows * P, 2]: max in log2
+// units, sum) into out [rows, D]; D in {64, 128}.
+hipError_t launch_combine_bf16(const float* ws_o, const float* ws_ml, bf16* out, int64_t rows,
+                               int P, int D, hipStream_t stream);
 
 // bf16 ring decode; D in {64, 128}, W <= kDecodeMaxW.  With a workspace of
 // decode_workspace_bytes(S, H, D, W) bytes the window may be split over

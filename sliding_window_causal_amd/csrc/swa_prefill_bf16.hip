@@ -78,6 +78,11 @@ struct Args {
     const bf16* vring;
     const int64_t* pos0;
     int C;
+    // chunk continuation split over the key range (nsplit > 1): partial
+    // unnormalised outputs, maxima (log2 units) and sums per (row, split)
+    int nsplit;
+    float* ws_o;          // [S * H * C * nsplit, D]
+    float* ws_ml;         // [S * H * C * nsplit, 2]
     // prefill only, optional: each row's log-sum-exp of its scaled scores,
     // ln(sum_j exp(s_ij * scale)), at lse[bh * T + i] (for the backward)
     float* lse;
@@ -124,7 +129,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // deals workgroups round-robin over 8 XCDs), heads stay together, and
     // within a head the tiles with the longest bands (the last ones) go first.
     const int bid = blockIdx.x;
-    const int logical = a.remap ? (bid & 7) * (a.nblocks >> 3) + (bid >> 3) : bid;
+    int logical = a.remap ? (bid & 7) * (a.nblocks >> 3) + (bid >> 3) : bid;
+    int sp = 0;                                      // key-range split (chunk continuation)
+    if constexpr (CHUNK) {
+        sp = logical % a.nsplit;
+        logical /= a.nsplit;
+    }
     const int bh = logical / a.nqt;
     const int qt = a.nqt - 1 - (logical - bh * a.nqt);
     const int W = a.W;
@@ -151,8 +161,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int qi = qw0 + lr;                         // this lane's query
     const int klo = max(i0 - W + 1, 0);
     const int khi = min(i0 + C::BM, T);
-    const int t0 = klo / C::BN;                      // workgroup's key tiles [t0, t1)
-    const int t1 = (khi + C::BN - 1) / C::BN;
+    int t0 = klo / C::BN;                            // workgroup's key tiles [t0, t1)
+    int t1 = (khi + C::BN - 1) / C::BN;
+    if constexpr (CHUNK) {
+        // split sp of nsplit takes its share of the band's tiles
+        const int per = (t1 - t0 + a.nsplit - 1) / a.nsplit;
+        const int s0 = t0 + sp * per;
+        t1 = min(t1, s0 + per);
+        t0 = s0;
+    }
     int wt0 = t1, wt1 = t1;                          // this wave's key tiles [wt0, wt1)
     if (qw0 < T) {
         wt0 = max(qw0 - W + 1, 0) / C::BN;
@@ -163,6 +180,34 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int k0 = t * C::BN;
         return (k0 + C::BN - 1 <= qw0) && (qw0 + 31 - k0 < W);
     };
+    // a split's partial row: unnormalised output o, max m (raw units) and
+    // this lane's half of the sum; the merge rescales partials to a common max
+    auto write_partial = [&](const f32x16 (&o)[D / 32], float m, float lsum) {
+        const int crow = qi - p0r;
+        if (crow >= a.C) return;
+        const int64_t idx = ((int64_t)bh * a.C + crow) * a.nsplit + sp;
+        float* po = a.ws_o + idx * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<f32x4*>(po + 32 * db + 8 * g + 4 * hh) =
+                    f32x4{o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+        const float l = swap_sum(lsum);
+        if (hh == 0) {
+            a.ws_ml[2 * idx] = m * a.c;                  // -inf for a row with no key here
+            a.ws_ml[2 * idx + 1] = l;
+        }
+    };
+    if constexpr (CHUNK) {
+        if (t0 >= t1) {                              // an empty split
+            f32x16 z[D / 32];
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) z[db] = f32x16{};
+            write_partial(z, -__builtin_inff(), 0.f);
+            return;
+        }
+    }
 
     // Q^T operand: q[qi][16 dc + 8 hh .. + 7] (rows past T read row T - 1;
     // their outputs are never stored).
@@ -407,6 +452,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     __builtin_amdgcn_s_waitcnt(0);   // no LDS load may outlive the workgroup
 
+    if constexpr (CHUNK) {
+        if (a.nsplit > 1) {
+            write_partial(o, m, lsum);
+            return;
+        }
+    }
+
     // ---- finalise: O / l, bf16, store (lane holds d = 32 db + 8 g + 4 hh + 0..3)
     const float l = swap_sum(lsum);
     const float inv = 1.f / l;
@@ -431,7 +483,7 @@ hipError_t launch(Args a, int64_t B, int64_t H, int64_t rows, hipStream_t stream
     using C = Cfg<D, NW>;
     a.H = (int)H;
     a.nqt = (int)((rows + C::BM - 1) / C::BM);
-    const int64_t nblocks = B * H * a.nqt;
+    const int64_t nblocks = B * H * a.nqt * (CHUNK ? a.nsplit : 1);
     a.nblocks = (int)nblocks;
     a.remap = (nblocks % 8 == 0) ? 1 : 0;
     void* args[] = {(void*)&a};
@@ -497,17 +549,42 @@ bool chunk_bf16_supports(const void* q, const void* kc, const void* vc, const vo
            W + C + 64 < ((int64_t)1 << 30);
 }
 
+int chunk_splits(int64_t S, int64_t H, int64_t C, int64_t W) {
+    // Splitting the key range pays while S * H * (C / 128) workgroups leave
+    // the GPU mostly idle; each split keeps at least 8 key tiles (256 keys).
+    const int64_t wgs = S * H * ((C + 127) / 128);
+    if (wgs >= kChunkSplitTargetWGs / 2) return 1;
+    const int64_t tiles = (W + 128 + 31) / 32;
+    int64_t p = (kChunkSplitTargetWGs + wgs - 1) / wgs;
+    p = p < tiles / 8 ? p : tiles / 8;
+    p = p < kChunkMaxSplits ? p : kChunkMaxSplits;
+    return p < 1 ? 1 : (int)p;
+}
+
+int64_t chunk_workspace_bytes(int64_t S, int64_t H, int64_t C, int64_t D, int64_t W) {
+    const int P = chunk_splits(S, H, C, W);
+    return P == 1 ? 0 : S * H * C * P * (D + 2) * (int64_t)sizeof(float);
+}
+
 hipError_t launch_chunk_bf16(const bf16* q, const bf16* kc, const bf16* vc, const bf16* kring,
                              const bf16* vring, const int64_t* pos0, bf16* out, int64_t S,
-                             int64_t H, int64_t C, int D, int64_t W, hipStream_t stream) {
+                             int64_t H, int64_t C, int D, int64_t W, void* workspace,
+                             hipStream_t stream) {
     Args a = make_args(q, kc, vc, out, contiguous_layout(H, C, D), 1.0f / sqrtf((float)D));
     a.kring = kring;
     a.vring = vring;
     a.pos0 = pos0;
     a.C = (int)C;
     a.W = (int)W;
-    if (D == 128) return launch<128, 4, true>(a, S, H, C, stream);
-    return launch<64, 4, true>(a, S, H, C, stream);
+    a.nsplit = workspace ? chunk_splits(S, H, C, W) : 1;
+    if (a.nsplit > 1) {
+        a.ws_o = (float*)workspace;
+        a.ws_ml = a.ws_o + S * H * C * a.nsplit * D;
+    }
+    hipError_t e = D == 128 ? launch<128, 4, true>(a, S, H, C, stream)
+                            : launch<64, 4, true>(a, S, H, C, stream);
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    return launch_combine_bf16(a.ws_o, a.ws_ml, out, S * H * C, a.nsplit, D, stream);
 }
 
 }  // namespace swa

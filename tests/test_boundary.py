@@ -28,7 +28,8 @@ def test_header_declares_entry_points():
               "swa_abi_version", "swa_chunk_forward", "swa_ring_append_chunk",
               "swa_forward_strided", "swa_decode_workspace_bytes", "swa_decode_split",
               "swa_decode_append", "swa_mha_forward", "swa_mha_workspace_bytes",
-              "swa_backward", "swa_backward_workspace_bytes", "swa_forward_lse"):
+              "swa_backward", "swa_backward_workspace_bytes", "swa_forward_lse",
+              "swa_chunk_forward_split", "swa_chunk_workspace_bytes"):
         assert n in names
 
 
@@ -279,6 +280,25 @@ def test_append_chunk_invalid_args(kw):
 
 def test_append_chunk_unsupported_dtype():
     assert _app_chunk(dt=4) == swa.SWA_ERR_UNSUPPORTED
+
+
+def test_chunk_workspace_bytes():
+    L = swa.lib()
+    n = L.swa_chunk_workspace_bytes(1, 4, 128, 128, 4096, swa.SWA_BF16)
+    assert n > 0 and n % (4 * (128 + 2)) == 0
+    assert L.swa_chunk_workspace_bytes(64, 32, 2048, 128, 4096, swa.SWA_BF16) == 0
+    assert L.swa_chunk_workspace_bytes(1, 4, 128, 128, 4096, swa.SWA_F32) == 0
+    assert L.swa_chunk_workspace_bytes(0, 4, 128, 128, 4096, swa.SWA_BF16) == -swa.SWA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(ws=None), dict(nb=64), dict(nb=-1),
+                                dict(ws=ctypes.c_void_p(0x1004)), dict(C=0)])
+def test_chunk_split_invalid_args(kw):
+    a = dict(ws=DUMMY, nb=1 << 40, C=128)
+    a.update(kw)
+    rc = swa.lib().swa_chunk_forward_split(DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, 1, 4,
+                                           a["C"], 128, 4096, swa.SWA_BF16, a["ws"], a["nb"], None)
+    assert rc == swa.SWA_ERR_INVALID_ARG
 
 
 def test_oversized_grid_is_unsupported():

@@ -238,3 +238,59 @@ def test_mfma_chunk_stream_matches_mfma_prefill():
     rows = [0, 511, 512, 513, 1511, 1512, T - 1]
     ref = so.swa_rows(npy(q[0]), npy(k[0]), npy(v[0]), W, rows)
     assert_close(out[0][:, rows], ref, dtype, "chunks vs oracle rows")
+
+
+# ---- key-range split for few streams (swa_chunk_forward_split) ----
+
+SPLIT_CASES = [
+    # D, W, C, pos0 per stream
+    (128, 4096, 128, [4096 * 3 + 77]),             # one stream, one query tile: 16 splits
+    (128, 1000, 300, [0, 5000]),                   # a young and a wrapped stream
+    (64, 640, 200, [300, 640, 100_003]),
+]
+
+
+@pytest.mark.parametrize("D,W,C,pos0", SPLIT_CASES)
+def test_split_chunk_matches_oracle_and_unsplit(D, W, C, pos0):
+    S, H = len(pos0), 4
+    dtype = torch.bfloat16
+    assert swa.swa_chunk_workspace_bytes(S, H, C, D, W, dtype) > 0
+    g = si.generator(200 + W, DEV)
+    qc, kc, vc = (si.normal((S, H, C, D), g, dtype, DEV) for _ in range(3))
+    kr = si.normal((S, H, W, D), g, dtype, DEV)
+    vr = si.normal((S, H, W, D), g, dtype, DEV)
+    for s in range(S):
+        if pos0[s] < W:
+            kr[s, :, pos0[s]:] = float("nan")
+            vr[s, :, pos0[s]:] = float("nan")
+    p0 = torch.tensor(pos0, dtype=torch.int64, device=DEV)
+    out = swa.chunk_attention(qc, kc, vc, kr, vr, p0, split=True)
+    base = swa.chunk_attention(qc, kc, vc, kr, vr, p0)
+    torch.cuda.synchronize()
+    ref = so.swa_chunk(npy(qc), npy(kc), npy(vc), npy(kr), npy(vr), pos0, W)
+    assert_close(out, ref, dtype, "split chunk vs oracle")
+    assert_close(out, npy(base).astype(np.float64), dtype, "split chunk vs unsplit")
+
+
+def test_split_chunk_stream_matches_prefill():
+    """A 1100-token sequence fed in chunks of 128 (the last ragged) through
+    the split path, against one prefill."""
+    H, D, W, T = 4, 128, 512, 1100
+    dtype = torch.bfloat16
+    g = si.generator(210, DEV)
+    q, k, v = (si.normal((1, H, T, D), g, dtype, DEV) for _ in range(3))
+    kr = torch.full((1, H, W, D), float("nan"), dtype=dtype, device=DEV)
+    vr = torch.full_like(kr, float("nan"))
+    outs, p = [], 0
+    while p < T:
+        C = min(128, T - p)
+        sl = slice(p, p + C)
+        qc, kc, vc = (x[:, :, sl].contiguous() for x in (q, k, v))
+        p0 = torch.tensor([p], dtype=torch.int64, device=DEV)
+        outs.append(swa.chunk_attention(qc, kc, vc, kr, vr, p0, split=True))
+        swa.swa_ring_append_chunk(kc, vc, kr, vr, p0)
+        p += C
+    out = torch.cat(outs, dim=2)
+    pre = swa.sliding_window_attention(q, k, v, W)
+    torch.cuda.synchronize()
+    assert_close(out, npy(pre).astype(np.float64), dtype, "split chunks vs prefill")
