@@ -295,7 +295,7 @@ def main() -> int:
         # path): 2048 new tokens of one stream, and 512 of four, 32 heads,
         # D = 128; every query sees W keys.
         res["chunk"] = []
-        for S, Cn in ((1, 2048), (4, 512)):
+        for S, Cn in ((1, 2048), (4, 512), (1, 128)):
             gc = si.generator(wp.seed, dev)
             qc, kc, vc = (si.normal((S, wp.H, Cn, wp.D), gc, torch.bfloat16, dev) for _ in range(3))
             krc = si.normal((S, wp.H, wp.W, wp.D), gc, torch.bfloat16, dev)
@@ -304,11 +304,17 @@ def main() -> int:
             oc = torch.empty_like(qc)
             tc = time_launches(lambda: swa.swa_chunk_forward(qc, kc, vc, krc, vrc, p0c, oc,
                                                              stream=stream), stream, 50, 20)
+            nws = swa.swa_chunk_workspace_bytes(S, wp.H, Cn, wp.D, wp.W, torch.bfloat16)
+            wsc = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+            ts = time_launches(lambda: swa.swa_chunk_forward_split(
+                qc, kc, vc, krc, vrc, p0c, oc, wsc, stream=stream), stream, 50, 20)
             fl = 4 * S * wp.H * wp.D * Cn * wp.W
             res["chunk"].append({"S": S, "C": Cn, "H": wp.H, "D": wp.D, "W": wp.W,
                                  "kernel_ms_mean": tc, "useful_flop_per_launch": fl,
-                                 "TFLOPs": fl / (tc * 1e-3) / 1e12})
-            del qc, kc, vc, krc, vrc, oc
+                                 "TFLOPs": fl / (tc * 1e-3) / 1e12,
+                                 "split_workspace_bytes": nws, "split_ms_mean": ts,
+                                 "split_TFLOPs": fl / (ts * 1e-3) / 1e12})
+            del qc, kc, vc, krc, vrc, oc, wsc
     if do_p and args.only == "all":
         # The whole attention module of one such layer (d_model 4096 = 32
         # heads x 128): q, k, v, output projections (rocBLAS) around the band.
