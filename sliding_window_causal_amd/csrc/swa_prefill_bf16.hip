@@ -28,12 +28,17 @@
 // Data movement: K and V tiles go HBM -> LDS directly (buffer loads with an
 // LDS destination; the hardware range check returns zeros past the sequence
 // end) through rings of PF + 1 slots, issued PF tiles ahead, with K one tile
-// ahead of V.  Iteration j therefore
-// issues S(j+1) = K(j+1) Q^T on the matrix cores while the vector ALUs run
-// the softmax of tile j, then O += V(j)^T P(j)^T.  The LDS layouts are XOR
-// swizzled on 16-byte chunks so every LDS read is bank-conflict free.
+// ahead of V.  Iteration j issues S(j+1) = K(j+1) Q^T on the matrix cores
+// while the vector ALUs run the softmax of tile j, then O += V(j)^T P(j)^T.
+// The K operands of S(j+1) were read from LDS during iteration j-1, so an
+// iteration starts its matrix work right after the barrier.  The LDS layouts
+// are XOR swizzled on 16-byte chunks so every LDS read is bank-conflict free;
+// the loop is unrolled over the ring's 4 slots, so slot addresses are
+// immediate offsets.
 
 #include "swa_mfma.h"
+
+#include <type_traits>
 
 namespace swa {
 namespace {
@@ -49,9 +54,10 @@ struct Cfg {
     static constexpr int R = PF + 1;            // LDS ring slots per matrix
     static constexpr int LDS_BYTES = 2 * R * TILEB;
     static constexpr int NLD_W = TILEB / 1024 / NW;   // 1-KiB LDS loads per wave per tile
-    // vmcnt that leaves the loads of the 2 PF - 2 most recent tile loads in
-    // flight (see the issue order in the kernel)
-    static constexpr int VM_WAIT = (2 * PF - 2) * NLD_W;
+    // vmcnt that leaves only the two most recent tile loads (those of the
+    // current step) in flight (see the issue order in the kernel)
+    static constexpr int VM_WAIT = (2 * PF - 4) * NLD_W;
+    static_assert(R == 4, "the key loop is unrolled over the 4 ring slots");
     static_assert(VM_WAIT < 64, "vmcnt range");
     static_assert(D == 64 || D == 128, "head size");
     static_assert((TILEB / 1024) % NW == 0, "tile loads split evenly over waves");
@@ -239,8 +245,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // V(j+PF) K(j+1+PF); tile indices past the band are clamped to its last
     // tile (loaded into a free slot, never read), so every step issues the
     // same number of loads and a fixed vmcnt waits for exactly the oldest.
-    auto kslot = [&](int t) { return ring + ((t - t0) % C::R) * C::TILEB; };
-    auto vslot = [&](int t) { return ring + (C::R + (t - t0) % C::R) * C::TILEB; };
+    // Ring slot s of K and of V (tile t lives in slot (t - t0) mod R).  Slot
+    // numbers are compile-time constants at every call site, so the LDS
+    // reads carry the slot in their immediate offset.
+    auto kslot_n = [&](int s) { return ring + (s % C::R) * C::TILEB; };
+    auto vslot_n = [&](int s) { return ring + (C::R + s % C::R) * C::TILEB; };
     uint32_t koff[C::NLD_W], voff[C::NLD_W];
     tile_offsets<D, NW, kSwzK>(koff, wave, lane, 2 * krs);
     tile_offsets<D, NW, kSwzV>(voff, wave, lane, 2 * vrs);
@@ -291,18 +300,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             lds_load16_global(lds + (wave * C::NLD_W + i) * 1024, src + logical * 8);
         }
     };
-    auto load_k = [&](int t) {
+    // tile t into ring slot s (s = t - t0 modulo the ring)
+    auto load_k = [&](int t, int s) {
         if constexpr (CHUNK)
-            load_chunk_tile(t, Kbh, Krh, ktb, kslab, koff, lds_addr(kslot(t)), false);
+            load_chunk_tile(t, Kbh, Krh, ktb, kslab, koff, lds_addr(kslot_n(s)), false);
         else
-            dma_tile(rows_rsrc(Kbh, min(t, t1 - 1) * ktb, kslab), lds_addr(kslot(t)), wave,
+            dma_tile(rows_rsrc(Kbh, min(t, t1 - 1) * ktb, kslab), lds_addr(kslot_n(s)), wave,
                             koff);
     };
-    auto load_v = [&](int t) {
+    auto load_v = [&](int t, int s) {
         if constexpr (CHUNK)
-            load_chunk_tile(t, Vbh, Vrh, vtb, vslab, voff, lds_addr(vslot(t)), true);
+            load_chunk_tile(t, Vbh, Vrh, vtb, vslab, voff, lds_addr(vslot_n(s)), true);
         else
-            dma_tile(rows_rsrc(Vbh, min(t, t1 - 1) * vtb, vslab), lds_addr(vslot(t)), wave,
+            dma_tile(rows_rsrc(Vbh, min(t, t1 - 1) * vtb, vslab), lds_addr(vslot_n(s)), wave,
                             voff);
     };
     // Publish loads: wait until at most VM_WAIT of this wave's loads are in
@@ -314,11 +324,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     };
 #pragma unroll
     for (int i = 0; i < C::PF; ++i) {
-        load_k(t0 + i);
-        load_v(t0 + i);
+        load_k(t0 + i, i);
+        load_v(t0 + i, i);
     }
-    load_k(t0 + C::PF);
-    publish();   // K(t0), V(t0), K(t0+1) have landed
+    load_k(t0 + C::PF, C::PF);
+    publish();   // K(t0), V(t0), K(t0+1), V(t0+1), K(t0+2) have landed
 
     // Row max of a score tile (in-lane over 16 keys, then across the lane
     // pair l, l ^ 32 that shares the query).
@@ -349,22 +359,32 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // its band, and their probabilities must come out as exact zeros.
     f32x16 sA = f32x16{}, sB = f32x16{};
     if (needs(t0)) {
-        qk_tile<D>(kslot(t0), qf, lr, hh, ksw, sA);
+        qk_tile<D>(kslot_n(0), qf, lr, hh, ksw, sA);
         if (!interior(t0)) mask_tile(sA, qi, t0 * C::BN, hh, W);
         raise_ref(tile_max(sA));
     }
+    // K operands of the next score tile live in registers one step ahead:
+    // step j computes S(j+1) from kf of K(j+1) and reads K(j+2) into the
+    // other set, so no step waits on LDS before its first MFMA.
+    bf16x8 kfA[D / 16], kfB[D / 16];
+#pragma unroll
+    for (int dc = 0; dc < D / 16; ++dc) kfA[dc] = read_row_frag<D>(kslot_n(1), lr, hh, dc);
     __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8) | 15 | (3 << 14));   // LDS reads done
     __builtin_amdgcn_s_barrier();   // every wave is done with K(t0) before its slot is reloaded
 
-    // ---- one key tile j: S(j+1) on the matrix cores alongside softmax(j)
-    auto body = [&](f32x16& sc, f32x16& sn, int j) {
+    // ---- one key tile j: S(j+1) on the matrix cores alongside softmax(j).
+    // KS = (j - t0) mod 4 is a compile-time constant, so every ring slot
+    // address below is one.
+    auto body = [&](auto ks, f32x16& sc, f32x16& sn, bf16x8 (&kc)[D / 16],
+                    bf16x8 (&kn)[D / 16], int j) {
+        constexpr int KS = decltype(ks)::value;
         // Slots released by the barrier that ended the previous step:
-        // V(j+PF) replaces V(j-1), K(j+1+PF) replaces K(j).
-        load_v(j + C::PF);
-        load_k(j + 1 + C::PF);
+        // V(j+PF) replaces V(j-1), K(j+1+PF) replaces K(j) (whose operands
+        // were read two steps ago).
+        load_v(j + C::PF, KS + C::PF);
+        load_k(j + 1 + C::PF, KS + 1 + C::PF);
         const bool nj = needs(j), nn = needs(j + 1);
-        const char* Kn = kslot(j + 1);
-        const char* Vc = vslot(j);
+        const char* Vc = vslot_n(KS);
         float mxn;
 
         // Every wave runs every tile of the workgroup, so the accumulator
@@ -381,16 +401,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             constexpr int NEA = 12;                 // exps issued in region A
             constexpr int NPRE = 2;                 // of which before the first MFMA
             bf16x8 p0, p1;
-            // All K(j+1) operands and the V(j) operands of chunk 0 are read
-            // from LDS up front, so their latency hides behind the first
-            // slices instead of stalling each MFMA.
-            bf16x8 kf[ND], va0[D / 32], va1[D / 32];
-            {
-                const char* r0 = Kn + lr * (2 * D);
-#pragma unroll
-                for (int dc = 0; dc < ND; ++dc)
-                    kf[dc] = *reinterpret_cast<const bf16x8*>(r0 + (((2 * dc + hh) ^ ksw) << 4));
-            }
+            // The V(j) operands of chunk 0 are read up front, so their
+            // latency hides behind region A.
+            bf16x8 va0[D / 32], va1[D / 32];
             read_v_chunk<D>(Vc, 0, lane, va0);
             // The first probabilities need no LDS data: they cover the
             // latency of the first operand reads.
@@ -405,7 +418,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             sn = f32x16{};
 #pragma unroll
             for (int dc = 0; dc < ND; ++dc) {
-                sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[dc], qf[dc], sn, 0, 0, 0);
+                sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[dc], qf[dc], sn, 0, 0, 0);
 #pragma unroll
                 for (int v = NPRE + dc * (NEA - NPRE) / ND; v < NPRE + (dc + 1) * (NEA - NPRE) / ND; ++v)
                     sc[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], c, -mc));
@@ -421,6 +434,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va0[db], p0, o[db], 0, 0, 0);
+            // K(j+2), published by the barrier that ended the previous step
+#pragma unroll
+            for (int dc = 0; dc < ND; ++dc) kn[dc] = read_row_frag<D>(kslot_n(KS + 2), lr, hh, dc);
 #pragma unroll
             for (int v = NEA; v < 16; ++v) sc[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], c, -mc));
             p1 = pack_p(sc, 8, ps);
@@ -440,13 +456,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             }
             raise_ref(mxn);
         }
-        publish();   // V(j+1) and K(j+2), needed by the next step, have landed
+        publish();   // V(j+2) and K(j+3) have landed
     };
 
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
     for (int j = t0;;) {
-        body(sA, sB, j);
+        body(I0{}, sA, sB, kfA, kfB, j);
         if (++j >= t1) break;
-        body(sB, sA, j);
+        body(I1{}, sB, sA, kfB, kfA, j);
+        if (++j >= t1) break;
+        body(I2{}, sA, sB, kfA, kfB, j);
+        if (++j >= t1) break;
+        body(I3{}, sB, sA, kfB, kfA, j);
         if (++j >= t1) break;
     }
 
