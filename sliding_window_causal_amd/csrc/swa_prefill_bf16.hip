@@ -126,6 +126,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     using C = Cfg<D, NW>;
     // Tile t lives in slot (t - t0) % R of the K ring and of the V ring.
     __shared__ __attribute__((aligned(1024))) char ring[2 * C::R * C::TILEB];
+    __shared__ int rerun;            // set when the fast pass must be redone
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS load bases go to M0
     const int lane = tid & 63;
@@ -233,10 +234,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int ksw = kswz<D>(lr);
 
     f32x16 o[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-    float m = -__builtin_inff();      // reference max (raw score units)
-    float lsum = 0.f;                 // this lane's half of the row sum
+    float m;                          // reference max (raw score units)
+    float lsum;                       // this lane's half of the row sum
+    // Fast pass (prefill, careful = false): the reference m only has to keep
+    // the exponents in range, so once every row of the wave has one, tiles
+    // inside every row's band skip the row max.  Scores that later exceed the
+    // reference by more than the fp32 exponent range make a probability, the
+    // row sum or the output non-finite; the workgroup then redoes its rows
+    // with the max taken on every tile (careful pass).  The chunk
+    // continuation always runs careful.
+    bool careful = CHUNK;
+    bool ref_set;                     // every row of the wave has a finite m
+    // Cleared before the prologue's tile loads (asm with memory clobbers
+    // keep the store ahead of them) and so before its first barrier.
+    if (tid == 0) rerun = 0;
     const float c = a.c;
     const float tau = kRescaleLog2 / c;
 
@@ -322,14 +333,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         __builtin_amdgcn_s_waitcnt((C::VM_WAIT & 15) | ((C::VM_WAIT >> 4) << 14) | (7 << 4) | (0 << 8));
         __builtin_amdgcn_s_barrier();
     };
-#pragma unroll
-    for (int i = 0; i < C::PF; ++i) {
-        load_k(t0 + i, i);
-        load_v(t0 + i, i);
-    }
-    load_k(t0 + C::PF, C::PF);
-    publish();   // K(t0), V(t0), K(t0+1), V(t0+1), K(t0+2) have landed
-
     // Row max of a score tile (in-lane over 16 keys, then across the lane
     // pair l, l ^ 32 that shares the query).
     auto tile_max = [&](const f32x16& s) {
@@ -353,7 +356,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
         }
+        ref_set = !__any(m == -__builtin_inff());
     };
+
+  for (;;) {   // fast pass, then (rarely) the careful pass
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+    m = -__builtin_inff();
+    lsum = 0.f;
+    ref_set = false;
+#pragma unroll
+    for (int i = 0; i < C::PF; ++i) {
+        load_k(t0 + i, i);
+        load_v(t0 + i, i);
+    }
+    load_k(t0 + C::PF, C::PF);
+    publish();   // K(t0), V(t0), K(t0+1), V(t0+1), K(t0+2) have landed
 
     // Score tiles start finite: a wave computes (and discards) tiles outside
     // its band, and their probabilities must come out as exact zeros.
@@ -385,7 +403,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         load_k(j + 1 + C::PF, KS + 1 + C::PF);
         const bool nj = needs(j), nn = needs(j + 1);
         const char* Vc = vslot_n(KS);
-        float mxn;
+        float mxn = 0.f;   // chunk continuation: the row max of S(j+1)
 
         // Every wave runs every tile of the workgroup, so the accumulator
         // path has no branches; a tile outside this wave's band gets
@@ -444,17 +462,24 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1[db], p1, o[db], 0, 0, 0);
-            mxn = tile_max(sn);
+            if constexpr (CHUNK) mxn = tile_max(sn);
             __builtin_amdgcn_sched_barrier(0);
             lsum += ps;
         }
+        // Edge tiles are masked; their max, and that of every tile in the
+        // careful pass or before every row has a reference, updates m.
         if (nn) {
-            // Edge tiles are masked, and their max taken again, here.
-            if (!interior(j + 1)) {
-                mask_tile(sn, qi, (j + 1) * C::BN, hh, W);
-                mxn = tile_max(sn);
+            const bool edge = !interior(j + 1);
+            if constexpr (CHUNK) {
+                if (edge) {
+                    mask_tile(sn, qi, (j + 1) * C::BN, hh, W);
+                    mxn = tile_max(sn);
+                }
+                raise_ref(mxn);
+            } else if (edge || careful || !ref_set) {
+                if (edge) mask_tile(sn, qi, (j + 1) * C::BN, hh, W);
+                raise_ref(tile_max(sn));
             }
-            raise_ref(mxn);
         }
         publish();   // V(j+2) and K(j+3) have landed
     };
@@ -474,7 +499,27 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (++j >= t1) break;
     }
 
-    __builtin_amdgcn_s_waitcnt(0);   // no LDS load may outlive the workgroup
+    __builtin_amdgcn_s_waitcnt(0);   // every tile load has landed
+    if (careful) break;
+    // Any inf or NaN in this lane's row sum or outputs shows in their sum:
+    // its exponent field is all ones.  The empty asm hides the bits' origin,
+    // so the test is not folded into a float compare, which this file's
+    // no-NaN float model would reduce to an infinity test.
+    {
+        float chk = lsum;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) chk += o[db][v];
+        uint32_t bits = __float_as_uint(chk);
+        asm volatile("" : "+v"(bits));
+        const bool bad = (bits & 0x7f800000u) == 0x7f800000u;
+        if (__any(bad) && lane == 0) rerun = 1;
+    }
+    __syncthreads();
+    if (rerun == 0) break;
+    careful = true;
+  }
 
     if constexpr (CHUNK) {
         if (a.nsplit > 1) {

@@ -170,6 +170,59 @@ def test_bf16_scaled_inputs_stay_within_tolerance():
     assert_close(out, so.swa_dense(npy(q), npy(k), npy(v), 200), torch.bfloat16)
 
 
+def _ramp_qkv(T, D, slope, seed):
+    """Scores that grow along the sequence: q = 1/4, k_j = slope * j plus a
+    little noise, v ~ N(0, 1); q . k_j / sqrt(D) rises by about
+    8 * slope * sqrt(D) / 4 per key."""
+    g = si.generator(seed, DEV)
+    q = torch.full((1, 2, T, D), 0.25, device=DEV)
+    ramp = slope * torch.arange(T, device=DEV, dtype=torch.float32).view(1, 1, T, 1)
+    k = ramp + 0.1 * si.normal((1, 2, T, D), g, torch.float32, DEV)
+    v = si.normal((1, 2, T, D), g, torch.float32, DEV)
+    return q.bfloat16(), k.bfloat16(), v.bfloat16()
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("T,W", [(1024, 1024), (2048, 256), (700, 100)])
+def test_bf16_scores_growing_beyond_fp32_range(T, W, D):
+    """Within a window the scores rise by hundreds of log2 units above those
+    of its first key tile, far past the fp32 exponent range: probabilities
+    taken against an early reference would overflow.  The output (and the
+    row log-sum-exp) must still be finite and match the oracle."""
+    q, k, v = _ramp_qkv(T, D, 1.0, seed=T + W + D)
+    s = q.float()[0, 0, 0] @ k.float()[0, 0].T / D ** 0.5
+    assert (s[W - 1] - s[0]).item() * 1.4427 > 200        # the growth is really there
+    out = run_fwd(q, k, v, W)
+    ref = so.swa_dense(npy(q), npy(k), npy(v), W)
+    assert_close(out, ref, torch.bfloat16, f"T={T} W={W} D={D}")
+    out2 = torch.empty_like(q)
+    lse = torch.empty(1, 2, T, dtype=torch.float32, device=DEV)
+    swa.swa_forward_lse(q, k, v, out2, lse, W)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out)
+    lref = so.swa_lse(npy(q), npy(k), W)
+    assert np.all(np.abs(npy(lse) - lref) <= 1e-2 + 1e-3 * np.abs(lref))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_one_huge_key_matches_oracle_and_stays_local(D):
+    """One key with an enormous dot product against half of the queries:
+    rows whose window holds it follow it (and overflow any early reference);
+    every other row is bit-identical to the run without it."""
+    T, W = 900, 200
+    q, k, v = si.prefill_qkv(1, 2, T, D, dtype=torch.bfloat16, seed=15, device=DEV)
+    base = run_fwd(q, k, v, W)
+    j0 = 300
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, j0] = 2000.0
+    v2[:, :, j0] = -1000.0
+    out = run_fwd(q, k2, v2, W)
+    assert_close(out, so.swa_dense(npy(q), npy(k2), npy(v2), W), torch.bfloat16, "huge key")
+    for i in range(T):
+        if not (j0 <= i <= j0 + W - 1):
+            assert torch.equal(out[:, :, i], base[:, :, i]), f"row {i}"
+
+
 # ----------------------------------------------------------------------------
 # Bitwise invariants
 # ----------------------------------------------------------------------------
