@@ -251,6 +251,13 @@ def main() -> int:
         res["config"]["prefill"] = {"B": wp.B, "H": wp.H, "T": wp.T, "D": wp.D, "W": wp.W,
                                     "useful_flop_per_launch": flops, "kernel_ms_mean": pm,
                                     "kernel_ms_min": min(p_ms)}
+        if do_d:
+            # context: in the step each prefill follows a decode that streams
+            # 16 GiB through the caches; launched back to back it starts warm
+            pb = time_launches(lambda: swa.swa_forward(q, k, v, out, wp.W, stream=stream),
+                               stream, 20, 5)
+            res["config"]["prefill"]["kernel_ms_back_to_back"] = pb
+            res["config"]["prefill"]["TFLOPs_back_to_back"] = flops / (pb * 1e-3) / 1e12
         res["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
                            "traffic": read_traffic("prefill_bf16_t8192_w4096_traffic.txt", sha),
