@@ -258,10 +258,21 @@ def main() -> int:
                                stream, 20, 5)
             res["config"]["prefill"]["kernel_ms_back_to_back"] = pb
             res["config"]["prefill"]["TFLOPs_back_to_back"] = flops / (pb * 1e-3) / 1e12
+            # context: what the vendor library's bf16 GEMM (torch.mm ->
+            # hipBLASLt) reaches on this device, 8192^3, fp32 accumulate
+            gg = si.generator(wp.seed + 13, dev)
+            ga = si.normal((8192, 8192), gg, torch.bfloat16, dev)
+            gb = si.normal((8192, 8192), gg, torch.bfloat16, dev)
+            tg = time_launches(lambda: torch.mm(ga, gb), stream, 10, 3)
+            vendor_ref = {"TFLOPs": 2 * 8192 ** 3 / (tg * 1e-3) / 1e12,
+                          "how": "torch.mm bf16 8192 x 8192 x 8192 on this device"}
+            del ga, gb
         res["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
                            "traffic": read_traffic("prefill_bf16_t8192_w4096_traffic.txt", sha),
                            "kernel": "prefill_bf16_kernel<128,4>", "kernel_source_sha": sha}
+        if do_d:
+            res["roofline"]["vendor_gemm_reference"] = vendor_ref
     if do_d:
         nbytes = decode_bytes(wd.S, wd.H, wd.D, wd.W)
         dm = sum(d_ms) / len(d_ms)
