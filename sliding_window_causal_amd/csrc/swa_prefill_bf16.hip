@@ -18,7 +18,9 @@
 //   softmax          running reference max m and sum l per query; exp2 with
 //                    the scale 1/sqrt(D) * log2(e) folded into one FMA.  The
 //                    reference is raised, and O rescaled by exp2(m_old -
-//                    m_new), only when a row max grows by more than 2^8.
+//                    m_new), only when a row max grows by more than 2^8; the
+//                    prefill's fast pass takes row maxima only on edge tiles
+//                    and a wave's first tiles (see the kernel).
 //   O^T += V^T P^T   P^T goes from the S^T accumulator straight into the B
 //                    operand (bf16, round to nearest even); the row sum is
 //                    taken over those same bf16 weights (v_dot2 with ones).
@@ -108,9 +110,9 @@ __device__ inline void qk_tile(const char* Kt, const bf16x8 (&qf)[D / 16], int l
     }
 }
 
-// Lazy rescale threshold in log2 units: probabilities stay below 2^8 and the
-// output accumulator is rarely rescaled.  O / l is the same quotient for any
-// reference.
+// Lazy rescale threshold in log2 units: where the max is taken, probabilities
+// stay below 2^8 and the output accumulator is rarely rescaled.  O / l is the
+// same quotient for any reference.
 constexpr float kRescaleLog2 = 8.0f;
 
 // CHUNK = false: prefill of [B, H, T, D].  CHUNK = true: the chunk
