@@ -64,8 +64,11 @@ const char* swa_status_string(int status);
  *   q, k, v, out : [B, H, T, D]  (the (batch, heads, seq, head_dim) layout of
  *                  "27. Sliding-Window Attention", Reference solution)
  *   W            : window in keys including the query itself (W >= 1)
- *   dtype        : SWA_BF16 needs D in {64, 128} and T * D < 2^31;
- *                  SWA_F32 takes 1 <= D <= 256
+ *   dtype        : SWA_BF16 needs D in {64, 128}; SWA_F32 takes 1 <= D <= 256.
+ *                  B * H * T < 2^31 for either (else SWA_ERR_UNSUPPORTED).  bf16
+ *                  runs on the matrix cores when each (b, h) slab of k and v is
+ *                  under 2 GiB (T * D < 2^30 here) and every pointer is 16-byte
+ *                  aligned, otherwise on the (slower) row kernel.
  *
  * Work is O(B * H * T * min(W, T) * D): only key tiles that intersect a
  * query tile's band are read ("NNX Sliding-Window Attention", A local mask is

@@ -312,6 +312,24 @@ def test_full_size_prefill_sampled_rows(name):
                      f"{name} all rows of b={b} h={h}")
 
 
+@pytest.mark.parametrize("T", [(1 << 23) - 1, 1 << 23])
+def test_bf16_longest_sequences_either_side_of_the_slab_limit(T):
+    """The matrix-core kernel addresses a (b, h) slab of k and v with 32-bit
+    byte offsets: with D = 128, T = 2^23 - 1 is the longest sequence it
+    takes and T = 2^23 runs on the row kernel.  Rows at the start, the middle
+    and the very end match the oracle on either side."""
+    D, W = 128, 4096
+    g = si.generator(T % 997, DEV)
+    q, k, v = (si.normal((1, 1, T, D), g, torch.bfloat16, DEV) for _ in range(3))
+    out = run_fwd(q, k, v, W)
+    for i in (0, W - 1, T // 2 + 17, T - 2, T - 1):
+        lo = max(0, i - W + 1)
+        qs, ks, vs = (npy(x[0, :, lo:i + 1]) for x in (q, k, v))
+        ref = so.swa_rows(qs, ks, vs, W, [i - lo])
+        assert_close(out[0][:, i:i + 1], ref, torch.bfloat16, f"T={T} row {i}")
+    del q, k, v, out
+
+
 # ----------------------------------------------------------------------------
 # Decode against the ring
 # ----------------------------------------------------------------------------
