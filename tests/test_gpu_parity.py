@@ -204,6 +204,23 @@ def test_bf16_scores_growing_beyond_fp32_range(T, W, D):
     assert np.all(np.abs(npy(lse) - lref) <= 1e-2 + 1e-3 * np.abs(lref))
 
 
+@pytest.mark.parametrize("D,W,T", [(128, 128, 700), (128, 4096, 5000), (64, 96, 400)])
+def test_bf16_equal_scores_far_below_zero(D, W, T):
+    """Every score equal to about -130 in log2 units (q = -a, k = 1): the
+    weights are uniform and each row is the mean of v over its window, but
+    exponentials taken against a zero reference would land in the fp32 and
+    bf16 subnormal range.  Rows whose first keys lie in a tile that is
+    interior to every row's band must still get a reference from a row
+    max."""
+    a = 130.0 / (D ** 0.5 * 1.4426950408889634)
+    a = float(torch.tensor(a).bfloat16())
+    q = torch.full((1, 2, T, D), -a, dtype=torch.bfloat16, device=DEV)
+    k = torch.ones_like(q)
+    v = si.normal((1, 2, T, D), si.generator(T + W, DEV), torch.bfloat16, DEV)
+    out = run_fwd(q, k, v, W)
+    assert_close(out, so.swa_dense(npy(q), npy(k), npy(v), W), torch.bfloat16, f"T={T} W={W}")
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_bf16_one_huge_key_matches_oracle_and_stays_local(D):
     """One key with an enormous dot product against half of the queries:
