@@ -153,8 +153,8 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
-              "the path shards by heads, batch or streams with no communication, and this build "
-              "does not launch multi-GPU runs.", file=sys.stderr)
+              "the path shards by heads, batch or streams with no communication, and bench.py "
+              "times one GPU's share; run it with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch

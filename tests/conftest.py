@@ -23,8 +23,8 @@ def _gpu_present() -> bool:
 
 
 def pytest_collection_modifyitems(config, items):
-    # Without a GPU (this CPU container) GPU tests are skipped; on a GPU machine
-    # they run, and a missing library makes them fail, never skip.
+    # Without a visible GPU the GPU tests are skipped; with one they run, and a
+    # missing library makes them fail, never skip.
     if _gpu_present():
         return
     skip = pytest.mark.skip(reason="no GPU visible")
