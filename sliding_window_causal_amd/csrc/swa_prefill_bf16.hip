@@ -238,6 +238,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     f32x16 o[D / 32];
     float m;                          // reference max (raw score units)
     float lsum;                       // this lane's half of the row sum
+    float mref;                       // m * c, 0 while m = -inf
     // Fast pass (prefill, careful = false): the reference m only has to keep
     // the exponents in range, so once every row of the wave has one, tiles
     // inside every row's band skip the row max.  Scores that later exceed the
@@ -354,6 +355,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             // masked, where m - m would be NaN); 0 when m = -inf.
             const float alpha = __builtin_amdgcn_exp2f(raise ? (m - mx) * c : 0.f);
             m = raise ? mx : m;
+            mref = m == -__builtin_inff() ? 0.f : m * c;
             lsum *= alpha;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
@@ -365,6 +367,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
     m = -__builtin_inff();
+    mref = 0.f;
     lsum = 0.f;
     ref_set = false;
 #pragma unroll
@@ -411,8 +414,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         // path has no branches; a tile outside this wave's band gets
         // mc = +inf and hence probabilities exp2(-inf) = 0 exactly.
         {
-            const float mc = !nj ? __builtin_inff() : (m == -__builtin_inff() ? 0.f : m * c);
-            float ps = 0.f;
+            const float mc = nj ? mref : __builtin_inff();
             // The schedule is written out slice by slice; each sched_barrier
             // closes a slice, so the MFMAs at the top of a slice run on the
             // matrix core while the slice's (independent) vector ALU work
@@ -443,7 +445,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 for (int v = NPRE + dc * (NEA - NPRE) / ND; v < NPRE + (dc + 1) * (NEA - NPRE) / ND; ++v)
                     sc[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], c, -mc));
                 if (dc == ND - 1) {
-                    p0 = pack_p(sc, 0, ps);
+                    p0 = pack_p(sc, 0, lsum);
                     read_v_chunk<D>(Vc, 1, lane, va1);
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -459,14 +461,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             for (int dc = 0; dc < ND; ++dc) kn[dc] = read_row_frag<D>(kslot_n(KS + 2), lr, hh, dc);
 #pragma unroll
             for (int v = NEA; v < 16; ++v) sc[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], c, -mc));
-            p1 = pack_p(sc, 8, ps);
+            p1 = pack_p(sc, 8, lsum);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
                 o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va1[db], p1, o[db], 0, 0, 0);
             if constexpr (CHUNK) mxn = tile_max(sn);
             __builtin_amdgcn_sched_barrier(0);
-            lsum += ps;
         }
         // Edge tiles are masked; their max, and that of every tile in the
         // careful pass or before every row has a reference, updates m.
