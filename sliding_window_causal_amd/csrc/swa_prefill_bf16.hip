@@ -184,11 +184,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         wt0 = max(qw0 - W + 1, 0) / C::BN;
         wt1 = (min(qw0 + 32, T) + C::BN - 1) / C::BN;
     }
-    auto needs = [&](int t) { return t >= wt0 && t < wt1; };
-    auto interior = [&](int t) {
-        const int k0 = t * C::BN;
-        return (k0 + C::BN - 1 <= qw0) && (qw0 + 31 - k0 < W);
-    };
+    // Tile tests as one unsigned range compare each (uniform, scalar ALU).
+    auto needs = [&](int t) { return (unsigned)(t - wt0) < (unsigned)(wt1 - wt0); };
+    // Interior tiles [ia, ia + ilen): every key at or below the wave's first
+    // query and inside its last query's window, so no key is masked.
+    const int xa = qw0 + 32 - W;                     // first key in every row's window
+    const int ia = xa <= 0 ? 0 : (xa + C::BN - 1) / C::BN;
+    const int ib = qw0 >= C::BN - 1 ? (qw0 - (C::BN - 1)) / C::BN + 1 : 0;
+    const int ilen = max(ib - ia, 0);
+    auto interior = [&](int t) { return (unsigned)(t - ia) < (unsigned)ilen; };
     // a split's partial row: unnormalised output o, max m (raw units) and
     // this lane's half of the sum; the merge rescales partials to a common max
     auto write_partial = [&](const f32x16 (&o)[D / 32], float m, float lsum) {
@@ -248,6 +252,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // continuation always runs careful.
     bool careful = CHUNK;
     bool ref_set;                     // every row of the wave has a finite m
+    // Fast-pass tiles [f_lo, f_lo + f_len): the interior tiles once ref_set
+    // holds; empty before that and in the careful pass.
+    int f_lo, f_len;
     // Cleared before the prologue's tile loads (asm with memory clobbers
     // keep the store ahead of them) and so before its first barrier.
     if (tid == 0) rerun = 0;
@@ -256,9 +263,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     // ---- prologue.  Tile loads are issued in the order K(t0) V(t0) K(t0+1)
     // V(t0+1) ... K(t0+PF-1) V(t0+PF-1) K(t0+PF), and then, in step j,
-    // V(j+PF) K(j+1+PF); tile indices past the band are clamped to its last
-    // tile (loaded into a free slot, never read), so every step issues the
-    // same number of loads and a fixed vmcnt waits for exactly the oldest.
+    // V(j+PF) K(j+1+PF).  Tiles past the band are loaded too (into a free
+    // slot, never read; zeros past the slab), so every step issues the same
+    // number of loads and a fixed vmcnt waits for exactly the oldest.
     // Ring slot s of K and of V (tile t lives in slot (t - t0) mod R).  Slot
     // numbers are compile-time constants at every call site, so the LDS
     // reads carry the slot in their immediate offset.
@@ -268,7 +275,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     tile_offsets<D, NW, kSwzK>(koff, wave, lane, 2 * krs);
     tile_offsets<D, NW, kSwzV>(voff, wave, lane, 2 * vrs);
     // bytes per key tile and per slab (the last row ends after D elements)
-    const int ktb = C::BN * 2 * krs, vtb = C::BN * 2 * vrs;
+    // (capped: a tile step at or past the slab end only has to empty it)
+    const int ktb = (int)min((int64_t)C::BN * 2 * krs, (int64_t)INT32_MAX);
+    const int vtb = (int)min((int64_t)C::BN * 2 * vrs, (int64_t)INT32_MAX);
     const int kslab = ((nrow - 1) * krs + D) * 2, vslab = ((nrow - 1) * vrs + D) * 2;
     // Chunk continuation: the ring slot of relative position x (x < 3 W
     // whenever W >= 64, which the two subtractions cover).
@@ -314,20 +323,33 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             lds_load16_global(lds + (wave * C::NLD_W + i) * 1024, src + logical * 8);
         }
     };
+    // Prefill: the next K and V tiles to load, as an address and the slab
+    // bytes left from there (0 past the slab end: such loads read nothing
+    // and write zeros).  Tiles are loaded in order, so each load just
+    // advances these by one tile.
+    const char* kp = nullptr;
+    const char* vp = nullptr;
+    int kr = 0, vr = 0;
     // tile t into ring slot s (s = t - t0 modulo the ring)
     auto load_k = [&](int t, int s) {
-        if constexpr (CHUNK)
+        if constexpr (CHUNK) {
             load_chunk_tile(t, Kbh, Krh, ktb, kslab, koff, lds_addr(kslot_n(s)), false);
-        else
-            dma_tile(rows_rsrc(Kbh, min(t, t1 - 1) * ktb, kslab), lds_addr(kslot_n(s)), wave,
-                            koff);
+        } else {
+            dma_tile(rows_rsrc(reinterpret_cast<const bf16*>(kp), 0, kr), lds_addr(kslot_n(s)),
+                     wave, koff);
+            kp += ktb;
+            kr = max(kr - ktb, 0);
+        }
     };
     auto load_v = [&](int t, int s) {
-        if constexpr (CHUNK)
+        if constexpr (CHUNK) {
             load_chunk_tile(t, Vbh, Vrh, vtb, vslab, voff, lds_addr(vslot_n(s)), true);
-        else
-            dma_tile(rows_rsrc(Vbh, min(t, t1 - 1) * vtb, vslab), lds_addr(vslot_n(s)), wave,
-                            voff);
+        } else {
+            dma_tile(rows_rsrc(reinterpret_cast<const bf16*>(vp), 0, vr), lds_addr(vslot_n(s)),
+                     wave, voff);
+            vp += vtb;
+            vr = max(vr - vtb, 0);
+        }
     };
     // Publish loads: wait until at most VM_WAIT of this wave's loads are in
     // flight and its LDS reads are done, then barrier.  No fence is needed:
@@ -370,6 +392,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     mref = 0.f;
     lsum = 0.f;
     ref_set = false;
+    f_lo = 0;
+    f_len = 0;
+    if constexpr (!CHUNK) {
+        // t0 * 32 < T, so the first tile starts inside both slabs
+        kp = reinterpret_cast<const char*>(Kbh) + (int64_t)t0 * ktb;
+        vp = reinterpret_cast<const char*>(Vbh) + (int64_t)t0 * vtb;
+        kr = (int)(kslab - (int64_t)t0 * ktb);
+        vr = (int)(vslab - (int64_t)t0 * vtb);
+    }
 #pragma unroll
     for (int i = 0; i < C::PF; ++i) {
         load_k(t0 + i, i);
@@ -385,6 +416,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         qk_tile<D>(kslot_n(0), qf, lr, hh, ksw, sA);
         if (!interior(t0)) mask_tile(sA, qi, t0 * C::BN, hh, W);
         raise_ref(tile_max(sA));
+        if (!careful && ref_set) {
+            f_lo = ia;
+            f_len = ilen;
+        }
     }
     // K operands of the next score tile live in registers one step ahead:
     // step j computes S(j+1) from kf of K(j+1) and reads K(j+2) into the
@@ -471,17 +506,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         }
         // Edge tiles are masked; their max, and that of every tile in the
         // careful pass or before every row has a reference, updates m.
-        if (nn) {
-            const bool edge = !interior(j + 1);
-            if constexpr (CHUNK) {
-                if (edge) {
+        if constexpr (CHUNK) {
+            if (nn) {
+                if (!interior(j + 1)) {
                     mask_tile(sn, qi, (j + 1) * C::BN, hh, W);
                     mxn = tile_max(sn);
                 }
                 raise_ref(mxn);
-            } else if (edge || careful || !ref_set) {
-                if (edge) mask_tile(sn, qi, (j + 1) * C::BN, hh, W);
-                raise_ref(tile_max(sn));
+            }
+        } else if ((unsigned)(j + 1 - f_lo) >= (unsigned)f_len && nn) {
+            if (!interior(j + 1)) mask_tile(sn, qi, (j + 1) * C::BN, hh, W);
+            raise_ref(tile_max(sn));
+            if (!careful && ref_set) {
+                f_lo = ia;
+                f_len = ilen;
             }
         }
         publish();   // V(j+2) and K(j+3) have landed
