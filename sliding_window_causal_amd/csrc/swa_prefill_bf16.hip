@@ -263,9 +263,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     // ---- prologue.  Tile loads are issued in the order K(t0) V(t0) K(t0+1)
     // V(t0+1) ... K(t0+PF-1) V(t0+PF-1) K(t0+PF), and then, in step j,
-    // V(j+PF) K(j+1+PF).  Tiles past the band are loaded too (into a free
-    // slot, never read; zeros past the slab), so every step issues the same
-    // number of loads and a fixed vmcnt waits for exactly the oldest.
+    // V(j+PF) K(j+1+PF).  Tiles past the band are issued too (as zeros,
+    // into a free slot, never read), so every step issues the same number
+    // of loads and a fixed vmcnt waits for exactly the oldest.
     // Ring slot s of K and of V (tile t lives in slot (t - t0) mod R).  Slot
     // numbers are compile-time constants at every call site, so the LDS
     // reads carry the slot in their immediate offset.
@@ -323,10 +323,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             lds_load16_global(lds + (wave * C::NLD_W + i) * 1024, src + logical * 8);
         }
     };
-    // Prefill: the next K and V tiles to load, as an address and the slab
-    // bytes left from there (0 past the slab end: such loads read nothing
-    // and write zeros).  Tiles are loaded in order, so each load just
-    // advances these by one tile.
+    // Prefill: the next K and V tiles to load, as an address and the bytes
+    // left from there to the end of the band's last tile (0 past it: such
+    // loads read nothing and write zeros).  Tiles are loaded in order, so
+    // each load just advances these by one tile.
     const char* kp = nullptr;
     const char* vp = nullptr;
     int kr = 0, vr = 0;
@@ -395,11 +395,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     f_lo = 0;
     f_len = 0;
     if constexpr (!CHUNK) {
-        // t0 * 32 < T, so the first tile starts inside both slabs
+        // t0 * 32 < T, so the first tile starts inside both slabs.  The
+        // range ends with the band: tiles past it are zeros, not reads.
         kp = reinterpret_cast<const char*>(Kbh) + (int64_t)t0 * ktb;
         vp = reinterpret_cast<const char*>(Vbh) + (int64_t)t0 * vtb;
-        kr = (int)(kslab - (int64_t)t0 * ktb);
-        vr = (int)(vslab - (int64_t)t0 * vtb);
+        kr = (int)(min((int64_t)kslab, (int64_t)t1 * ktb) - (int64_t)t0 * ktb);
+        vr = (int)(min((int64_t)vslab, (int64_t)t1 * vtb) - (int64_t)t0 * vtb);
     }
 #pragma unroll
     for (int i = 0; i < C::PF; ++i) {
