@@ -230,13 +230,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
         for (int dc = 0; dc < D / 16; ++dc) qf[dc] = *reinterpret_cast<const bf16x8*>(qp + 16 * dc);
     }
-    if (a.qneg) {
-#pragma unroll
-        for (int dc = 0; dc < D / 16; ++dc) qf[dc] = -qf[dc];
-    }
-    // Land Q before any tile load is issued: the compiler's own waits for
-    // these registers would otherwise count (and drain) the tile loads.
-    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
+    // Q is not waited for here: the prologue's tile loads are issued behind
+    // it and one wait covers both, so they share one memory round trip.  A
+    // negative scale flips q after that wait.
+    bool negate_q = a.qneg != 0;
     const int ksw = kswz<D>(lr);
 
     f32x16 o[D / 32];
@@ -408,7 +405,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         load_v(t0 + i, i);
     }
     load_k(t0 + C::PF, C::PF);
-    publish();   // K(t0), V(t0), K(t0+1), V(t0+1), K(t0+2) have landed
+    // Every load so far has landed (Q and all of the prologue's tiles): a
+    // full wait, which also tells the compiler that Q is in registers on
+    // every path, so it adds no waits of its own inside the key loop.
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+    if (negate_q) {
+#pragma unroll
+        for (int dc = 0; dc < D / 16; ++dc) qf[dc] = -qf[dc];
+        negate_q = false;
+    }
 
     // Score tiles start finite: a wave computes (and discards) tiles outside
     // its band, and their probabilities must come out as exact zeros.
@@ -577,15 +583,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         a.lse[(int64_t)bh * T + qi] = (m * c + __builtin_amdgcn_logf(l)) * kLn2;
     if (qi < T) {
         bf16* orow = a.out + b * a.L.o.b + h * a.L.o.h + (int64_t)(qi - p0r) * a.L.o.t;
+        // All packs first, each in registers of its own, then the stores:
+        // a store's data registers are not rewritten while it is queued.
+        bf16x4 w[D / 32][4];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                bf16x4 w;
+            for (int g = 0; g < 4; ++g)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = (bf16)(o[db][4 * g + e] * inv);
-                *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g + 4 * hh) = w;
-            }
+                for (int e = 0; e < 4; ++e) w[db][g][e] = (bf16)(o[db][4 * g + e] * inv);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g + 4 * hh) = w[db][g];
     }
 }
 
