@@ -183,6 +183,22 @@ def _ramp_qkv(T, D, slope, seed):
 
 
 @pytest.mark.parametrize("D", [64, 128])
+def test_bf16_negative_scale_with_scores_growing_beyond_fp32_range(D):
+    """A negative scale is applied as -q times |scale|; q is flipped once,
+    after the prologue's wait.  Keys ramping the other way make the scaled
+    scores climb hundreds of log2 units within a window, so workgroups redo
+    their rows in the careful pass, which must not flip q again."""
+    T, W = 1024, 512
+    q, k, v = _ramp_qkv(T, D, -1.0, seed=77 + D)
+    scale = -1.0 / D ** 0.5
+    s = (q.float()[0, 0, 0] @ k.float()[0, 0].T) * scale
+    assert (s[W - 1] - s[0]).item() * 1.4427 > 200        # the growth is really there
+    out = swa.sliding_window_attention(q, k, v, W, scale=scale)
+    ref = so.swa_dense(npy(q), npy(k), npy(v), W, scale=scale)
+    assert_close(out, ref, torch.bfloat16, f"D={D} scale {scale}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("T,W", [(1024, 1024), (2048, 256), (700, 100)])
 def test_bf16_scores_growing_beyond_fp32_range(T, W, D):
     """Within a window the scores rise by hundreds of log2 units above those
