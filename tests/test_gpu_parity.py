@@ -162,6 +162,23 @@ def test_bf16_prefill_vs_dense_oracle(T, W, D):
     assert_close(out, ref, torch.bfloat16, f"T={T} W={W} D={D}")
 
 
+def test_bf16_tile_boundary_sweep():
+    """Sequence lengths on either side of the 128-query workgroup tile and
+    windows on either side of the 32-key tile (and of W = 64, where an edge
+    tile becomes one-sided): the kernel's band, interior and fast-pass tile
+    ranges and the end of its tile loads all move by one here."""
+    bad = []
+    for T in (127, 128, 129, 255, 256, 257):
+        for W in (31, 32, 33, 63, 64, 65, 95, 96, 97, 128, 129):
+            q, k, v = si.prefill_qkv(1, 2, T, 64, dtype=torch.bfloat16, seed=7 * T + W, device=DEV)
+            out = npy(run_fwd(q, k, v, W)).astype(np.float64)
+            ref = so.swa_dense(npy(q), npy(k), npy(v), W)
+            over = np.abs(out - ref) - (BF_ATOL + BF_RTOL * np.abs(ref))
+            if not (np.isfinite(out).all() and (over <= 0).all()):
+                bad.append((T, W, float(np.nanmax(over))))
+    assert not bad, bad
+
+
 def test_bf16_scaled_inputs_stay_within_tolerance():
     """Larger logits (q, k ~ N(0, 3^2)) exercise the running-max rescale."""
     q, k, v = si.prefill_qkv(1, 4, 600, 128, dtype=torch.float32, seed=12, device=DEV)
