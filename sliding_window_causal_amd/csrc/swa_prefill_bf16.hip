@@ -260,9 +260,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     // ---- prologue.  Tile loads are issued in the order K(t0) V(t0) K(t0+1)
     // V(t0+1) ... K(t0+PF-1) V(t0+PF-1) K(t0+PF), and then, in step j,
-    // V(j+PF) K(j+1+PF).  Tiles past the band are issued too (as zeros,
-    // into a free slot, never read), so every step issues the same number
-    // of loads and a fixed vmcnt waits for exactly the oldest.
+    // V(j+PF) K(j+1+PF).  Tiles past the band are issued too (into a free
+    // slot, never read: zeros in the prefill, the band's last tile again in
+    // the chunk continuation), so every step issues the same number of
+    // loads and a fixed vmcnt waits for exactly the oldest.
     // Ring slot s of K and of V (tile t lives in slot (t - t0) mod R).  Slot
     // numbers are compile-time constants at every call site, so the LDS
     // reads carry the slot in their immediate offset.
