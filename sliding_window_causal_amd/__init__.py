@@ -29,6 +29,9 @@ Entry points (same names as the C ABI):
                                                  module forward with projections
 Conveniences that allocate the output with torch:
   sliding_window_attention(q, k, v, window_size, scale=None, layout=None) -> out
+                                                 differentiable: with an input that
+                                                 requires grad, the forward keeps its row
+                                                 log-sum-exp and backward calls swa_backward
   decode(q, kring, vring, pos, split=False) -> out
   decode_append(q, knew, vnew, kring, vring, pos) -> out
   chunk_attention(q, kc, vc, kring, vring, pos0, split=False) -> out
@@ -488,6 +491,29 @@ class SlidingWindowMHA:
 _LAYOUTS = ("bhtd", "bshd", "btd")
 
 
+class _SlidingWindowAttention(torch.autograd.Function):
+    """swa_forward_lse forward, swa_backward backward, on contiguous
+    [B, H, T, D] tensors; the row log-sum-exp saved by the forward spares the
+    backward its own forward pass."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, window_size, scale):
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+        swa_forward_lse(q, k, v, out, lse, window_size, scale=scale)
+        ctx.save_for_backward(q, k, v, out, lse)
+        ctx.window_size, ctx.scale = window_size, scale
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse = ctx.saved_tensors
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        swa_backward(q, k, v, out, dout.contiguous(), dq, dk, dv, ctx.window_size,
+                     scale=ctx.scale, lse=lse)
+        return dq, dk, dv, None, None
+
+
 def sliding_window_attention(q, k, v, window_size: int, scale=None, layout: str = None):
     """Prefill returning a new tensor in the layout of ``q``.
 
@@ -496,6 +522,12 @@ def sliding_window_attention(q, k, v, window_size: int, scale=None, layout: str 
     the scores (None: 1/sqrt(D)).  Contiguous [B, H, T, D] inputs with the
     default scale go through swa_forward; everything else through
     swa_forward_strided, reading the tensors in place.
+
+    When autograd is on and q, k or v requires grad, the result is
+    differentiable: the inputs are brought to contiguous [B, H, T, D] (views,
+    or copies where the layout needs them), the forward runs swa_forward_lse
+    and the backward swa_backward with that log-sum-exp; the result is then a
+    view in the layout of ``q``.
     """
     if layout is None:
         layout = "btd" if q.dim() == 3 else "bhtd"
@@ -503,6 +535,15 @@ def sliding_window_attention(q, k, v, window_size: int, scale=None, layout: str 
         raise ValueError(f"layout must be one of {_LAYOUTS}")
     if q.dim() != (3 if layout == "btd" else 4):
         raise ValueError(f"layout {layout!r} needs {3 if layout == 'btd' else 4}-D tensors")
+    if torch.is_grad_enabled() and any(t.requires_grad for t in (q, k, v)):
+        if layout == "btd":
+            to4, back = (lambda t: t.unsqueeze(1)), (lambda t: t.squeeze(1))
+        elif layout == "bshd":
+            to4, back = (lambda t: t.transpose(1, 2)), (lambda t: t.transpose(1, 2))
+        else:
+            to4, back = (lambda t: t), (lambda t: t)
+        qb, kb, vb = (to4(t).contiguous() for t in (q, k, v))
+        return back(_SlidingWindowAttention.apply(qb, kb, vb, window_size, scale))
     out = torch.empty_like(q)
     if layout == "btd":
         views = [t.unsqueeze(1) for t in (q, k, v, out)]
