@@ -225,31 +225,54 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a) {
 
 // Merge the P partials of each (stream, head): with M the largest partial
 // max, o = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.  Empty splits
-// (m_p = -inf) get weight 0; a stream with no occupied slot gets 0.
+// (m_p = -inf) get weight 0; a stream with no occupied slot gets 0.  One
+// wavefront per row: lane p holds split p's (max, sum) (P <= 64), M and the
+// weighted sum come from wave reductions, and the output loop takes each
+// split's weight from its lane and keeps eight splits' loads in flight.
 template <int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ ws_o,
                                                             const float* __restrict__ ws_ml,
                                                             bf16* __restrict__ out, int P) {
+    constexpr int R = D / 64;
     const int64_t sh = blockIdx.x;
+    const int lane = threadIdx.x;
     const float* ml = ws_ml + 2 * sh * P;
-    float M = -__builtin_inff();
-    for (int p = 0; p < P; ++p) M = fmaxf(M, ml[2 * p]);
-    float L = 0.f;
-    float o[D / 64];
+    float mp = -__builtin_inff(), lp = 0.f;
+    if (lane < P) {
+        mp = ml[2 * lane];
+        lp = ml[2 * lane + 1];
+    }
+    float M = mp;
 #pragma unroll
-    for (int r = 0; r < D / 64; ++r) o[r] = 0.f;
-    for (int p = 0; p < P; ++p) {
-        const float m = ml[2 * p];
-        if (m == -__builtin_inff()) continue;
-        const float w = __builtin_amdgcn_exp2f(m - M);
-        L = fmaf(w, ml[2 * p + 1], L);
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float wp = mp == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mp - M);
+    float L = wp * lp;
 #pragma unroll
-        for (int r = 0; r < D / 64; ++r)
-            o[r] = fmaf(w, ws_o[(sh * P + p) * D + threadIdx.x + 64 * r], o[r]);
+    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    float o[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) o[r] = 0.f;
+    const float* po = ws_o + sh * P * D + lane;
+    for (int p = 0; p < P; p += 8) {
+        float y[8][R];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int r = 0; r < R; ++r) y[u][r] = p + u < P ? po[(int64_t)(p + u) * D + 64 * r] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            // weight of split p + u: 0 for an empty split, whose row is never used
+            const float w = p + u < P
+                ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wp), p + u)) : 0.f;
+            if (w != 0.f) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) o[r] = fmaf(w, y[u][r], o[r]);
+            }
+        }
     }
 #pragma unroll
-    for (int r = 0; r < D / 64; ++r)
-        out[sh * D + threadIdx.x + 64 * r] = (bf16)(L > 0.f ? o[r] / L : 0.f);
+    for (int r = 0; r < R; ++r)
+        out[sh * D + lane + 64 * r] = (bf16)(L > 0.f ? o[r] / L : 0.f);
 }
 
 template <int D>
@@ -350,8 +373,11 @@ hipError_t launch_ring_append_chunk(const void* kc, const void* vc, void* kring,
                            stream);
 }
 
+static_assert(kDecMaxSplits <= 64 && kChunkMaxSplits <= 64, "one combine lane per split");
+
 hipError_t launch_combine_bf16(const float* ws_o, const float* ws_ml, bf16* out, int64_t rows,
                                int P, int D, hipStream_t stream) {
+    if (P < 1 || P > 64) return hipErrorInvalidValue;
     void* cargs[] = {(void*)&ws_o, (void*)&ws_ml, (void*)&out, (void*)&P};
     const void* k = D == 128 ? (const void*)decode_combine_kernel<128>
                              : (const void*)decode_combine_kernel<64>;
