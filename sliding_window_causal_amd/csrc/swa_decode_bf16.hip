@@ -386,9 +386,10 @@ hipError_t launch_combine_bf16(const float* ws_o, const float* ws_ml, bf16* out,
 
 int decode_splits(int64_t S, int64_t H, int64_t W) {
     // Splitting pays while S * H workgroups leave most compute units idle
-    // (measured at D = 128, W = 4096: 2.3x at S * H = 32, 1.7x at 64, none
-    // from 128 on).  Aim for kDecSplitTargetWGs workgroups with at least
-    // kDecSplitMinSlots slots each (smaller splits measured slower).
+    // (measured at D = 128, W = 4096: 2.9x at S * H = 32, 1.8x at 64, 1.14x
+    // at 128, 1.01x at 256, none from 512 on).  Aim for kDecSplitTargetWGs
+    // workgroups with at least kDecSplitMinSlots slots each (smaller splits
+    // measured slower, and so did a target of 4096 at S * H = 256 and 512).
     const int64_t sh = S * H;
     if (sh >= kDecSplitTargetWGs / 4) return 1;
     int64_t p = (kDecSplitTargetWGs + sh - 1) / sh;

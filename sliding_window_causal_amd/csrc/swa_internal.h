@@ -100,7 +100,7 @@ hipError_t launch_chunk_bf16(const bf16* q, const bf16* kc, const bf16* vc, cons
                              int64_t H, int64_t C, int D, int64_t W, void* workspace,
                              hipStream_t stream);
 // Merge P partial rows (ws_o [rows * P, D], ws_ml [rows * P, 2]: max in log2
-// units, sum) into out [rows, D]; D in {64, 128}.
+// units, sum) into out [rows, D]; D in {64, 128}, 1 <= P <= 64.
 hipError_t launch_combine_bf16(const float* ws_o, const float* ws_ml, bf16* out, int64_t rows,
                                int P, int D, hipStream_t stream);
 
@@ -110,7 +110,7 @@ hipError_t launch_combine_bf16(const float* ws_o, const float* ws_ml, bf16* out,
 // kernel; with knew / vnew the current token's k, v are read from there and
 // written into slot pos mod W by the same launch.
 constexpr int64_t kDecodeMaxW = 16384;
-constexpr int64_t kDecSplitTargetWGs = 512;
+constexpr int64_t kDecSplitTargetWGs = 2048;
 constexpr int64_t kDecSplitMinSlots = 256;
 constexpr int64_t kDecMaxSplits = 64;
 int decode_splits(int64_t S, int64_t H, int64_t W);
