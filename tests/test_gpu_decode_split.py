@@ -156,6 +156,27 @@ def test_fused_negative_position():
     assert torch.equal(kr[1, :, 5], kn[1])
 
 
+@pytest.mark.parametrize("pos", [16383 + 5000, 9000])
+def test_sixty_four_way_split_merge(pos):
+    """One head against a 16384-slot ring takes the most splits, 64: the
+    merge's lanes cover them all, in eight batches of partial rows.  Also a
+    ring only partly filled (position 9000), where the last splits are empty
+    (their max is -inf) and must not contribute."""
+    S, H, D, W = 1, 1, 128, 16384
+    assert swa.swa_decode_workspace_bytes(S, H, D, W, torch.bfloat16) == 64 * (D + 2) * 4
+    q, k, v = _case(S, H, D, W, [pos], torch.bfloat16, seed=pos)
+    kr, vr = _rings(k, v, [pos], W, torch.bfloat16)
+    qs = q[:, :, pos].contiguous()
+    p = torch.tensor([pos], dtype=torch.int64, device=DEV)
+    out = swa.decode(qs, kr, vr, p, split=True)
+    whole = swa.decode(qs, kr, vr, p)
+    torch.cuda.synchronize()
+    ek, ev = so.ring_fill(npy(k), npy(v), [pos], W)
+    ref = so.swa_decode(npy(qs), ek, ev, [pos], W)
+    assert_close(out, ref, torch.bfloat16, f"64-way split, pos {pos}")
+    assert_close(whole, ref, torch.bfloat16, f"one workgroup, pos {pos}")
+
+
 def test_full_size_single_stream_split():
     """One stream, 32 heads, D = 128, a full 4096-slot ring at a wrapped head."""
     S, H, D, W = 1, 32, 128, 4096
