@@ -23,15 +23,35 @@ constexpr int kMaxDevices = 64;
 
 // One rocBLAS handle per device, created on first use and kept until the
 // process ends (the library's only state besides cached device properties).
-rocblas_handle device_handle() {
-    static std::mutex mu;
+// A handle carries the stream its calls go to, so a caller holds the
+// device's lock (taken here) from setting the stream until its last rocBLAS
+// call has been issued: module calls on other host threads and streams then
+// cannot redirect its products.  Launches are asynchronous, so the lock is
+// held only for the time it takes to issue them.
+struct LockedHandle {
+    std::unique_lock<std::mutex> lock;
+    rocblas_handle h = nullptr;
+};
+
+LockedHandle device_handle() {
+    static std::mutex create_mu;
+    static std::mutex use_mu[kMaxDevices];
     static rocblas_handle handles[kMaxDevices] = {};
+    LockedHandle r;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-    std::lock_guard<std::mutex> lock(mu);
-    if (!handles[dev] && rocblas_create_handle(&handles[dev]) != rocblas_status_success)
-        handles[dev] = nullptr;
-    return handles[dev];
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return r;
+    rocblas_handle h = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(create_mu);
+        if (!handles[dev] && rocblas_create_handle(&handles[dev]) != rocblas_status_success)
+            handles[dev] = nullptr;
+        h = handles[dev];
+    }
+    if (h) {
+        r.lock = std::unique_lock<std::mutex>(use_mu[dev]);
+        r.h = h;
+    }
+    return r;
 }
 
 // C[r, c] = bias[c] (0 without a bias) for r < rows, c < cols; row stride ldc.
@@ -106,7 +126,8 @@ int swa_mha_forward(const void* x, const void* wq, const void* bq, const void* w
     if (workspace_bytes < need || ((uintptr_t)workspace & 15) != 0) return SWA_ERR_INVALID_ARG;
 
     hipStream_t st = (hipStream_t)stream;
-    rocblas_handle h = device_handle();
+    LockedHandle lh = device_handle();   // held until this call returns
+    rocblas_handle h = lh.h;
     if (!h || rocblas_set_stream(h, st) != rocblas_status_success) return SWA_ERR_LAUNCH;
     const int64_t eb = elem_bytes(dtype);
     char* qkv = (char*)workspace;                       // [rows, 3 d_model]

@@ -111,3 +111,47 @@ def test_module_corruption_outside_window_is_bitwise_invisible():
     assert torch.equal(out[0, :j0], base[0, :j0])
     assert torch.equal(out[0, j0 + W:], base[0, j0 + W:])
     assert not torch.equal(out[0, j0:j0 + W], base[0, j0:j0 + W])
+
+
+def test_module_calls_from_two_threads_on_two_streams():
+    """Two host threads run the module at the same time, each on a stream of
+    its own (ctypes releases the GIL during the call): every result equals
+    the same call made alone.  The library's rocBLAS handle carries a stream,
+    so each call holds it from setting the stream to its last product."""
+    import threading
+    B, T, dm, H, W, N = 1, 1024, 1024, 8, 256, 20
+    g = si.generator(130, DEV)
+    xs = [si.normal((B, T, dm), g, torch.bfloat16, DEV) for _ in range(2)]
+    (wq, wk, wv, wo), (bq, bk, bv, bo) = _weights(dm, torch.bfloat16, g)
+    refs = []
+    for x in xs:
+        o = torch.empty_like(x)
+        swa.swa_mha_forward(x, wq, bq, wk, bk, wv, bv, wo, bo, o, H, W)
+        refs.append(o)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(2)]
+    outs = [[], []]
+    errors = []
+
+    def worker(i):
+        try:
+            with torch.cuda.stream(streams[i]):
+                for _ in range(N):
+                    o = torch.empty_like(xs[i])
+                    swa.swa_mha_forward(xs[i], wq, bq, wk, bk, wv, bv, wo, bo, o, H, W)
+                    outs[i].append(o)
+        except Exception as e:          # reported below, on the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        assert len(outs[i]) == N
+        for n, o in enumerate(outs[i]):
+            assert torch.equal(o, refs[i]), f"thread {i}, call {n}"
+
