@@ -59,6 +59,7 @@ struct BArgs {
     const float* lse;     // [B * H * T] log-sum-exp of the scaled scores (forward)
     float* delta;         // [B * H * T] dout . out (written by DQ)
     int T, W, nrt, nblocks, remap;
+    int nfull;            // longest-first dispatch (xcd_logical_tile); -1: plain order
     float c;              // log2(e) * scale
     float scale;
 };
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int lr = lane & 31, hh = lane >> 5;
 
     const int bid = blockIdx.x;
-    const int logical = a.remap ? (bid & 7) * (a.nblocks >> 3) + (bid >> 3) : bid;
+    const int logical = xcd_logical_tile(bid, a.nblocks, a.remap, a.nrt, a.nfull);
     const int bh = logical / a.nrt;
     const int rti = logical - bh * a.nrt;
     // longest bands first: the last query tiles (DQ), the first key tiles (DV, DK)
@@ -299,6 +300,9 @@ hipError_t launch_mode(BArgs a, int64_t B, int64_t H, hipStream_t st) {
     const int64_t nblocks = B * H * a.nrt;
     a.nblocks = (int)nblocks;
     a.remap = nblocks % 8 == 0 ? 1 : 0;
+    // row tiles within W - 1 of the sequence's far end (DQ: its start; DV, DK:
+    // its end) have shorter bands
+    a.nfull = xcd_longest_first_nfull(nblocks, a.nrt, (a.W - 1 + C::BM - 1) / C::BM);
     void* args[] = {(void*)&a};
     return hipLaunchKernel((const void*)bwd_bf16_kernel<D, MODE>, dim3((unsigned)nblocks),
                            dim3(256), args, 0, st);

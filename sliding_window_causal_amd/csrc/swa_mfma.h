@@ -108,6 +108,44 @@ __device__ inline void dma_tile(__amdgpu_buffer_rsrc_t rsrc, uint32_t buf, int w
     for (int i = 0; i < N; ++i) lds_load16(rsrc, buf + (wave * N + i) * 1024, voff[i]);
 }
 
+// Dispatch order of a grid of nblocks workgroups, nper per (b, h) slab, rank
+// r of a slab's workgroups having the r-th longest band (ranks below nfull
+// full length, later ranks ever shorter).  The hardware deals workgroups
+// round-robin over the 8 XCDs and each XCD dispatches its share in order;
+// with remap, an XCD's share is consecutive logical tiles (logical tile
+// bh * nper + r), so a slab's keys stay in one XCD's L2.  With nfull >= 0
+// (each share is whole slabs) the share goes out longest first: the
+// full-length ranks slab by slab, then the shorter ranks rank by rank across
+// the share's slabs, so the last workgroups of an XCD are its shortest.
+__device__ inline int xcd_logical_tile(int bid, int nblocks, int remap, int nper, int nfull) {
+    if (!remap) return bid;
+    const int per = nblocks >> 3;               // workgroups per XCD
+    const int p = bid >> 3;                     // dispatch position on the XCD
+    if (nfull < 0) return (bid & 7) * per + p;
+    const int G = per / nper;                   // slabs per XCD
+    int slab, rank;
+    if (p < G * nfull) {
+        slab = p / nfull;
+        rank = p - slab * nfull;
+    } else {
+        const int pr = p - G * nfull;
+        rank = nfull + pr / G;
+        slab = pr - (rank - nfull) * G;
+    }
+    return (bid & 7) * per + slab * nper + rank;
+}
+
+// nfull for xcd_logical_tile on the host: nshort of a slab's nper ranks have
+// shorter bands; -1 (plain order) unless every XCD's share is whole slabs and
+// at most 8 of them.  Longest-first pays where an XCD holds few slabs (a late
+// slab's full-length workgroups otherwise overrun the others at the end of
+// the grid); with many, the tail is short already and the short workgroups of
+// many slabs at once reuse L2 less.
+inline int xcd_longest_first_nfull(int64_t nblocks, int64_t nper, int64_t nshort) {
+    if (nblocks % 8 != 0 || (nblocks / 8) % nper != 0 || (nblocks / 8) / nper > 8) return -1;
+    return (int)(nper - (nshort < nper ? nshort : nper));
+}
+
 // Band mask of a tile starting at key k0: key j is visible to query qi iff
 // 0 <= qi - j < W (one unsigned compare).
 __device__ inline void mask_tile(f32x16& s, int qi, int k0, int hh, int W) {

@@ -40,7 +40,6 @@
 
 #include "swa_mfma.h"
 
-#include <algorithm>
 #include <type_traits>
 
 namespace swa {
@@ -78,9 +77,7 @@ struct Args {
     int nqt;        // query tiles per (b, h)
     int nblocks;    // grid size
     int remap;      // 1: spread consecutive logical tiles over one XCD
-    int nfull;      // >= 0: each XCD's share is whole (b, h) slabs, dispatched
-                    // longest band first (query tiles of a head past the first
-                    // nfull ranks have shorter bands); -1: plain order
+    int nfull;      // longest-first dispatch (xcd_logical_tile); -1: plain order
     float c;        // log2(e) * |scale| (scale defaults to 1 / sqrt(D))
     int qneg;       // 1: scale < 0, applied as -q (exact) times |scale|
     // chunk continuation only: q, k, v, out are the chunk [S, H, C, D]
@@ -138,33 +135,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int lane = tid & 63;
     const int lr = lane & 31, hh = lane >> 5;
 
-    // Logical tile: consecutive logical tiles land on one XCD (the hardware
-    // deals workgroups round-robin over 8 XCDs and each XCD dispatches its
-    // share in order).  Logical tile bh * nqt + r is rank r of head bh, rank 0
-    // being the last query tile (ranks below nfull have full-length bands,
-    // later ranks ever shorter ones near the sequence start).  When an XCD's
-    // share is whole heads it goes out longest first: the full-band ranks
-    // head by head (one head's keys at a time in L2), then the shorter ranks
-    // rank by rank across its heads, so the last workgroups are the shortest
-    // and no CU waits long for a late full-length one.
+    // Logical tile bh * nqt + r is rank r of head bh; rank 0 is the last
+    // query tile, and ranks past the full-band ones (the query tiles near the
+    // sequence start) have ever shorter bands.  xcd_logical_tile spreads the
+    // logical tiles over the XCDs, longest first where that pays.
     const int bid = blockIdx.x;
-    int logical = a.remap ? (bid & 7) * (a.nblocks >> 3) + (bid >> 3) : bid;
-    if (!CHUNK && a.remap && a.nfull >= 0) {
-        const int per = a.nblocks >> 3;              // workgroups per XCD
-        const int p = bid >> 3;                      // dispatch position on the XCD
-        const int G = per / a.nqt;                   // heads per XCD
-        const int nf = a.nfull;
-        int head, rank;
-        if (p < G * nf) {
-            head = p / nf;
-            rank = p - head * nf;
-        } else {
-            const int pr = p - G * nf;
-            rank = nf + pr / G;
-            head = pr - (rank - nf) * G;
-        }
-        logical = (bid & 7) * per + head * a.nqt + rank;
-    }
+    int logical = xcd_logical_tile(bid, a.nblocks, a.remap, CHUNK ? a.nqt * a.nsplit : a.nqt,
+                                   CHUNK ? -1 : a.nfull);
     int sp = 0;                                      // key-range split (chunk continuation)
     if constexpr (CHUNK) {
         sp = logical % a.nsplit;
@@ -636,15 +613,10 @@ hipError_t launch(Args a, int64_t B, int64_t H, int64_t rows, hipStream_t stream
     const int64_t nblocks = B * H * a.nqt * (CHUNK ? a.nsplit : 1);
     a.nblocks = (int)nblocks;
     a.remap = (nblocks % 8 == 0) ? 1 : 0;
-    // ranks 0 .. nfull-1 of a head have full-length bands: query tiles that
-    // start at or past row W - 1 (W = min(W, T) here).  Longest-first pays
-    // where an XCD holds few heads (measured: 4.2% faster at 4 heads per XCD,
-    // where a late head's full-length tiles otherwise overran the others;
-    // 1.5% slower at 32, where the tail was already short and the short
-    // tiles of many heads at once reuse L2 less).
-    const int nshort = (int)std::min<int64_t>(a.nqt, (a.W - 1 + C::BM - 1) / C::BM);
-    const bool whole_heads = a.remap && (nblocks / 8) % a.nqt == 0;
-    a.nfull = (!CHUNK && whole_heads && (nblocks / 8) / a.nqt <= 8) ? a.nqt - nshort : -1;
+    // the query tiles that start before row W - 1 (W = min(W, T) here) have
+    // shorter bands (measured: longest first 4.4% faster at 4 heads per XCD,
+    // 1.5% slower at 32)
+    a.nfull = CHUNK ? -1 : xcd_longest_first_nfull(nblocks, a.nqt, (a.W - 1 + C::BM - 1) / C::BM);
     void* args[] = {(void*)&a};
     return hipLaunchKernel((const void*)prefill_bf16_kernel<D, NW, CHUNK>,
                            dim3((unsigned)nblocks), dim3(C::NT), args, 0, stream);
