@@ -12,7 +12,7 @@
 //
 // Three kernels share one skeleton: a workgroup of 4 wavefronts owns 128
 // "row" items (32 per wavefront) and walks 32-item "column" tiles of its band
-// through an LDS ring (HBM -> LDS buffer loads, 2 tiles ahead, one barrier
+// through an LDS ring (HBM -> LDS buffer loads, 3 tiles ahead, one barrier
 // per tile).  Per wavefront and tile:
 //   DQ  rows = queries, columns = keys:  S^T = K Q^T, dP^T = V dO^T,
 //       dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T      (24 MFMAs)
@@ -23,6 +23,9 @@
 // l % 32 (a row item) and 16 column-tile items 8 (v/4) + 4 (l/32) + v%4, so
 // the packed probabilities feed the next product's B operand directly, as in
 // the forward kernel, and transposed operands come from ds_read_b64_tr_b16.
+// DQ reads its k tile, and DK its q tile, both whole and transposed, from one
+// LDS copy laid out with the bswz swizzle, which serves both reads without
+// bank conflicts.
 
 #include "swa_mfma.h"
 
@@ -37,8 +40,8 @@ struct BCfg {
     static constexpr int BM = 32 * NW;          // row items per workgroup
     static constexpr int BN = 32;               // column items per tile
     static constexpr int TILEB = BN * 2 * D;    // bytes per tile
-    static constexpr int NTL = MODE == kDV ? 2 : 3;   // tile kinds per step
-    static constexpr int PF = 2;                // tiles in flight ahead
+    static constexpr int NTL = 2;               // tile kinds per step
+    static constexpr int PF = 3;                // tiles in flight ahead
     static constexpr int R = PF + 1;            // ring slots per tile kind
     static constexpr int NLD_W = TILEB / 1024 / NW;
     // loads per wave per tile: the tiles, plus (DV, DK) one for the column
@@ -169,17 +172,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
 
     // ---- tile ring: kind x of tile t in slot x * R + (t - t0) % R
-    // DQ: 0 = K (rows whole), 1 = K (transposed reads), 2 = V (rows whole)
+    // DQ: 0 = K (read whole and transposed), 1 = V (rows whole)
     // DV: 0 = Q (rows whole), 1 = dout (transposed reads)
-    // DK: 0 = Q (rows whole), 1 = Q (transposed reads), 2 = dout (rows whole)
+    // DK: 0 = Q (read whole and transposed), 1 = dout (rows whole)
+    constexpr int SW0 = MODE == kDV ? kSwzK : kSwzB;   // swizzle of kind 0
+    constexpr int SW1 = MODE == kDV ? kSwzV : kSwzK;   // swizzle of kind 1
     auto slot = [&](int x, int t) { return ring + (x * C::R + (t - t0) % C::R) * C::TILEB; };
-    const bf16* src[3];
+    const bf16* src[2];
     src[0] = ROWQ ? K : Q;
-    src[1] = MODE == kDQ ? K : (MODE == kDV ? DO : Q);
-    src[2] = ROWQ ? V : DO;
-    uint32_t offk[C::NLD_W], offv[C::NLD_W];
-    tile_offsets<D, C::NW, kSwzK>(offk, wave, lane, 2 * D);
-    tile_offsets<D, C::NW, kSwzV>(offv, wave, lane, 2 * D);
+    src[1] = ROWQ ? V : DO;
+    uint32_t off0[C::NLD_W], off1[C::NLD_W];
+    tile_offsets<D, C::NW, SW0>(off0, wave, lane, 2 * D);
+    tile_offsets<D, C::NW, SW1>(off1, wave, lane, 2 * D);
     const int slab = T * D * 2;
     // DV, DK: lanes 0..7 of every wave copy the tile's 32 log2 normalisers
     // and (DK) lanes 8..15 its 32 deltas into the slot's stats (all waves
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int boff = tt * C::TILEB;
 #pragma unroll
         for (int x = 0; x < C::NTL; ++x)
-            dma_tile(rows_rsrc(src[x], boff, slab), lds_addr(slot(x, t)), wave, x == 1 ? offv : offk);
+            dma_tile(rows_rsrc(src[x], boff, slab), lds_addr(slot(x, t)), wave, x == 1 ? off1 : off0);
         if (!ROWQ) {
             const uint32_t sbase = lds_addr(&stats[(t - t0) % C::R][0]);
             // lane l < 8 (l < 16) fetches items 4 (l % 8) .. + 3 of L (delta)
@@ -226,7 +230,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int k0 = j * C::BN;
             const char* A0 = slot(0, j);
             const char* A1 = slot(1, j);
-            const char* A2 = slot(2, j);
             float Ls[16], Ds[16];
             if (!ROWQ) {
                 const float* st = &stats[(j - t0) % C::R][0];
@@ -237,11 +240,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
             for (int dc = 0; dc < D / 16; ++dc) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row_frag<D>(A0, lr, hh, dc), f0[dc],
-                                                            s, 0, 0, 0);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row_frag<D, SW0>(A0, lr, hh, dc),
+                                                            f0[dc], s, 0, 0, 0);
                 if (MODE != kDV)
                     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        read_row_frag<D>(A2, lr, hh, dc), f1[dc], dp, 0, 0, 0);
+                        read_row_frag<D, kSwzK>(A1, lr, hh, dc), f1[dc], dp, 0, 0, 0);
             }
             // band mask: row item ri against column items k0 + 8 (v/4) + 4 hh + v%4
             if (!interior(j)) {
@@ -264,8 +267,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const bf16x8 b0 = pack8(s, 0), b1 = pack8(s, 8);
             // accumulate: (DQ) dQ^T += K^T dS^T, (DV) dV^T += dO^T P, (DK) dK^T += Q^T dS
             bf16x8 t0f[D / 32], t1f[D / 32];
-            read_v_chunk<D>(A1, 0, lane, t0f);
-            read_v_chunk<D>(A1, 1, lane, t1f);
+            // transposed operand: kind 0 (k or q) for DQ, DK; kind 1 (dout) for DV
+            const char* At = MODE == kDV ? A1 : A0;
+            read_v_chunk<D, MODE == kDV ? kSwzV : kSwzB>(At, 0, lane, t0f);
+            read_v_chunk<D, MODE == kDV ? kSwzV : kSwzB>(At, 1, lane, t1f);
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t0f[db], b0, acc[db], 0, 0, 0);

@@ -36,6 +36,19 @@ template <int D> __device__ inline int kswz(int row) {
 template <int D> __device__ inline int vswz(int row) {
     return D == 128 ? 4 * (row & 3) : 4 * (row & 1);
 }
+// Tile read both ways (whole rows, and transposed): chunk c of row r is
+// stored at c ^ bswz(r), the bit reversal of r's low four bits (D = 128) or
+// of bits 1..3 (D = 64).  It spreads the 16 lanes of a whole-row read over
+// 16 bank groups and the 32 lanes of a transposing read over all 64 banks,
+// so one copy of the tile serves both reads without conflicts.
+template <int D> __device__ inline int bswz(int row) {
+    if (D == 128) {
+        const int r = row & 15;
+        return ((r & 1) << 3) | ((r & 2) << 1) | ((r & 4) >> 1) | ((r & 8) >> 3);
+    }
+    const int r = (row >> 1) & 7;
+    return ((r & 1) << 2) | (r & 2) | ((r & 4) >> 2);
+}
 
 // Buffer resource over the bytes [off, slab_bytes) of one (batch, head)
 // slab whose rows are at least D elements apart: loads past the sequence
@@ -69,8 +82,9 @@ __device__ inline uint32_t lds_addr(const void* p) {
 // Swizzle selectors for tile layouts in LDS.
 constexpr int kSwzK = 0;   // kswz: rows read whole (16 lanes over 16 rows of one chunk column)
 constexpr int kSwzV = 1;   // vswz: rows read through ds_read_b64_tr_b16
+constexpr int kSwzB = 2;   // bswz: rows read both ways
 template <int D, int SW> __device__ inline int swz(int row) {
-    return SW == kSwzV ? vswz<D>(row) : kswz<D>(row);
+    return SW == kSwzV ? vswz<D>(row) : SW == kSwzB ? bswz<D>(row) : kswz<D>(row);
 }
 
 // Source offsets of one tile's loads (N 1-KiB loads per wave, NW waves).
