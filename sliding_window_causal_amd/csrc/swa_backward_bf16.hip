@@ -29,6 +29,8 @@
 
 #include "swa_mfma.h"
 
+#include <type_traits>
+
 namespace swa {
 namespace {
 
@@ -177,7 +179,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // DK: 0 = Q (read whole and transposed), 1 = dout (rows whole)
     constexpr int SW0 = MODE == kDV ? kSwzK : kSwzB;   // swizzle of kind 0
     constexpr int SW1 = MODE == kDV ? kSwzV : kSwzK;   // swizzle of kind 1
-    auto slot = [&](int x, int t) { return ring + (x * C::R + (t - t0) % C::R) * C::TILEB; };
+    // Ring slot s of kind x (tile t lives in slot (t - t0) mod R); slot numbers
+    // are compile-time constants at every call site (the key loop is unrolled
+    // over the R = 4 slots), so LDS addresses carry them as immediates.
+    static_assert(C::R == 4, "the loop is unrolled over 4 ring slots");
+    auto slot = [&](int x, int s) { return ring + (x * C::R + s % C::R) * C::TILEB; };
     const bf16* src[2];
     src[0] = ROWQ ? K : Q;
     src[1] = ROWQ ? V : DO;
@@ -193,14 +199,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const_cast<float*>(a.lse) + (int64_t)bh * T, 0, T * 4, 0x00020000);
     const __amdgpu_buffer_rsrc_t del_rs = __builtin_amdgcn_make_buffer_rsrc(
         a.delta + (int64_t)bh * T, 0, T * 4, 0x00020000);
-    auto load = [&](int t) {
+    auto load = [&](int t, int s) {   // tile t into ring slot s
         const int tt = min(t, t1 - 1);
         const int boff = tt * C::TILEB;
 #pragma unroll
         for (int x = 0; x < C::NTL; ++x)
-            dma_tile(rows_rsrc(src[x], boff, slab), lds_addr(slot(x, t)), wave, x == 1 ? off1 : off0);
+            dma_tile(rows_rsrc(src[x], boff, slab), lds_addr(slot(x, s)), wave, x == 1 ? off1 : off0);
         if (!ROWQ) {
-            const uint32_t sbase = lds_addr(&stats[(t - t0) % C::R][0]);
+            const uint32_t sbase = lds_addr(&stats[s % C::R][0]);
             // lane l < 8 (l < 16) fetches items 4 (l % 8) .. + 3 of L (delta)
             const uint32_t soff = (tt * C::BN + 4 * (lane & 7)) * 4;
             if (lane < 8) lds_load16(lse_rs, sbase, soff);
@@ -222,17 +228,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const float c = a.c;
 
 #pragma unroll
-    for (int i = 0; i < C::PF; ++i) load(t0 + i);
+    for (int i = 0; i < C::PF; ++i) load(t0 + i, i);
     publish();                // tile t0 has landed
-    for (int j = t0; j < t1; ++j) {
-        load(j + C::PF);      // into the slot of tile j - 1, released by the last barrier
+    // one column tile j, in ring slot KS = (j - t0) mod 4
+    auto step = [&](auto ks, int j) {
+        constexpr int KS = decltype(ks)::value;
+        load(j + C::PF, KS + C::PF);   // into the slot of tile j - 1, released by the last barrier
         if (needs(j)) {
             const int k0 = j * C::BN;
-            const char* A0 = slot(0, j);
-            const char* A1 = slot(1, j);
+            const char* A0 = slot(0, KS);
+            const char* A1 = slot(1, KS);
             float Ls[16], Ds[16];
             if (!ROWQ) {
-                const float* st = &stats[(j - t0) % C::R][0];
+                const float* st = &stats[KS][0];
                 read_stats(st, hh, Ls);
                 if (MODE == kDK) read_stats(st + 32, hh, Ds);
             }
@@ -279,6 +287,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t1f[db], b1, acc[db], 0, 0, 0);
         }
         publish();            // tile j + 1 has landed; tile j's slots are free
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    for (int j = t0; j < t1;) {
+        step(I0{}, j);
+        if (++j >= t1) break;
+        step(I1{}, j);
+        if (++j >= t1) break;
+        step(I2{}, j);
+        if (++j >= t1) break;
+        step(I3{}, j);
+        ++j;
     }
     __builtin_amdgcn_s_waitcnt(0);   // no LDS load may outlive the workgroup
 
