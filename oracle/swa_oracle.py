@@ -269,6 +269,60 @@ def swa_backward(q, k, v, W: int, dout, scale=None):
     return dq, dk, dv
 
 
+def _band_weights_and_ds(q, k, v, dout, rows, keys_lo: int, keys_hi: int, W: int, sc: float):
+    """For query rows ``rows`` (consecutive, ascending) of one head: the softmax
+    weights P over keys [keys_lo, keys_hi) (zero outside each row's band) and
+    dS = P * (dP - rowsum(P * dP)) with dP = dout v^T, as in ``swa_backward``.
+    Every row's band must lie inside [keys_lo, keys_hi)."""
+    i = np.asarray(rows)[:, None]
+    j = np.arange(keys_lo, keys_hi)[None, :]
+    band = (j <= i) & (i - j < W)                           # P1 step 2, P5 band rule
+    s = np.matmul(q[rows], k[keys_lo:keys_hi].T) * sc
+    s = np.where(band, s, -np.inf)
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    P = e / e.sum(axis=1, keepdims=True)                    # P3 Step 2
+    dP = np.matmul(dout[rows], v[keys_lo:keys_hi].T)
+    return P, P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+
+
+def swa_backward_rows(q, k, v, W: int, dout, q_rows: Iterable[int], k_rows: Iterable[int],
+                      scale=None):
+    """``swa_backward`` restricted to sampled rows, from the band alone, so that
+    it runs at full size: dq for query rows ``q_rows``, dk and dv for key rows
+    ``k_rows``.  Same formulas as ``swa_backward``:
+      dq_i = scale * sum over j in band(i) of dS_ij k_j,  band(i) = [i-W+1, i]
+      dk_j = scale * sum over i in rows(j) of dS_ij q_i,  rows(j) = [j, j+W-1]
+      dv_j =         sum over i in rows(j) of P_ij dout_i
+    where row i's P and dS need all of band(i), so a key row reads the keys
+    [j-W+1, j+W-1].
+
+    q, k: (T, D); v, dout: (T, Dv), one head.  Returns (dq (len(q_rows), D),
+    dk (len(k_rows), D), dv (len(k_rows), Dv)) float64.
+    """
+    W = _check_window(W)
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    T, D = q.shape
+    sc = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    q_rows, k_rows = [int(r) for r in q_rows], [int(r) for r in k_rows]
+    for r in q_rows + k_rows:
+        if not 0 <= r < T:
+            raise IndexError(f"row {r} outside [0, {T})")
+    dq = np.empty((len(q_rows), D))
+    for n, i in enumerate(q_rows):
+        lo = max(0, i - W + 1)
+        _, dS = _band_weights_and_ds(q, k, v, dout, [i], lo, i + 1, W, sc)
+        dq[n] = np.matmul(dS, k[lo:i + 1])[0] * sc
+    dk = np.empty((len(k_rows), D))
+    dv = np.empty((len(k_rows), v.shape[1]))
+    for n, j in enumerate(k_rows):
+        rows = np.arange(j, min(T, j + W))
+        P, dS = _band_weights_and_ds(q, k, v, dout, rows, max(0, j - W + 1), min(T, j + W), W, sc)
+        col = j - max(0, j - W + 1)
+        dk[n] = np.matmul(dS[:, col], q[rows]) * sc
+        dv[n] = np.matmul(P[:, col], dout[rows])
+    return dq, dk, dv
+
+
 def mha_forward(x, wq, bq, wk, bk, wv, bv, wo, bo, H: int, W: int):
     """Multi-head sliding-window self-attention module forward in float64
     [P5 "A complete example with moving averages", the module's __call__].

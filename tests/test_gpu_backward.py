@@ -130,3 +130,41 @@ def test_forward_lse_and_backward_reusing_it(dtype, D, T, W, scale):
     torch.cuda.synchronize()
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["prefill_bf16_b1_h32_t8192_d128_w4096",
+                                  "prefill_bf16_b8_h32_t4096_d128_w1024"])
+def test_full_size_backward_sampled_rows(name):
+    """The prefill workloads at full size, launched as the benchmark times them
+    (workspace allocated once; with and without the forward's log-sum-exp).
+    dq of sampled query rows and dk, dv of sampled key rows (window and tile
+    edges, sequence ends, random rows) against the oracle's band-only
+    gradients, in the first and last head and a random one."""
+    w = si.WORKLOADS[name]
+    q, k, v = si.workload_qkv(w, DEV)
+    do = si.normal(tuple(q.shape), si.generator(w.seed + 11, DEV), torch.bfloat16, DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=DEV)
+    swa.swa_forward_lse(q, k, v, out, lse, w.W)
+    ws = torch.empty(int(swa.lib().swa_backward_workspace_bytes(w.B, w.H, w.T)),
+                     dtype=torch.uint8, device=DEV)
+    runs = {}
+    for with_lse in (False, True):
+        g = [torch.empty_like(q) for _ in range(3)]
+        swa.swa_backward(q, k, v, out, do, *g, w.W, lse=lse if with_lse else None, workspace=ws)
+        runs[with_lse] = g
+    torch.cuda.synchronize()
+    q_rows = si.sample_rows(w.T, w.W, n_random=16, seed=w.seed)
+    rng = np.random.default_rng(w.seed + 5)
+    edges = {0, 1, w.W - 1, w.W, w.T - w.W, w.T - 1}
+    k_rows = sorted({r for r in edges if 0 <= r < w.T} | {int(r) for r in rng.integers(0, w.T, 3)})
+    heads = [(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(w.H)))]
+    for b, h in heads:
+        rq, rk, rv = so.swa_backward_rows(npy(q[b, h]), npy(k[b, h]), npy(v[b, h]), w.W,
+                                          npy(do[b, h]), q_rows, k_rows)
+        qi, ki = torch.as_tensor(q_rows, device=DEV), torch.as_tensor(k_rows, device=DEV)
+        for with_lse, (dq, dk, dv) in runs.items():
+            tag = f"{name} b={b} h={h} lse={with_lse}"
+            _check(dq[b, h][qi], rq, torch.bfloat16, "dq " + tag)
+            _check(dk[b, h][ki], rk, torch.bfloat16, "dk " + tag)
+            _check(dv[b, h][ki], rv, torch.bfloat16, "dv " + tag)

@@ -666,3 +666,34 @@ def test_planted_noncausal_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(so, "band_mask", symmetric)
     assert not pin_mask_probe(TIERS["dense"])
     assert not pin_causal_sdpa(TIERS["dense"])
+
+
+@pytest.mark.parametrize("T,W,scale", [(23, 1, None), (23, 5, None), (23, 9, 0.35),
+                                       (23, 23, None), (23, 40, -0.2), (64, 17, None)])
+def test_backward_rows_match_full_backward(T, W, scale):
+    """The sampled-row gradients equal the full chain-rule gradients (which the
+    tests above pin to torch autograd and central differences) on every row,
+    including rows whose band is cut by the sequence start or end."""
+    r = _rng(60 + T + W)
+    D, Dv = 6, 4
+    q, k = r.standard_normal((T, D)), r.standard_normal((T, D))
+    v, do = r.standard_normal((T, Dv)), r.standard_normal((T, Dv))
+    dq, dk, dv = so.swa_backward(q, k, v, W, do, scale=scale)
+    rows = range(T)
+    sq, sk, sv = so.swa_backward_rows(q, k, v, W, do, rows, rows, scale=scale)
+    for mine, ref in ((sq, dq), (sk, dk), (sv, dv)):
+        assert np.max(np.abs(mine - ref)) <= 1e-12
+    # an arbitrary sample, in any order, gives those rows
+    qs, ks = [T - 1, 0, T // 2], [3, T - 1, 0]
+    sq, sk, sv = so.swa_backward_rows(q, k, v, W, do, qs, ks, scale=scale)
+    assert np.max(np.abs(sq - dq[qs])) <= 1e-12
+    assert np.max(np.abs(sk - dk[ks])) <= 1e-12
+    assert np.max(np.abs(sv - dv[ks])) <= 1e-12
+
+
+def test_backward_rows_rejects_rows_outside_the_sequence():
+    x = np.zeros((4, 2))
+    with pytest.raises(IndexError):
+        so.swa_backward_rows(x, x, x, 2, x, [4], [])
+    with pytest.raises(IndexError):
+        so.swa_backward_rows(x, x, x, 2, x, [], [-1])
