@@ -355,6 +355,37 @@ def mha_forward(x, wq, bq, wk, bk, wv, bv, wo, bo, H: int, W: int):
     return proj(concat, wo, bo)
 
 
+def mha_rows(x, wq, bq, wk, bk, wv, bv, wo, bo, H: int, W: int, rows: Iterable[int]):
+    """Rows ``rows`` of ``mha_forward`` for one sequence, without the T x T
+    scores, so that it runs at full size: the same steps 1-4, with step 3 done
+    by ``swa_rows`` over each row's band, and the query projection taken only
+    for the sampled rows.
+
+    x: (T, d_model); weights and biases as in ``mha_forward``.
+    Returns (len(rows), d_model) float64.
+    """
+    x = _f64(x)
+    T, dm = x.shape
+    H = int(H)
+    if H < 1 or dm % H != 0:
+        raise ValueError("d_model must be a positive multiple of the head count")
+    dh = dm // H
+    rows = [int(r) for r in rows]
+
+    def proj(a, w, b):
+        y = np.matmul(a, _f64(w))
+        return y if b is None else y + _f64(b)
+
+    k, v = proj(x, wk, bk), proj(x, wv, bv)           # (T, dm): every row may be a key
+    o = np.empty((len(rows), dm))
+    for h in range(H):
+        cols = slice(h * dh, (h + 1) * dh)
+        qh = np.zeros((T, dh))
+        qh[rows] = proj(x[rows], wq, bq)[:, cols]       # only sampled rows act as queries
+        o[:, cols] = swa_rows(qh, k[:, cols], v[:, cols], W, rows)
+    return proj(o, wo, bo)
+
+
 def ring_slot(p: int, W: int) -> int:
     """Slot of absolute position p in a W-slot ring.
 

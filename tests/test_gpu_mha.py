@@ -155,3 +155,30 @@ def test_module_calls_from_two_threads_on_two_streams():
         for n, o in enumerate(outs[i]):
             assert torch.equal(o, refs[i]), f"thread {i}, call {n}"
 
+
+
+def test_full_size_module_sampled_rows():
+    """The module of one 32-head layer (d_model 4096 = 32 x 128, T 8192,
+    W 4096, inputs and weights drawn as the benchmark draws them, workspace
+    allocated once): sampled output rows (window and tile edges, both ends,
+    random rows) against the oracle's row-by-row module forward."""
+    w = si.WORKLOADS["prefill_bf16_b1_h32_t8192_d128_w4096"]
+    dm = w.H * w.D
+    g = si.generator(w.seed + 7, DEV)
+    x = si.normal((w.B, w.T, dm), g, torch.bfloat16, DEV)
+    wts = [si.normal((dm, dm), g, torch.float32, DEV).mul_(dm ** -0.5).to(torch.bfloat16)
+           for _ in range(4)]
+    bss = [torch.zeros(dm, dtype=torch.bfloat16, device=DEV) for _ in range(4)]
+    out = torch.empty_like(x)
+    ws = torch.empty(swa.swa_mha_workspace_bytes(w.B, w.T, dm, torch.bfloat16),
+                     dtype=torch.uint8, device=DEV)
+    swa.swa_mha_forward(x, wts[0], bss[0], wts[1], bss[1], wts[2], bss[2], wts[3], bss[3], out,
+                        w.H, w.W, workspace=ws)
+    torch.cuda.synchronize()
+    rows = si.sample_rows(w.T, w.W, n_random=12, seed=w.seed + 7)
+    ref = so.mha_rows(npy(x[0]), npy(wts[0]), npy(bss[0]), npy(wts[1]), npy(bss[1]),
+                      npy(wts[2]), npy(bss[2]), npy(wts[3]), npy(bss[3]), w.H, w.W, rows)
+    g64 = npy(out[0][torch.as_tensor(rows, device=DEV)]).astype(np.float64)
+    assert np.all(np.isfinite(g64))
+    err, bound = np.abs(g64 - ref), BF_ATOL + BF_RTOL * np.abs(ref)
+    assert np.all(err <= bound), f"max err {err.max():.3e}, worst ratio {(err / bound).max():.3f}"

@@ -697,3 +697,20 @@ def test_backward_rows_rejects_rows_outside_the_sequence():
         so.swa_backward_rows(x, x, x, 2, x, [4], [])
     with pytest.raises(IndexError):
         so.swa_backward_rows(x, x, x, 2, x, [], [-1])
+
+
+@pytest.mark.parametrize("H,W,bias", [(1, 3, True), (2, 5, False), (4, 40, True), (3, 1, True)])
+def test_mha_rows_match_the_module_forward(H, W, bias):
+    """Sampled rows of the module equal the pinned mha_forward's rows, in any
+    order and with repeats."""
+    r = _rng(70 + H + W)
+    T, dm = 21, 12
+    x = r.standard_normal((T, dm))
+    ws = [r.standard_normal((dm, dm)) / math.sqrt(dm) for _ in range(4)]
+    bs = [r.standard_normal(dm) if bias else None for _ in range(4)]
+    args = (ws[0], bs[0], ws[1], bs[1], ws[2], bs[2], ws[3], bs[3], H, W)
+    ref = so.mha_forward(x, *args)
+    assert np.max(np.abs(so.mha_rows(x, *args, range(T)) - ref)) <= 1e-12
+    rows = [T - 1, 0, 7, 7, W]
+    rows = [i for i in rows if i < T]
+    assert np.max(np.abs(so.mha_rows(x, *args, rows) - ref[rows])) <= 1e-12
