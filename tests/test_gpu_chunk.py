@@ -294,3 +294,33 @@ def test_split_chunk_stream_matches_prefill():
     pre = swa.sliding_window_attention(q, k, v, W)
     torch.cuda.synchronize()
     assert_close(out, npy(pre).astype(np.float64), dtype, "split chunks vs prefill")
+
+
+@pytest.mark.parametrize("S,C", [(1, 2048), (4, 512), (1, 128)])
+def test_chunk_benchmark_shapes(S, C):
+    """The chunk shapes the benchmark times (32 heads, D 128, full 4096-slot
+    rings at write head 5W + 123, inputs drawn as it draws them), through both
+    the plain and the split launch: every row of three (stream, head) pairs
+    against the oracle (two pairs at C 2048)."""
+    w = si.WORKLOADS["prefill_bf16_b1_h32_t8192_d128_w4096"]
+    H, D, W = w.H, w.D, w.W
+    g = si.generator(w.seed, DEV)
+    qc, kc, vc = (si.normal((S, H, C, D), g, torch.bfloat16, DEV) for _ in range(3))
+    kr = si.normal((S, H, W, D), g, torch.bfloat16, DEV)
+    vr = si.normal((S, H, W, D), g, torch.bfloat16, DEV)
+    pos0 = [5 * W + 123] * S
+    p0 = torch.tensor(pos0, dtype=torch.int64, device=DEV)
+    plain = torch.empty_like(qc)
+    swa.swa_chunk_forward(qc, kc, vc, kr, vr, p0, plain)
+    nws = swa.swa_chunk_workspace_bytes(S, H, C, D, W, torch.bfloat16)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=DEV)
+    split = torch.empty_like(qc)
+    swa.swa_chunk_forward_split(qc, kc, vc, kr, vr, p0, split, ws)
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (S - 1, H - 1), (S // 2, 13)]
+    for s, h in pairs[:2] if C > 512 else pairs:
+        sl = (slice(s, s + 1), slice(h, h + 1))
+        ref = so.swa_chunk(npy(qc[sl]), npy(kc[sl]), npy(vc[sl]), npy(kr[sl]), npy(vr[sl]),
+                           pos0[s:s + 1], W)
+        assert_close(plain[sl], ref, torch.bfloat16, f"plain S={S} C={C} s={s} h={h}")
+        assert_close(split[sl], ref, torch.bfloat16, f"split S={S} C={C} s={s} h={h}")
