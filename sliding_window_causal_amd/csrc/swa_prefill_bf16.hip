@@ -20,7 +20,9 @@
 //                    reference is raised, and O rescaled by exp2(m_old -
 //                    m_new), only when a row max grows by more than 2^8; the
 //                    prefill's fast pass takes row maxima only on edge tiles
-//                    and a wave's first tiles (see the kernel).
+//                    and the first interior tile where a row's window starts
+//                    on it, and redoes just the rows that overflow (see the
+//                    kernel).
 //   O^T += V^T P^T   P^T goes from the S^T accumulator straight into the B
 //                    operand (bf16, round to nearest even); the row sum is
 //                    taken over those same bf16 weights (v_dot2 with ones).
@@ -196,6 +198,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int ib = qw0 >= C::BN - 1 ? (qw0 - (C::BN - 1)) / C::BN + 1 : 0;
     const int ilen = max(ib - ia, 0);
     auto interior = [&](int t) { return (unsigned)(t - ia) < (unsigned)ilen; };
+    // Fast-pass tiles [fa, fa + flen): interior tiles that every row of the
+    // wave reaches with a key already seen in an earlier tile, i.e. all
+    // interior tiles but the first when the last row's window starts on it
+    // (xa a multiple of the tile, or xa <= 0).  Fixed by positions alone,
+    // so which tiles take the row max never depends on data.
+    const int fa = ia + ((xa <= 0 || xa % C::BN == 0) ? 1 : 0);
+    const int flen = max(ib - fa, 0);
     // a split's partial row: unnormalised output o, max m (raw units) and
     // this lane's half of the sum; the merge rescales partials to a common max
     auto write_partial = [&](const f32x16 (&o)[D / 32], float m, float lsum) {
@@ -244,16 +253,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     float lsum;                       // this lane's half of the row sum
     float mref;                       // m * c, 0 while m = -inf
     // Fast pass (prefill, careful = false): the reference m only has to keep
-    // the exponents in range, so once every row of the wave has one, tiles
-    // inside every row's band skip the row max.  Scores that later exceed the
-    // reference by more than the fp32 exponent range make a probability, the
-    // row sum or the output non-finite; the workgroup then redoes its rows
-    // with the max taken on every tile (careful pass).  The chunk
-    // continuation always runs careful.
+    // the exponents in range, so the fast-pass tiles [fa, fa + flen) skip the
+    // row max.  A row whose scores there exceed its reference by more than
+    // the fp32 exponent range gets a non-finite probability, row sum or
+    // output; such rows (and only they) are redone with the max taken on
+    // every tile (careful pass) and stored from it, while every other row
+    // keeps its fast-pass result.  Each row's result therefore depends on
+    // its own window only, bit for bit.  The chunk continuation always runs
+    // careful.
     bool careful = CHUNK;
-    bool ref_set;                     // every row of the wave has a finite m
-    // Fast-pass tiles [f_lo, f_lo + f_len): the interior tiles once ref_set
-    // holds; empty before that and in the careful pass.
+    bool redo = true;                 // careful pass: this row is stored from it
+    // Tiles that skip the row max: [fa, fa + flen) in the fast pass, none in
+    // the careful pass.
     int f_lo, f_len;
     // Cleared before the prologue's tile loads (asm with memory clobbers
     // keep the store ahead of them) and so before its first barrier.
@@ -371,6 +382,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // row max is mx: raise m if mx exceeds it by more than 2^8 and rescale
     // what has been accumulated so far.  Runs between tiles, outside the
     // MFMA/VALU overlap regions.
+    // Scores of a tile outside this wave's band: all -inf, so its
+    // probabilities are exact zeros whatever its keys hold (a finite key can
+    // still overflow the fp32 dot product).  The empty asm keeps this a
+    // branch taken on those few tiles rather than selects on every tile.
+    auto kill_tile = [&](f32x16& s) {
+        asm volatile("");
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] = -__builtin_inff();
+    };
     auto raise_ref = [&](float mx) {
         const bool raise = mx > m + tau;               // false while the row is fully masked
         if (__any(raise)) {
@@ -383,7 +403,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
         }
-        ref_set = !__any(m == -__builtin_inff());
     };
 
   for (;;) {   // fast pass, then (rarely) the careful pass
@@ -392,9 +411,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     m = -__builtin_inff();
     mref = 0.f;
     lsum = 0.f;
-    ref_set = false;
-    f_lo = 0;
-    f_len = 0;
+    f_lo = careful ? 0 : fa;
+    f_len = careful ? 0 : flen;
     if constexpr (!CHUNK) {
         // t0 * 32 < T, so the first tile starts inside both slabs.  The
         // range ends with the band: tiles past it are zeros, not reads.
@@ -420,17 +438,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         negate_q = false;
     }
 
-    // Score tiles start finite: a wave computes (and discards) tiles outside
-    // its band, and their probabilities must come out as exact zeros.
-    f32x16 sA = f32x16{}, sB = f32x16{};
+    f32x16 sA, sB;
     if (needs(t0)) {
         qk_tile<D>(kslot_n(0), qf, lr, hh, ksw, sA);
         if (!interior(t0)) mask_tile(sA, qi, t0 * C::BN, hh, W);
         raise_ref(tile_max(sA));
-        if (!careful && ref_set) {
-            f_lo = ia;
-            f_len = ilen;
-        }
+    } else {
+        kill_tile(sA);
     }
     // K operands of the next score tile live in registers one step ahead:
     // step j computes S(j+1) from kf of K(j+1) and reads K(j+2) into the
@@ -457,10 +471,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         float mxn = 0.f;   // chunk continuation: the row max of S(j+1)
 
         // Every wave runs every tile of the workgroup, so the accumulator
-        // path has no branches; a tile outside this wave's band gets
-        // mc = +inf and hence probabilities exp2(-inf) = 0 exactly.
+        // path has no branches; a tile outside this wave's band arrives with
+        // scores -inf (kill_tile) and so gets probabilities exp2(-inf) = 0.
         {
-            const float mc = nj ? mref : __builtin_inff();
+            const float mc = mref;
             // The schedule is written out slice by slice; each sched_barrier
             // closes a slice, so the MFMAs at the top of a slice run on the
             // matrix core while the slice's (independent) vector ALU work
@@ -481,8 +495,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             // Region A: S(j+1) = K(j+1) Q^T, one MFMA per 16-wide d slice, with
             // the probabilities of keys NPRE..NEA-1 of tile j and the operand
             // p0 of keys 0..15.  S(j+1) is computed even where this wave does
-            // not need it (at the end from a stale but finite buffer); it is
-            // then never used.
+            // not need it (at the end from a stale buffer); kill_tile then
+            // replaces its scores.
             sn = f32x16{};
 #pragma unroll
             for (int dc = 0; dc < ND; ++dc) {
@@ -515,23 +529,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             if constexpr (CHUNK) mxn = tile_max(sn);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // Edge tiles are masked; their max, and that of every tile in the
-        // careful pass or before every row has a reference, updates m.
-        if constexpr (CHUNK) {
-            if (nn) {
+        // Edge tiles are masked; the max of every tile outside the fast-pass
+        // range (all tiles in the careful pass) updates m.
+        if (!nn) {
+            kill_tile(sn);
+        } else if constexpr (CHUNK) {
+            {
                 if (!interior(j + 1)) {
                     mask_tile(sn, qi, (j + 1) * C::BN, hh, W);
                     mxn = tile_max(sn);
                 }
                 raise_ref(mxn);
             }
-        } else if ((unsigned)(j + 1 - f_lo) >= (unsigned)f_len && nn) {
+        } else if ((unsigned)(j + 1 - f_lo) >= (unsigned)f_len) {
             if (!interior(j + 1)) mask_tile(sn, qi, (j + 1) * C::BN, hh, W);
             raise_ref(tile_max(sn));
-            if (!careful && ref_set) {
-                f_lo = ia;
-                f_len = ilen;
-            }
         }
         publish();   // V(j+2) and K(j+3) have landed
     };
@@ -552,12 +564,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
 
     __builtin_amdgcn_s_waitcnt(0);   // every tile load has landed
-    if (careful) break;
-    // Any inf or NaN in this lane's row sum or outputs shows in their sum:
-    // its exponent field is all ones.  The empty asm hides the bits' origin,
-    // so the test is not folded into a float compare, which this file's
-    // no-NaN float model would reduce to an infinity test.
-    {
+    if constexpr (CHUNK) {
+        if (a.nsplit > 1) {
+            write_partial(o, m, lsum);
+            return;
+        }
+    }
+    // Fast pass: a row is redone when its row sum or any output of either
+    // lane that holds it is inf or NaN.  Any such value shows in this lane's
+    // sum: its exponent field is all ones.  The empty asm hides the bits'
+    // origin, so the test is not folded into a float compare, which this
+    // file's no-NaN float model would reduce to an infinity test.
+    bool row_bad = false;
+    if (!careful) {
         float chk = lsum;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
@@ -565,44 +584,46 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             for (int v = 0; v < 16; ++v) chk += o[db][v];
         uint32_t bits = __float_as_uint(chk);
         asm volatile("" : "+v"(bits));
-        const bool bad = (bits & 0x7f800000u) == 0x7f800000u;
-        if (__any(bad) && lane == 0) rerun = 1;
+        const uint32_t bad = (bits & 0x7f800000u) == 0x7f800000u ? 1u : 0u;
+        const auto pr = __builtin_amdgcn_permlane32_swap(bad, bad, false, false);
+        row_bad = (pr[0] | pr[1]) != 0u && qi < T;
     }
-    __syncthreads();
-    if (rerun == 0) break;
-    careful = true;
-  }
 
-    if constexpr (CHUNK) {
-        if (a.nsplit > 1) {
-            write_partial(o, m, lsum);
-            return;
+    // ---- finalise the rows this pass owns: the fast pass stores its good
+    // rows, the careful pass the rows the fast pass could not finish.  O / l,
+    // bf16, store (lane holds d = 32 db + 8 g + 4 hh + 0..3).
+    if (careful ? redo : !row_bad) {
+        const float l = swap_sum(lsum);
+        const float inv = 1.f / l;
+        if (!CHUNK && a.lse != nullptr && qi < T && hh == 0)
+            a.lse[(int64_t)bh * T + qi] = (m * c + __builtin_amdgcn_logf(l)) * kLn2;
+        if (qi < T) {
+            bf16* orow = a.out + b * a.L.o.b + h * a.L.o.h + (int64_t)(qi - p0r) * a.L.o.t;
+            // All packs first, each in registers of its own, then the
+            // stores: a store's data registers are not rewritten while it is
+            // queued.
+            bf16x4 w[D / 32][4];
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[db][g][e] = (bf16)(o[db][4 * g + e] * inv);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g + 4 * hh) = w[db][g];
         }
     }
-
-    // ---- finalise: O / l, bf16, store (lane holds d = 32 db + 8 g + 4 hh + 0..3)
-    const float l = swap_sum(lsum);
-    const float inv = 1.f / l;
-    if (!CHUNK && a.lse != nullptr && qi < T && hh == 0)
-        a.lse[(int64_t)bh * T + qi] = (m * c + __builtin_amdgcn_logf(l)) * kLn2;
-    if (qi < T) {
-        bf16* orow = a.out + b * a.L.o.b + h * a.L.o.h + (int64_t)(qi - p0r) * a.L.o.t;
-        // All packs first, each in registers of its own, then the stores:
-        // a store's data registers are not rewritten while it is queued.
-        bf16x4 w[D / 32][4];
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) w[db][g][e] = (bf16)(o[db][4 * g + e] * inv);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g + 4 * hh) = w[db][g];
-    }
+    if (careful) break;
+    if (__any(row_bad) && lane == 0) rerun = 1;
+    __syncthreads();
+    if (rerun == 0) break;
+    redo = row_bad;
+    careful = true;
+  }
 }
 
 template <int D, int NW, bool CHUNK>
