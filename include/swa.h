@@ -19,7 +19,8 @@
  *    stated layout; element type is the `dtype` argument (SWA_F32 = float,
  *    SWA_BF16 = bfloat16).  Output has the input dtype.
  *  - The caller owns every buffer.  The library never allocates, frees or
- *    synchronises; it keeps no state beyond cached device attributes.
+ *    synchronises; it keeps no state beyond cached device attributes and the
+ *    static device scratch array of swa_decode_split_noalloc.
  *  - `out` must not alias any input.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream).  A launch failure returns SWA_ERR_LAUNCH; faults surface when
@@ -49,7 +50,8 @@ typedef enum {
     SWA_OK = 0,
     SWA_ERR_INVALID_ARG = 1,
     SWA_ERR_UNSUPPORTED = 2,
-    SWA_ERR_LAUNCH = 3
+    SWA_ERR_LAUNCH = 3,
+    SWA_ERR_SCRATCH_LIMIT = 4   /* swa_decode_split_noalloc: sizes need more than its static scratch */
 } swa_status_t;
 
 /* Version of this ABI (bumped on any signature or semantic change). */
@@ -194,6 +196,30 @@ int swa_decode_split(const void* q, const void* kring, const void* vring, const 
 int swa_decode_append(const void* q, const void* knew, const void* vnew, void* kring, void* vring,
                       const int64_t* pos, void* out, int64_t S, int64_t H, int64_t D, int64_t W,
                       int dtype, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Decode as swa_decode_split, allocating nothing: for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  The split's
+ * partial results live in a static device array of
+ * SWA_NOALLOC_SCRATCH_BYTES bytes inside the library, one copy per GPU, held
+ * until the process ends; it covers every size swa_decode_workspace_bytes()
+ * asks for (at most about 1.3 MiB: the split stops at 512 (stream, head)
+ * pairs and 2048 workgroups).  Same kernels and bit-identical results as
+ * swa_decode_split with a workspace of its own.
+ *
+ *   arguments    : as swa_decode_split without the workspace; `stream` must
+ *                  belong to the GPU that holds q, the rings and out
+ * Calls that overlap on one GPU (concurrent streams, or threads) share that
+ * GPU's array and race: serialise them.  Nothing needs to be zero on entry.
+ * Returns SWA_ERR_SCRATCH_LIMIT (before any HIP call) if the sizes would
+ * need more than SWA_NOALLOC_SCRATCH_BYTES, and SWA_ERR_LAUNCH if the
+ * array's device address cannot be found.
+ */
+#define SWA_NOALLOC_SCRATCH_BYTES (2 * 1024 * 1024)
+int swa_decode_split_noalloc(const void* q, const void* kring, const void* vring,
+                             const int64_t* pos, void* out, int64_t S, int64_t H, int64_t D,
+                             int64_t W, int dtype, void* stream);
 
 /*
  * Ring append (not part of the timed path): for every stream s and head h,

@@ -15,6 +15,9 @@ Entry points (same names as the C ABI):
   swa_decode_split(q, kring, vring, pos, out)    decode, window split over workgroups
   swa_decode_append(q, knew, vnew, kring, vring, pos, out)
                                                  append + decode in one launch
+  swa_decode_split_noalloc(q, kring, vring, pos, out)
+                                                 split decode with the library's static
+                                                 scratch (allocates nothing)
   swa_chunk_forward(q, kc, vc, kring, vring, pos0, out)
                                                  chunk of new tokens continuing a ring
   swa_chunk_forward_split(q, kc, vc, kring, vring, pos0, out)
@@ -50,7 +53,8 @@ __all__ = [
     "SWA_ERR_UNSUPPORTED", "SWA_ERR_LAUNCH", "SWAError", "lib", "abi_version",
     "status_string", "swa_forward", "swa_forward_strided", "swa_decode", "swa_ring_append", "swa_chunk_forward",
     "swa_ring_append_chunk", "swa_chunk_workspace_bytes", "swa_chunk_forward_split",
-    "swa_decode_workspace_bytes", "swa_decode_split",
+    "swa_decode_workspace_bytes", "swa_decode_split", "swa_decode_split_noalloc",
+    "SWA_ERR_SCRATCH_LIMIT", "NOALLOC_SCRATCH_BYTES",
     "swa_decode_append", "swa_forward_lse", "swa_backward", "swa_mha_workspace_bytes", "swa_mha_forward", "SlidingWindowMHA",
     "sliding_window_attention", "decode", "decode_append", "chunk_attention",
 ]
@@ -59,6 +63,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libswa.so")
 
 SWA_F32, SWA_BF16 = 0, 1
 SWA_OK, SWA_ERR_INVALID_ARG, SWA_ERR_UNSUPPORTED, SWA_ERR_LAUNCH = 0, 1, 2, 3
+SWA_ERR_SCRATCH_LIMIT = 4
+NOALLOC_SCRATCH_BYTES = 2 * 1024 * 1024     # SWA_NOALLOC_SCRATCH_BYTES of include/swa.h
 
 _DTYPES = {torch.float32: SWA_F32, torch.bfloat16: SWA_BF16}
 _lib = None
@@ -108,6 +114,8 @@ def lib() -> ctypes.CDLL:
     L.swa_decode_workspace_bytes.restype = i64
     L.swa_decode_split.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, p, i64, p]
     L.swa_decode_split.restype = i32
+    L.swa_decode_split_noalloc.argtypes = [p, p, p, p, p, i64, i64, i64, i64, i32, p]
+    L.swa_decode_split_noalloc.restype = i32
     L.swa_decode_append.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i32, p, i64, p]
     L.swa_decode_append.restype = i32
     L.swa_chunk_forward.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i32, p]
@@ -324,6 +332,17 @@ def swa_decode_split(q, kring, vring, pos, out, workspace=None, stream=None) -> 
     ws, nb = _workspace(q, S, H, D, W, workspace)
     _check(lib().swa_decode_split(_ptr(q), _ptr(kring), _ptr(vring), _ptr(pos), _ptr(out), S, H,
                                   D, W, code, _ptr(ws), nb, _stream(q, stream)))
+
+
+def swa_decode_split_noalloc(q, kring, vring, pos, out, stream=None) -> None:
+    """swa_decode_split with the split's partials in the library's static
+    device scratch: no allocation, no workspace; overlapping calls on one GPU
+    race."""
+    _check_device(q, kring, vring, pos, out)
+    code = _dtype_code(q, kring, vring, out)
+    S, H, D, W = _decode_dims(q, kring, vring, pos, out)
+    _check(lib().swa_decode_split_noalloc(_ptr(q), _ptr(kring), _ptr(vring), _ptr(pos),
+                                          _ptr(out), S, H, D, W, code, _stream(q, stream)))
 
 
 def swa_decode_append(q, knew, vnew, kring, vring, pos, out, workspace=None, stream=None) -> None:

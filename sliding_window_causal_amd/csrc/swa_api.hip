@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int64_t kMaxRowD = 256;
 
 bool positive(int64_t x) { return x >= 1; }
@@ -66,6 +66,9 @@ const char* swa_status_string(int status) {
         case SWA_ERR_INVALID_ARG: return "invalid argument (null pointer, size < 1 or window < 1)";
         case SWA_ERR_UNSUPPORTED: return "unsupported dtype or head size for this entry point";
         case SWA_ERR_LAUNCH: return "kernel launch failed";
+        case SWA_ERR_SCRATCH_LIMIT:
+            return "sizes need more scratch than the allocation-free entry point holds "
+                   "(SWA_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

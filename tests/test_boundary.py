@@ -46,9 +46,9 @@ def test_exported_symbols_are_c_linkage():
 
 
 def test_abi_version_and_status_strings():
-    assert swa.abi_version() == 1
+    assert swa.abi_version() == 2
     for code in (swa.SWA_OK, swa.SWA_ERR_INVALID_ARG, swa.SWA_ERR_UNSUPPORTED,
-                 swa.SWA_ERR_LAUNCH, 99):
+                 swa.SWA_ERR_LAUNCH, swa.SWA_ERR_SCRATCH_LIMIT, 99):
         s = swa.status_string(code)
         assert isinstance(s, str) and s
 
@@ -333,3 +333,36 @@ def test_product_package_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.replace("no fallback", ""), f
+
+
+def _dnoalloc(q=DUMMY, kr=DUMMY, vr=DUMMY, pos=DUMMY, o=DUMMY, S=1, H=4, D=128, W=4096,
+              dt=swa.SWA_BF16):
+    return swa.lib().swa_decode_split_noalloc(q, kr, vr, pos, o, S, H, D, W, dt, None)
+
+
+@pytest.mark.parametrize("kw,code", [(dict(q=None), swa.SWA_ERR_INVALID_ARG),
+                                     (dict(kr=None), swa.SWA_ERR_INVALID_ARG),
+                                     (dict(pos=None), swa.SWA_ERR_INVALID_ARG),
+                                     (dict(o=None), swa.SWA_ERR_INVALID_ARG),
+                                     (dict(S=0), swa.SWA_ERR_INVALID_ARG),
+                                     (dict(W=-2), swa.SWA_ERR_INVALID_ARG),
+                                     (dict(dt=7, S=1024), swa.SWA_ERR_UNSUPPORTED),
+                                     (dict(D=96, S=1024), swa.SWA_ERR_UNSUPPORTED)])
+def test_noalloc_decode_rejects_before_any_hip_call(kw, code):
+    assert _dnoalloc(**kw) == code
+
+
+def test_noalloc_scratch_covers_every_split_size():
+    """The static scratch holds the split's partials for every size the split
+    policy produces (splits stop at 512 (stream, head) pairs, 2048 workgroups
+    and 64 splits), so swa_decode_split_noalloc never returns
+    SWA_ERR_SCRATCH_LIMIT for a size swa_decode_split takes."""
+    L = swa.lib()
+    worst = 0
+    for sh in range(1, 600):
+        for D in (64, 128):
+            for W in (1, 255, 256, 257, 1000, 4096, 8191, 16384):
+                n = L.swa_decode_workspace_bytes(1, sh, D, W, swa.SWA_BF16)
+                assert n >= 0
+                worst = max(worst, n)
+    assert 0 < worst <= swa.NOALLOC_SCRATCH_BYTES
