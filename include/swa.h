@@ -308,9 +308,16 @@ int swa_ring_append_chunk(const void* kc, const void* vc, void* kring, void* vri
  *   scale          : finite; 0 selects 1 / sqrt(D)
  *   dtype          : SWA_F32 or SWA_BF16 (fp32 accumulation), 1 <= D <= 256
  *   workspace      : device memory of swa_backward_workspace_bytes() bytes
- *                    (per-row log-sum-exp and rowsum(dout * out)), 4-byte
- *                    aligned, owned by the caller
- * Row-wise kernels (one wavefront per query row, then per key row).
+ *                    (per-row log normaliser and delta), 4-byte aligned,
+ *                    owned by the caller
+ * bf16 with D in {64, 128} and 16-byte aligned pointers runs on the matrix
+ * cores.  There delta_i = dout_i . out_i at scales up to 1 / sqrt(D) in
+ * magnitude; for a sharper softmax (|scale| sqrt(D) > 1.001) a first kernel
+ * takes each row's sum of the rebuilt weights and delta_i = sum_j P_ij dP_ij
+ * in fp32 (rows renormalised), and dS reaches the matrix cores as two bf16
+ * terms, which keeps the gradients within the bf16 tolerance at any scale.
+ * Other shapes run row-wise kernels (one wavefront per query row, then per
+ * key row; fp32 arithmetic, delta as that band sum).
  */
 int64_t swa_backward_workspace_bytes(int64_t B, int64_t H, int64_t T);
 int swa_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,

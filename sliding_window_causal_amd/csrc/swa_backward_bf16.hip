@@ -10,7 +10,16 @@
 // P is rebuilt tile by tile as exp2(s * c - L_i log2(e)) from the forward's
 // per-row log-sum-exp L_i (c = log2(e) * scale), so no T x T array exists.
 //
-// Three kernels share one skeleton: a workgroup of 4 wavefronts owns 128
+// Sharper softmaxes (an explicit |scale| above 1/sqrt(D)) raise two roundings
+// above the bf16 bar: delta taken from the bf16 output cancels against dP
+// of the dominant key, and so does any common error of the rebuilt P (the
+// forward's row sums run over bf16 weights).  There the precise variant
+// first runs ST (below) for each row's z_i = sum_j P_ij and
+// y_i = sum_j P_ij dP_ij in fp32, replaces L_i by L_i + ln z_i (so the
+// rebuilt weights sum to one) and takes delta_i = y_i / z_i, and DQ and DK
+// feed dS to the matrix cores as two bf16 terms (hi + lo) instead of one.
+//
+// The kernels share one skeleton: a workgroup of 4 wavefronts owns 128
 // "row" items (32 per wavefront) and walks 32-item "column" tiles of its band
 // through an LDS ring (HBM -> LDS buffer loads, 3 tiles ahead, one barrier
 // per tile).  Per wavefront and tile:
@@ -19,6 +28,9 @@
 //   DV  rows = keys, columns = queries:  S = Q K^T, dV^T += dO^T P   (16)
 //   DK  rows = keys, columns = queries:  S = Q K^T, dP = dO V^T,
 //       dS = P (dP - delta), dK^T += Q^T dS                           (24)
+//   ST  rows = queries, columns = keys:  S^T = K Q^T, dP^T = V dO^T,
+//       z += P, y += P dP                                             (16)
+// (DQ and DK issue 8 more with the split dS.)
 // The accumulator layout of v_mfma_f32_32x32x16_bf16 gives lane l column
 // l % 32 (a row item) and 16 column-tile items 8 (v/4) + 4 (l/32) + v%4, so
 // the packed probabilities feed the next product's B operand directly, as in
@@ -34,7 +46,7 @@
 namespace swa {
 namespace {
 
-enum Mode { kDQ = 0, kDV = 1, kDK = 2 };
+enum Mode { kDQ = 0, kDV = 1, kDK = 2, kST = 3 };
 
 template <int D, int MODE>
 struct BCfg {
@@ -48,7 +60,7 @@ struct BCfg {
     static constexpr int NLD_W = TILEB / 1024 / NW;
     // loads per wave per tile: the tiles, plus (DV, DK) one for the column
     // items' statistics
-    static constexpr int NLD_T = NTL * NLD_W + (MODE == kDQ ? 0 : MODE == kDV ? 1 : 2);
+    static constexpr int NLD_T = NTL * NLD_W + (MODE == kDV ? 1 : MODE == kDK ? 2 : 0);
     static constexpr int VM_WAIT = (PF - 1) * NLD_T;
     static_assert(D == 64 || D == 128, "head size");
     static_assert(VM_WAIT < 64, "vmcnt range");
@@ -62,7 +74,8 @@ struct BArgs {
     const bf16* dout;
     bf16* grad;           // dq, dk or dv, [B, H, T, D]
     const float* lse;     // [B * H * T] log-sum-exp of the scaled scores (forward)
-    float* delta;         // [B * H * T] dout . out (written by DQ)
+    float* delta;         // [B * H * T] dout . out (written by DQ; precise: by ST)
+    float* lse_w;         // ST: [B * H * T] log normaliser of the rebuilt weights
     int T, W, nrt, nblocks, remap;
     int nfull;            // longest-first dispatch (xcd_logical_tile); -1: plain order
     float c;              // log2(e) * scale
@@ -88,10 +101,21 @@ __device__ inline void read_stats(const float* st, int hh, float (&x)[16]) {
     }
 }
 
-template <int D, int MODE>
+// Eight values as two bf16 B operands whose sum is them to about 2^-16
+// relative: hi = bf16(x), lo = bf16(x - hi).
+__device__ inline void pack8_split(const f32x16& s, int e0, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        hi[e] = (bf16)s[e0 + e];
+        lo[e] = (bf16)(s[e0 + e] - (float)hi[e]);
+    }
+}
+
+// PREC: the precise variant (DQ: delta from ST; DQ, DK: split dS).
+template <int D, int MODE, bool PREC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_bf16_kernel(BArgs a) {
     using C = BCfg<D, MODE>;
-    constexpr bool ROWQ = MODE == kDQ;          // rows are queries (else keys)
+    constexpr bool ROWQ = MODE == kDQ || MODE == kST;   // rows are queries (else keys)
     __shared__ __attribute__((aligned(1024))) char ring[C::NTL * C::R * C::TILEB];
     // DV, DK: log2 normaliser and delta of the 32 column items of a tile
     // (128 bytes each) per ring slot
@@ -154,21 +178,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             if (MODE != kDV) f1[dc] = *reinterpret_cast<const bf16x8*>(p1 + 16 * dc);
         }
     }
-    // DQ: this row's log2 normaliser and delta = dout . out (also published
-    // for the DK kernel)
+    // DQ, ST: this row's log2 normaliser; DQ: delta = dout . out (also
+    // published for the DK kernel), or (precise) ST's delta
     float Lrow = 0.f, drow = 0.f;
     if (ROWQ) {
         Lrow = a.lse[(int64_t)bh * T + rc] * kLog2e;
-        const bf16* po = a.o + off + (int64_t)rc * D + 8 * hh;
-        float d = 0.f;
+        if (MODE == kDQ && PREC) {
+            drow = a.delta[(int64_t)bh * T + rc];
+        } else if (MODE == kDQ) {
+            const bf16* po = a.o + off + (int64_t)rc * D + 8 * hh;
+            float d = 0.f;
 #pragma unroll
-        for (int dc = 0; dc < D / 16; ++dc) {
-            const bf16x8 ov = *reinterpret_cast<const bf16x8*>(po + 16 * dc);
+            for (int dc = 0; dc < D / 16; ++dc) {
+                const bf16x8 ov = *reinterpret_cast<const bf16x8*>(po + 16 * dc);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) d = fmaf((float)f1[dc][e], (float)ov[e], d);
+                for (int e = 0; e < 8; ++e) d = fmaf((float)f1[dc][e], (float)ov[e], d);
+            }
+            drow = swap_sum(d);
+            if (hh == 0 && ri < T) a.delta[(int64_t)bh * T + ri] = drow;
         }
-        drow = swap_sum(d);
-        if (hh == 0 && ri < T) a.delta[(int64_t)bh * T + ri] = drow;
     }
     // land the register operands before any tile load is counted
     __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
@@ -177,7 +205,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // DQ: 0 = K (read whole and transposed), 1 = V (rows whole)
     // DV: 0 = Q (rows whole), 1 = dout (transposed reads)
     // DK: 0 = Q (read whole and transposed), 1 = dout (rows whole)
-    constexpr int SW0 = MODE == kDV ? kSwzK : kSwzB;   // swizzle of kind 0
+    // ST: 0 = K, 1 = V (rows whole)
+    constexpr int SW0 = MODE == kDV || MODE == kST ? kSwzK : kSwzB;   // swizzle of kind 0
     constexpr int SW1 = MODE == kDV ? kSwzV : kSwzK;   // swizzle of kind 1
     // Ring slot s of kind x (tile t lives in slot (t - t0) mod R); slot numbers
     // are compile-time constants at every call site (the key loop is unrolled
@@ -226,6 +255,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
     const float c = a.c;
+    // masked scores: -inf, or +inf for a negative scale (s * c is then -inf)
+    const float sfill = c >= 0.f ? -__builtin_inff() : __builtin_inff();
+    float zsum = 0.f, ysum = 0.f;               // ST: this lane's share of z and y
 
 #pragma unroll
     for (int i = 0; i < C::PF; ++i) load(t0 + i, i);
@@ -261,30 +293,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     const int col = k0 + 8 * (vv >> 2) + 4 * hh + (vv & 3);
                     const int qq = ROWQ ? ri : col, kk = ROWQ ? col : ri;
                     const bool ok = (unsigned)(qq - kk) < (unsigned)W && qq < T;
-                    s[vv] = ok ? s[vv] : -__builtin_inff();
+                    s[vv] = ok ? s[vv] : sfill;
                 }
             }
-            // P and (DQ, DK) dS
+            // P and (DQ, DK) dS; (ST) the row sums of P and P dP
 #pragma unroll
             for (int vv = 0; vv < 16; ++vv) {
                 const float L = ROWQ ? Lrow : Ls[vv] * kLog2e;
                 const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[vv], c, -L));
-                if (MODE == kDV) s[vv] = p;
-                else s[vv] = p * (dp[vv] - (ROWQ ? drow : Ds[vv]));
+                if (MODE == kST) {
+                    zsum += p;
+                    ysum = __builtin_fmaf(p, dp[vv], ysum);
+                } else if (MODE == kDV) {
+                    s[vv] = p;
+                } else {
+                    s[vv] = p * (dp[vv] - (ROWQ ? drow : Ds[vv]));
+                }
             }
-            const bf16x8 b0 = pack8(s, 0), b1 = pack8(s, 8);
-            // accumulate: (DQ) dQ^T += K^T dS^T, (DV) dV^T += dO^T P, (DK) dK^T += Q^T dS
-            bf16x8 t0f[D / 32], t1f[D / 32];
-            // transposed operand: kind 0 (k or q) for DQ, DK; kind 1 (dout) for DV
-            const char* At = MODE == kDV ? A1 : A0;
-            read_v_chunk<D, MODE == kDV ? kSwzV : kSwzB>(At, 0, lane, t0f);
-            read_v_chunk<D, MODE == kDV ? kSwzV : kSwzB>(At, 1, lane, t1f);
+            if constexpr (MODE != kST) {
+                // accumulate: (DQ) dQ^T += K^T dS^T, (DV) dV^T += dO^T P, (DK) dK^T += Q^T dS
+                bf16x8 t0f[D / 32], t1f[D / 32];
+                // transposed operand: kind 0 (k or q) for DQ, DK; kind 1 (dout) for DV
+                const char* At = MODE == kDV ? A1 : A0;
+                read_v_chunk<D, MODE == kDV ? kSwzV : kSwzB>(At, 0, lane, t0f);
+                read_v_chunk<D, MODE == kDV ? kSwzV : kSwzB>(At, 1, lane, t1f);
+                if constexpr (PREC && MODE != kDV) {
+                    bf16x8 h0, l0, h1, l1;
+                    pack8_split(s, 0, h0, l0);
+                    pack8_split(s, 8, h1, l1);
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t0f[db], b0, acc[db], 0, 0, 0);
+                    for (int db = 0; db < D / 32; ++db) {
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t0f[db], h0, acc[db], 0, 0, 0);
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t0f[db], l0, acc[db], 0, 0, 0);
+                    }
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t1f[db], b1, acc[db], 0, 0, 0);
+                    for (int db = 0; db < D / 32; ++db) {
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t1f[db], h1, acc[db], 0, 0, 0);
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t1f[db], l1, acc[db], 0, 0, 0);
+                    }
+                } else {
+                    const bf16x8 b0 = pack8(s, 0), b1 = pack8(s, 8);
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t0f[db], b0, acc[db], 0, 0, 0);
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(t1f[db], b1, acc[db], 0, 0, 0);
+                }
+            }
         }
         publish();            // tile j + 1 has landed; tile j's slots are free
     };
@@ -304,6 +360,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     __builtin_amdgcn_s_waitcnt(0);   // no LDS load may outlive the workgroup
 
+    if constexpr (MODE == kST) {
+        // each row's z and y over its band (lanes l, l ^ 32 hold halves)
+        const float z = swap_sum(zsum), y = swap_sum(ysum);
+        if (hh == 0 && ri < T) {
+            a.lse_w[(int64_t)bh * T + ri] = (Lrow + __builtin_amdgcn_logf(z)) * kLn2;
+            a.delta[(int64_t)bh * T + ri] = y / z;
+        }
+        return;
+    }
+
     // store (lane holds d = 32 db + 8 g + 4 hh + 0..3 of row item ri)
     const float f = MODE == kDV ? 1.f : a.scale;
     if (ri < T) {
@@ -320,7 +386,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
-template <int D, int MODE>
+template <int D, int MODE, bool PREC>
 hipError_t launch_mode(BArgs a, int64_t B, int64_t H, hipStream_t st) {
     using C = BCfg<D, MODE>;
     a.nrt = (a.T + C::BM - 1) / C::BM;
@@ -331,21 +397,29 @@ hipError_t launch_mode(BArgs a, int64_t B, int64_t H, hipStream_t st) {
     // its end) have shorter bands
     a.nfull = xcd_longest_first_nfull(nblocks, a.nrt, (a.W - 1 + C::BM - 1) / C::BM);
     void* args[] = {(void*)&a};
-    return hipLaunchKernel((const void*)bwd_bf16_kernel<D, MODE>, dim3((unsigned)nblocks),
+    return hipLaunchKernel((const void*)bwd_bf16_kernel<D, MODE, PREC>, dim3((unsigned)nblocks),
                            dim3(256), args, 0, st);
 }
 
-template <int D>
-hipError_t launch_all(BArgs a, bf16* dq, bf16* dk, bf16* dv, int64_t B, int64_t H,
+// lse_ws: workspace row normalisers (precise: written by ST from a.lse)
+template <int D, bool PREC>
+hipError_t launch_all(BArgs a, float* lse_ws, bf16* dq, bf16* dk, bf16* dv, int64_t B, int64_t H,
                       hipStream_t st) {
+    hipError_t e;
+    if constexpr (PREC) {
+        a.lse_w = lse_ws;
+        e = launch_mode<D, kST, true>(a, B, H, st);
+        if (e != hipSuccess) return e;
+        a.lse = lse_ws;
+    }
     a.grad = dq;
-    hipError_t e = launch_mode<D, kDQ>(a, B, H, st);
+    e = launch_mode<D, kDQ, PREC>(a, B, H, st);
     if (e != hipSuccess) return e;
     a.grad = dv;
-    e = launch_mode<D, kDV>(a, B, H, st);
+    e = launch_mode<D, kDV, false>(a, B, H, st);
     if (e != hipSuccess) return e;
     a.grad = dk;
-    return launch_mode<D, kDK>(a, B, H, st);
+    return launch_mode<D, kDK, PREC>(a, B, H, st);
 }
 
 }  // namespace
@@ -355,7 +429,11 @@ bool backward_bf16_supports(const void* q, const void* k, const void* v, const v
     if (D != 64 && D != 128) return false;
     for (const void* p : {q, k, v, o, dout})
         if (((uintptr_t)p & 15) != 0) return false;
-    return scale >= 0.0 && T * D * 2 < ((int64_t)1 << 31);
+    return T * D * 2 < ((int64_t)1 << 31);
+}
+
+bool backward_bf16_precise(double scale, int64_t D) {
+    return fabs(scale) * sqrt((double)D) > kBwdFastSharpness;
 }
 
 hipError_t launch_backward_bf16(const bf16* q, const bf16* k, const bf16* v, const bf16* o,
@@ -383,8 +461,12 @@ hipError_t launch_backward_bf16(const bf16* q, const bf16* k, const bf16* v, con
     a.W = (int)(W < T ? W : T);
     a.c = kLog2e * scale;
     a.scale = scale;
-    if (D == 128) return launch_all<128>(a, dq, dk, dv, B, H, stream);
-    return launch_all<64>(a, dq, dk, dv, B, H, stream);
+    if (backward_bf16_precise(scale, D)) {
+        if (D == 128) return launch_all<128, true>(a, lse, dq, dk, dv, B, H, stream);
+        return launch_all<64, true>(a, lse, dq, dk, dv, B, H, stream);
+    }
+    if (D == 128) return launch_all<128, false>(a, lse, dq, dk, dv, B, H, stream);
+    return launch_all<64, false>(a, lse, dq, dk, dv, B, H, stream);
 }
 
 }  // namespace swa

@@ -54,11 +54,16 @@ hipError_t launch_rowwise_backward(const T* q, const T* k, const T* v, const T* 
                                    hipStream_t stream);
 
 // bf16 matrix-core backward (contiguous [B, H, T, D], D in {64, 128},
-// 16-byte aligned, scale > 0): unless lse_in is given, the forward again for
-// the per-row log-sum-exp (into lse; its output goes to dq); then dq (and
-// delta), dv, dk kernels.
+// 16-byte aligned, any finite scale): unless lse_in is given, the forward
+// again for the per-row log-sum-exp (into lse; its output goes to dq); then
+// dq (and delta), dv, dk kernels.  With |scale| sqrt(D) above
+// kBwdFastSharpness (a softmax sharper than the default scale's) the precise
+// variant runs: a row-statistics kernel first (normalisers into lse, delta),
+// and dS split into two bf16 terms.
+constexpr double kBwdFastSharpness = 1.001;
 bool backward_bf16_supports(const void* q, const void* k, const void* v, const void* o,
                             const void* dout, int64_t T, int64_t D, double scale);
+bool backward_bf16_precise(double scale, int64_t D);
 hipError_t launch_backward_bf16(const bf16* q, const bf16* k, const bf16* v, const bf16* o,
                                 const bf16* dout, bf16* dq, bf16* dk, bf16* dv,
                                 const float* lse_in, float* lse, float* delta, int64_t B,

@@ -197,8 +197,10 @@ __global__ __launch_bounds__(64) void rowwise_chunk_kernel(
 //   dV = P^T dout, dP = dout v^T, dS = P (dP - delta), delta_i = dout_i . out_i
 //   (= sum_j P_ij dP_ij), dQ = dS k * scale, dK = dS^T q * scale.
 // bwd_query_kernel: one wavefront per query row i: the row's log-sum-exp of
-// the scores (one online pass over its band), delta_i, then a second pass
-// accumulating dQ_i.  bwd_key_kernel: one wavefront per key row j, over the
+// the scores and delta_i = sum_j P_ij dP_ij (one online pass over its band,
+// in fp32: taken from a bf16 output, delta would carry that rounding into
+// dS = P (dP - delta) where dP of a dominant key cancels it), then a second
+// pass accumulating dQ_i.  bwd_key_kernel: one wavefront per key row j, over the
 // queries i in [j, j + W - 1] that see it, accumulating dK_j and dV_j from
 // the per-row log-sum-exp and delta the first kernel left in the workspace.
 
@@ -218,13 +220,11 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
     const int64_t base = bh * Tn * D;
     const T* K = k + base;
     const T* V = v + base;
-    float dl = 0.f;
+    (void)o;
     for (int d = lane; d < D; d += 64) {
         qs[d] = to_f32(q[base + i * D + d]);
         ds_[d] = to_f32(dout[base + i * D + d]);
-        dl = fmaf(ds_[d], to_f32(o[base + i * D + d]), dl);
     }
-    dl = wave_sum(dl);
     __syncthreads();
     const int64_t kbeg = i - W + 1 > 0 ? i - W + 1 : 0, kend = i + 1;
     auto score = [&](int64_t j) {
@@ -233,16 +233,27 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
         for (int d = 0; d < D; ++d) acc = fmaf(qs[d], to_f32(kr[d]), acc);
         return acc * scale;
     };
-    // pass 1: log-sum-exp of the row's scores
-    float m = -__builtin_inff(), l = 0.f;
+    auto dprod = [&](int64_t j) {                // dP_ij = dout_i . v_j
+        const T* vr = V + j * D;
+        float dp = 0.f;
+        for (int d = 0; d < D; ++d) dp = fmaf(ds_[d], to_f32(vr[d]), dp);
+        return dp;
+    };
+    // pass 1: log-sum-exp of the row's scores and sum_j e_j dP_ij, both
+    // against the running max
+    float m = -__builtin_inff(), l = 0.f, y = 0.f;
     for (int64_t c0 = kbeg; c0 < kend; c0 += 64) {
         const int64_t j = c0 + lane;
         const float s = j < kend ? score(j) : -__builtin_inff();
         const float mn = fmaxf(m, wave_max(s));      // finite: key c0 is valid
-        l = l * expf(m - mn) + wave_sum(j < kend ? expf(s - mn) : 0.f);
+        const float e = j < kend ? expf(s - mn) : 0.f;
+        const float r = expf(m - mn);
+        l = l * r + wave_sum(e);
+        y = y * r + wave_sum(j < kend ? e * dprod(j) : 0.f);
         m = mn;
     }
     const float L = m + logf(l);
+    const float dl = y / l;
     // pass 2: dQ_i = scale * sum_j dS_ij k_j (lanes own columns d = lane + 64 r)
     float acc[kRowDPL];
 #pragma unroll
@@ -252,10 +263,7 @@ __global__ __launch_bounds__(64) void bwd_query_kernel(
         float dsv = 0.f;
         if (j < kend) {
             const float p = expf(score(j) - L);
-            const T* vr = V + j * D;
-            float dp = 0.f;
-            for (int d = 0; d < D; ++d) dp = fmaf(ds_[d], to_f32(vr[d]), dp);
-            dsv = p * (dp - dl);
+            dsv = p * (dprod(j) - dl);
         }
         ps[lane] = dsv;
         __syncthreads();

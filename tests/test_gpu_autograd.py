@@ -83,6 +83,23 @@ def test_autograd_is_the_explicit_calls_bitwise(dtype, D):
         assert torch.equal(a, b), f"d{name}"
 
 
+@pytest.mark.parametrize("scale", [0.3, -0.2])
+def test_autograd_at_a_sharp_explicit_scale(scale):
+    """D = 128 with an explicit scale well above 1/sqrt(D) (and a negative
+    one) through autograd, against the oracle at the bf16 bar."""
+    T, D, W = 300, 128, 100
+    q, k, v = _leaves((1, 2, T, D), torch.bfloat16, 960)
+    do = si.normal((1, 2, T, D), si.generator(961, DEV), torch.bfloat16, DEV)
+    out = swa.sliding_window_attention(q, k, v, W, scale=scale)
+    out.backward(do)
+    torch.cuda.synchronize()
+    _check(out, so.swa_dense(npy(q), npy(k), npy(v), W, scale=scale), torch.bfloat16, "out")
+    rq, rk, rv = so.swa_backward(npy(q), npy(k), npy(v), W, npy(do), scale=scale)
+    _check(q.grad, rq, torch.bfloat16, "dq")
+    _check(k.grad, rk, torch.bfloat16, "dk")
+    _check(v.grad, rv, torch.bfloat16, "dv")
+
+
 def test_autograd_layouts_and_scale_match_bhtd():
     """[B, T, H, D] and [B, T, D] inputs, with an explicit scale, give the
     [B, H, T, D] path's output and gradients, moved back to their layout."""

@@ -88,6 +88,53 @@ def test_backward_with_explicit_scale(dtype):
     _check(dv, rv, dtype, "dv")
 
 
+@pytest.mark.parametrize("D,T,W,scale", [(128, 300, 100, 0.3), (128, 400, 400, 0.3),
+                                         (128, 600, 256, 0.5), (128, 300, 100, 1.0),
+                                         (64, 256, 64, 0.6), (128, 300, 2, -0.15),
+                                         (64, 300, 2, -0.15), (128, 500, 200, -0.3),
+                                         (64, 257, 300, 0.09)])
+def test_bf16_backward_at_sharp_explicit_scales(D, T, W, scale):
+    """Explicit scales up to about 11x the default 1/sqrt(D), and negative
+    ones (the scale argument of "Implementation: Sliding Window Attention",
+    Step 2): the softmax is sharp, dP of a row's dominant key cancels delta,
+    and the gradients must still meet the unchanged bf16 bar (the matrix-core
+    path then takes each row's normaliser and delta in fp32 and splits dS
+    into two bf16 terms)."""
+    B, H = 1, 2
+    g = si.generator(190 + D + T + W, DEV)
+    q, k, v, do = (si.normal((B, H, T, D), g, torch.bfloat16, DEV) for _ in range(4))
+    dq, dk, dv = _run(q, k, v, W, do, scale=scale)
+    rq, rk, rv = so.swa_backward(npy(q), npy(k), npy(v), W, npy(do), scale=scale)
+    _check(dq, rq, torch.bfloat16, f"dq scale {scale}")
+    _check(dk, rk, torch.bfloat16, f"dk scale {scale}")
+    _check(dv, rv, torch.bfloat16, f"dv scale {scale}")
+
+
+@pytest.mark.parametrize("scale", [0.3, -0.3])
+def test_bf16_sharp_scale_backward_mid_size(scale):
+    """Several workgroups, a ragged tail, with and without the forward's
+    log-sum-exp (bitwise equal), at a sharp explicit scale."""
+    B, H, T, D, W = 2, 2, 1000, 128, 200
+    g = si.generator(199, DEV)
+    q, k, v, do = (si.normal((B, H, T, D), g, torch.bfloat16, DEV) for _ in range(4))
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=DEV)
+    swa.swa_forward_lse(q, k, v, out, lse, W, scale=scale)
+    g1 = [torch.empty_like(q) for _ in range(3)]
+    g2 = [torch.empty_like(q) for _ in range(3)]
+    swa.swa_backward(q, k, v, out, do, *g1, W, scale=scale)
+    swa.swa_backward(q, k, v, out, do, *g2, W, scale=scale, lse=lse)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+    for bb in range(B):
+        rq, rk, rv = so.swa_backward(npy(q[bb]), npy(k[bb]), npy(v[bb]), W, npy(do[bb]),
+                                     scale=scale)
+        _check(g1[0][bb], rq, torch.bfloat16, f"dq[{bb}]")
+        _check(g1[1][bb], rk, torch.bfloat16, f"dk[{bb}]")
+        _check(g1[2][bb], rv, torch.bfloat16, f"dv[{bb}]")
+
+
 def test_key_gradient_support_is_its_window():
     """dk_j, dv_j depend on dout only at queries j .. j + W - 1: changing
     dout elsewhere leaves them bitwise unchanged."""
