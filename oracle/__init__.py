@@ -16,7 +16,13 @@ from .swa_oracle import (  # noqa: F401
     band_mask_max_form,
     swa_dense,
     swa_rows,
+    swa_blocked,
     swa_loop,
+    swa_lse,
+    swa_backward,
+    swa_backward_rows,
+    mha_forward,
+    mha_rows,
     ring_fill,
     ring_slot,
     swa_decode,

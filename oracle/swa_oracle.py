@@ -65,15 +65,17 @@ def _check_window(W) -> int:
     return W
 
 
-def band_mask(T: int, W: int) -> np.ndarray:
+def band_mask(T: int, W: int, rows=None, keys=None) -> np.ndarray:
     """Boolean (T, T) band: ``[i, j]`` is True iff key j is visible to query i.
 
     [P1 step 2: keep (j <= i) & ((i - j) < window_size).  P5 "Build the band by
     index difference": diff = i - j, keep (diff >= 0) & (diff < W).]
+    With ``rows`` and ``keys`` (index sequences) only that (rows, keys) block
+    of it.
     """
     W = _check_window(W)
-    i = np.arange(T)[:, None]
-    j = np.arange(T)[None, :]
+    i = (np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64))[:, None]
+    j = (np.arange(T) if keys is None else np.asarray(keys, dtype=np.int64))[None, :]
     diff = i - j
     return (diff >= 0) & (diff < W)
 
@@ -93,7 +95,7 @@ def band_mask_max_form(T: int, W: int) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
-# Prefill: three independent tiers of the same definition
+# Prefill: four independent tiers of the same definition
 # ----------------------------------------------------------------------------
 
 def _f64(x) -> np.ndarray:
@@ -173,15 +175,58 @@ def swa_rows(q, k, v, W: int, rows: Iterable[int], scale=None):
         if not 0 <= i < T:
             raise IndexError(f"row {i} outside [0, {T})")
         lo = max(0, i - W + 1)
-        kk = K[:, lo:i + 1, :].astype(np.float64)              # (N, n, D)
-        vv = V[:, lo:i + 1, :].astype(np.float64)              # (N, n, Dv)
-        qi = Q[:, i, :].astype(np.float64)                     # (N, D)
+        kk = _f64(K[:, lo:i + 1, :])                           # (N, n, D)
+        vv = _f64(V[:, lo:i + 1, :])                           # (N, n, Dv)
+        qi = _f64(Q[:, i, :])                                  # (N, D)
         s = _scores(np.matmul(kk, qi[:, :, None])[:, :, 0], D, scale)   # (N, n)
         m = s.max(axis=1, keepdims=True)
         e = np.exp(s - m)
         w = e / e.sum(axis=1, keepdims=True)
         out[:, r, :] = np.matmul(w[:, None, :], vv)[:, 0, :]
     return out.reshape(lead + (len(rows), Dv))
+
+
+def swa_blocked(q, k, v, W: int, block: int = 256, scale=None, start: int = 0, stop=None):
+    """The dense recipe of ``swa_dense``, a block of queries at a time.
+
+    Queries [i0, i1) can only see keys [max(0, i0 - W + 1), i1) (the band of
+    ``band_mask``: j <= i and i - j < W), so each block takes that slab of
+    keys only: scores by matmul, the band mask by select, the stable softmax
+    and the weighted sum of v [P1 steps 1-5; P3 Step 2; P5 "Mask before
+    softmax"].  Keys outside the slab are masked for every query of the
+    block, and masked entries add exact zeros, so this is ``swa_dense`` up to
+    summation order, with memory O(block * (W + block)) instead of O(T^2)
+    (P5 "A local mask is not a sparse implementation" names that gap).
+
+    q, k: (..., T, D); v: (..., T, Dv) (any float dtype, upcast exactly).
+    Returns the rows [start, stop) (default: all), (..., stop - start, Dv)
+    float64.
+    """
+    W = _check_window(W)
+    if block < 1:
+        raise ValueError("block must be >= 1")
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
+    T, D = q.shape[-2], q.shape[-1]
+    if k.shape[-2] != T or v.shape[-2] != T or k.shape[-1] != D:
+        raise ValueError("q, k, v must share T, and q, k must share D")
+    stop = T if stop is None else int(stop)
+    start = int(start)
+    if not 0 <= start <= stop <= T:
+        raise IndexError(f"rows [{start}, {stop}) outside [0, {T}]")
+    out = np.empty(q.shape[:-2] + (stop - start, v.shape[-1]), dtype=np.float64)
+    for i0 in range(start, stop, block):
+        i1 = min(stop, i0 + block)
+        lo = max(0, i0 - W + 1)
+        qb = _f64(q[..., i0:i1, :])
+        kb = _f64(k[..., lo:i1, :])
+        vb = _f64(v[..., lo:i1, :])
+        scores = _scores(np.matmul(qb, np.swapaxes(kb, -1, -2)), D, scale)
+        mask = band_mask(T, W, rows=range(i0, i1), keys=range(lo, i1))
+        scores = np.where(mask, scores, -np.inf)
+        row_max = scores.max(axis=-1, keepdims=True)
+        e = np.exp(scores - row_max)
+        out[..., i0 - start:i1 - start, :] = np.matmul(e / e.sum(axis=-1, keepdims=True), vb)
+    return out
 
 
 def swa_loop(q, k, v, W: int):
@@ -223,7 +268,7 @@ def swa_loop(q, k, v, W: int):
 
 
 # ----------------------------------------------------------------------------
-# Decode against a bounded W-slot ring
+# Row log-sum-exp and the backward (the chain rule through the definition)
 # ----------------------------------------------------------------------------
 
 def swa_lse(q, k, W: int, scale=None):
@@ -323,6 +368,10 @@ def swa_backward_rows(q, k, v, W: int, dout, q_rows: Iterable[int], k_rows: Iter
     return dq, dk, dv
 
 
+# ----------------------------------------------------------------------------
+# The multi-head module forward (projections around the attention)
+# ----------------------------------------------------------------------------
+
 def mha_forward(x, wq, bq, wk, bk, wv, bv, wo, bo, H: int, W: int):
     """Multi-head sliding-window self-attention module forward in float64
     [P5 "A complete example with moving averages", the module's __call__].
@@ -385,6 +434,10 @@ def mha_rows(x, wq, bq, wk, bk, wv, bv, wo, bo, H: int, W: int, rows: Iterable[i
         o[:, cols] = swa_rows(qh, k[:, cols], v[:, cols], W, rows)
     return proj(o, wo, bo)
 
+
+# ----------------------------------------------------------------------------
+# Decode against a bounded W-slot ring, and the chunk continuation
+# ----------------------------------------------------------------------------
 
 def ring_slot(p: int, W: int) -> int:
     """Slot of absolute position p in a W-slot ring.
@@ -465,14 +518,12 @@ def swa_decode(q, kring, vring, pos: Sequence[int], W: int):
         if p < 0:
             raise ValueError("pos must be >= 0")
         slots = [w for w, _ in _ring_tokens(p, W)]
-        kk = kring[s][:, slots, :].astype(np.float64)           # (H, n, D)
-        vv = vring[s][:, slots, :].astype(np.float64)           # (H, n, Dv)
-        qs = q[s].astype(np.float64)                            # (H, D)
-        sc = np.matmul(kk, qs[:, :, None])[:, :, 0] / root_d
-        m = sc.max(axis=1, keepdims=True)
-        e = np.exp(sc - m)
-        w = e / e.sum(axis=1, keepdims=True)
-        out[s] = np.matmul(w[:, None, :], vv)[:, 0, :]
+        for h in range(H):
+            kk = _f64(kring[s, h])[slots]                       # (n, D)
+            vv = _f64(vring[s, h])[slots]                       # (n, Dv)
+            sc = (kk @ _f64(q[s, h])) / root_d                  # (n,)
+            e = np.exp(sc - sc.max())
+            out[s, h] = (e / e.sum()) @ vv
     return out
 
 

@@ -22,6 +22,8 @@ from oracle import swa_oracle as so
 TIERS = {
     "dense": lambda q, k, v, W: so.swa_dense(q, k, v, W),
     "rows": lambda q, k, v, W: so.swa_rows(q, k, v, W, range(q.shape[-2])),
+    # small blocks, so the pins' short sequences span several of them
+    "blocked": lambda q, k, v, W: so.swa_blocked(q, k, v, W, block=3),
     "loop": lambda q, k, v, W: so.swa_loop(q, k, v, W),
 }
 
@@ -233,6 +235,47 @@ def test_tiers_agree_random():
         ref = so.swa_dense(q, k, v, W)
         assert np.max(np.abs(so.swa_rows(q, k, v, W, range(T)) - ref)) <= 1e-12
         assert np.max(np.abs(so.swa_loop(q, k, v, W) - ref)) <= 1e-12
+        for block in (1, 2, 5, T, 256):
+            assert np.max(np.abs(so.swa_blocked(q, k, v, W, block=block) - ref)) <= 1e-12
+
+
+@pytest.mark.parametrize("T,W,block,scale", [(300, 64, 64, None), (300, 64, 37, None),
+                                             (257, 300, 50, 0.3), (200, 1, 16, None),
+                                             (129, 128, 128, -0.2)])
+def test_blocked_tier_matches_dense_across_blocks(T, W, block, scale):
+    """Blocks aligned and not aligned with W, W > T, W = 1, a ragged last
+    block and explicit (also negative) scales: the band-blocked tier is the
+    dense recipe to 1e-12."""
+    r = _rng(T + W + block)
+    q, k, v = (r.standard_normal((2, T, 16)) for _ in range(3))
+    ref = so.swa_dense(q, k, v, W, scale=scale)
+    got = so.swa_blocked(q, k, v, W, block=block, scale=scale)
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
+def test_blocked_tier_row_ranges_are_rows_of_the_whole():
+    r = _rng(31)
+    T, W = 300, 70
+    q, k, v = (r.standard_normal((3, T, 8)) for _ in range(3))
+    ref = so.swa_dense(q, k, v, W)
+    for a, b, block in ((0, T, 64), (69, 69 + 64, 64), (100, 101, 16), (250, T, 7), (5, 5, 4)):
+        got = so.swa_blocked(q, k, v, W, block=block, start=a, stop=b)
+        assert got.shape == (3, b - a, 8)
+        assert np.max(np.abs(got - ref[:, a:b]), initial=0.0) <= 1e-12
+
+
+def test_blocked_tier_rejects_bad_arguments():
+    x = np.zeros((4, 2))
+    with pytest.raises(IndexError):
+        so.swa_blocked(x, x, x, 2, start=3, stop=2)
+    with pytest.raises(IndexError):
+        so.swa_blocked(x, x, x, 2, stop=5)
+    with pytest.raises(ValueError):
+        so.swa_blocked(x, x, x, 2, block=0)
+    with pytest.raises(ValueError):
+        so.swa_blocked(x, x, x, 0)
+    with pytest.raises(ValueError):
+        so.swa_blocked(x, np.zeros((5, 2)), x, 2)
 
 
 def test_convexity():
