@@ -14,8 +14,12 @@ Prints one JSON line.  ``value`` is the prefill's useful band TFLOP/s,
 (bytes of the valid slots' k and v plus q and out) is reported beside it.
 Kernel times come from HIP events recorded on the stream the kernels are
 launched on; ms_per_step is the wall time of the K timed steps between two
-device synchronisations.  The ``cpu_baseline`` leg times the fp64 CPU oracle
-on a bounded sample of the same prefill workload (one BLAS thread).
+device synchronisations.  The two other prefill workloads (a batched
+narrow band, B=8 T=4096 W=1024, and a long context, T=65536 W=4096) are
+timed after the steps, each with its own roofline fraction.  The
+``cpu_baseline`` leg times the fp64 CPU oracle's band-blocked tier on a
+bounded sample of the T=8192 layer's query blocks, on all the host cores the
+process may use (multithreaded BLAS for the matmuls).
 """
 
 from __future__ import annotations
@@ -33,6 +37,12 @@ sys.path.insert(0, ROOT)
 METRIC = ("band attention TFLOP/s & % MFMA peak (prefill); KV GB/s & % HBM peak (decode)")
 PREFILL = "prefill_bf16_b1_h32_t8192_d128_w4096"
 DECODE = "decode_bf16_s256_h32_d128_w4096"
+# the other prefill workloads, timed after the steps
+PREFILL_MORE = {"prefill_narrow": "prefill_bf16_b8_h32_t4096_d128_w1024",
+                "prefill_long": "prefill_bf16_b1_h32_t65536_d128_w4096"}
+# MI355X: 256 compute units; dense bf16 matrix work per CU and clock
+CUS = 256
+BF16_FLOP_PER_CLK_CU = 4096
 # MI355X published peaks: dense bf16 matrix throughput and HBM3E bandwidth.
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
@@ -60,6 +70,30 @@ def decode_bytes(S, H, D, n, elem=2) -> int:
     return 2 * S * H * n * D * elem + 2 * S * H * D * elem
 
 
+def stats_ms(ms):
+    """mean, median and min of a list of per-launch milliseconds."""
+    xs = sorted(ms)
+    n = len(xs)
+    med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    return {"kernel_ms_mean": sum(xs) / n, "kernel_ms_median": med, "kernel_ms_min": xs[0]}
+
+
+def time_each(fn, stream, reps: int, warmup: int = 5):
+    """Per-call milliseconds of reps back-to-back fn() calls, each bracketed
+    by HIP events on the launching stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
 def time_launches(fn, stream, reps: int, warmup: int = 10) -> float:
     """Mean ms of one fn() call over reps back-to-back calls (HIP events on
     the launching stream)."""
@@ -84,42 +118,83 @@ def source_sha(paths) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(name: str, sha: str):
-    """HBM bytes per launch from a committed PMC summary, if it was taken on
-    this exact kernel source (else None)."""
+def read_profile_value(name: str, sha: str, key: str):
+    """A figure from a committed PMC summary, if it was taken on this exact
+    kernel source (else None)."""
     path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
     kv = {}
     for ln in open(path):
         if ":" in ln and not ln.startswith("#"):
-            key, val = ln.split(":", 1)
-            kv[key.strip()] = val.strip()
-    if kv.get("kernel_source_sha") != sha or "hbm_bytes_per_launch" not in kv:
+            k, val = ln.split(":", 1)
+            kv[k.strip()] = val.strip()
+    if kv.get("kernel_source_sha") != sha or key not in kv:
         return None
-    return float(kv["hbm_bytes_per_launch"])
+    return float(kv[key])
 
 
-def cpu_baseline_prefill(q, k, v, W, seconds: float):
-    """Time the fp64 oracle's per-row tier on rows of the prefill workload
-    until about ``seconds`` have passed; returns useful TFLOP/s."""
+def read_traffic(name: str, sha: str):
+    """HBM bytes per launch from a committed PMC summary, if it was taken on
+    this exact kernel source (else None)."""
+    return read_profile_value(name, sha, "hbm_bytes_per_launch")
+
+
+def clock_fields(tflops: float, name: str, sha: str):
+    """The sustained shader clock a committed counter summary measured for
+    this kernel source (busy cycles over the dispatch time), and the
+    fraction of the dense bf16 peak at that clock."""
+    mhz = read_profile_value(name, sha, "sclk_mhz")
+    if mhz is None:
+        return {"clock_mhz": None, "peak_at_clock": None, "frac_at_clock": None}
+    peak = CUS * BF16_FLOP_PER_CLK_CU * mhz * 1e6 / 1e12
+    return {"clock_mhz": mhz, "peak_at_clock": peak, "frac_at_clock": tflops / peak}
+
+
+def host_info():
+    """Cores this process may run on, the BLAS library's thread count and the
+    CPU model."""
+    from threadpoolctl import threadpool_info
+    cores = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        cores = min(cores, int(env))
+    model = ""
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = [f"{d.get('internal_api')}:{d.get('num_threads')}" for d in threadpool_info()
+            if d.get("user_api") == "blas"]
+    return cores, model, blas
+
+
+def cpu_baseline_prefill(q, k, v, W, seconds: float, block: int = 256):
+    """Time the fp64 oracle's band-blocked tier on the prefill workload's
+    query blocks, in random order, until all are done or about ``seconds``
+    have passed; returns useful TFLOP/s (each block's band pairs)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle import swa_oracle as so
 
-    qh = q[0].float().cpu().numpy()
-    kh = k[0].float().cpu().numpy()
-    vh = v[0].float().cpu().numpy()
+    # exact fp64 copies of the inputs, staged before the timed region
+    qh, kh, vh = (x[0].double().cpu().numpy() for x in (q, k, v))
     H, T, D = qh.shape
+    cores, model, _ = host_info()
     rng = np.random.default_rng(0)
-    rows = rng.integers(W, T, size=4096)          # full-window rows, the steady state
+    starts = rng.permutation(np.arange(0, T, block))
     flops = 0
     done = 0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=cores, user_api="blas"):
+        _, _, blas = host_info()
         t0 = time.perf_counter()
-        for i in rows:
-            so.swa_rows(qh, kh, vh, W, [int(i)])
-            flops += 4 * H * D * min(int(i) + 1, W)
+        for i0 in starts:
+            i1 = min(T, int(i0) + block)
+            so.swa_blocked(qh, kh, vh, W, block=block, start=int(i0), stop=i1)
+            flops += 4 * H * D * (band_pairs(i1, W) - band_pairs(int(i0), W))
             done += 1
             if time.perf_counter() - t0 >= seconds:
                 break
@@ -127,10 +202,15 @@ def cpu_baseline_prefill(q, k, v, W, seconds: float):
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"{done} random full-window rows (all {H} heads) of the {PREFILL} layer, "
-                  f"fp64 per-row oracle tier, one BLAS thread, {dt:.1f} s",
+        "sample": (f"the whole {PREFILL} layer" if done == len(starts) else
+                   f"{done} of the {len(starts)} blocks of {block} queries (all {H} heads, "
+                   f"random order) of the {PREFILL} layer") +
+                  f", fp64 band-blocked oracle tier, {dt:.1f} s",
+        "blas_threads": blas,
+        "cpu_model": model,
+        "affinity_cores": len(os.sched_getaffinity(0)),
     }
 
 
@@ -146,7 +226,9 @@ def main() -> int:
     ap.add_argument("--workload", default=PREFILL,
                     help="prefill workload for --only prefill (the default step always uses the "
                          "T=8192/W=4096 layer)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-more-prefill", action="store_true",
+                    help="skip the narrow-band and long-context prefill lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -244,13 +326,14 @@ def main() -> int:
     }
     if do_p:
         flops = prefill_flops(wp.B, wp.H, wp.T, wp.D, wp.W)
-        pm = sum(p_ms) / len(p_ms)
+        pst = stats_ms(p_ms)
+        pm = pst["kernel_ms_mean"]
         tflops = flops / (pm * 1e-3) / 1e12
         sha = source_sha(PREFILL_SOURCES)
         res["value"] = tflops
         res["config"]["prefill"] = {"B": wp.B, "H": wp.H, "T": wp.T, "D": wp.D, "W": wp.W,
-                                    "useful_flop_per_launch": flops, "kernel_ms_mean": pm,
-                                    "kernel_ms_min": min(p_ms)}
+                                    "useful_flop_per_launch": flops, **pst,
+                                    "TFLOPs_median": flops / (pst["kernel_ms_median"] * 1e-3) / 1e12}
         if do_d:
             # context: in the step each prefill follows a decode that streams
             # 16 GiB through the caches; launched back to back it starts warm
@@ -270,16 +353,19 @@ def main() -> int:
         res["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": tflops / PEAK_BF16_TFLOPS,
                            "traffic": read_traffic("prefill_bf16_t8192_w4096_traffic.txt", sha),
-                           "kernel": "prefill_bf16_kernel<128,4>", "kernel_source_sha": sha}
+                           "kernel": "prefill_bf16_kernel<128,4>", "kernel_source_sha": sha,
+                           **clock_fields(tflops, "prefill_bf16_t8192_w4096_counters.txt", sha)}
         if do_d:
             res["roofline"]["vendor_gemm_reference"] = vendor_ref
     if do_d:
         nbytes = decode_bytes(wd.S, wd.H, wd.D, wd.W)
-        dm = sum(d_ms) / len(d_ms)
+        dst = stats_ms(d_ms)
+        dm = dst["kernel_ms_mean"]
         gbs = nbytes / (dm * 1e-3) / 1e9
         sha = source_sha(DECODE_SOURCES)
         res["decode"] = {
-            "value": gbs, "unit": "GB/s", "kernel_ms_mean": dm, "kernel_ms_min": min(d_ms),
+            "value": gbs, "unit": "GB/s", **dst,
+            "GBs_median": nbytes / (dst["kernel_ms_median"] * 1e-3) / 1e9,
             "S": wd.S, "H": wd.H, "D": wd.D, "W": wd.W, "bytes_per_launch": nbytes,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS,
@@ -377,6 +463,30 @@ def main() -> int:
                                    "forward rerun (absent given lse) and the recomputed S "
                                    "products are not"}
         del dob, gq, gk, gv, wsb, lse
+    if do_p and args.only == "all" and not args.no_more_prefill:
+        # The other prefill workloads, each timed launch by launch (HIP events
+        # on the stream) after 5 warm-up launches.
+        sha = source_sha(PREFILL_SOURCES)
+        for key, name in PREFILL_MORE.items():
+            w = si.WORKLOADS[name]
+            qm, km, vm = si.workload_qkv(w, dev)
+            om = torch.empty_like(qm)
+            ms = time_each(lambda: swa.swa_forward(qm, km, vm, om, w.W, stream=stream), stream,
+                           20, 5)
+            st = stats_ms(ms)
+            fl = prefill_flops(w.B, w.H, w.T, w.D, w.W)
+            tf = fl / (st["kernel_ms_mean"] * 1e-3) / 1e12
+            res[key] = {"workload": name, "B": w.B, "H": w.H, "T": w.T, "D": w.D, "W": w.W,
+                        "useful_flop_per_launch": fl, **st, "TFLOPs": tf,
+                        "TFLOPs_median": fl / (st["kernel_ms_median"] * 1e-3) / 1e12,
+                        "roofline": {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                                     "traffic": read_traffic(f"{name}_traffic.txt", sha),
+                                     "kernel": "prefill_bf16_kernel<128,4>",
+                                     "kernel_source_sha": sha,
+                                     **clock_fields(tf, f"{name}_counters.txt", sha)}}
+            del qm, km, vm, om
+        print("# more prefill workloads done", file=sys.stderr, flush=True)
     if do_p and args.only == "all" and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(q, k, v, wp.W, args.cpu_seconds)
     res["device"] = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
