@@ -19,25 +19,24 @@
 // rebuilt weights sum to one) and takes delta_i = y_i / z_i, and DQ and DK
 // feed dS to the matrix cores as two bf16 terms (hi + lo) instead of one.
 //
-// The kernels share one skeleton: a workgroup of 4 wavefronts owns 128
-// "row" items (32 per wavefront) and walks 32-item "column" tiles of its band
-// through an LDS ring (HBM -> LDS buffer loads, 3 tiles ahead, one barrier
-// per tile).  Per wavefront and tile:
-//   DQ  rows = queries, columns = keys:  S^T = K Q^T, dP^T = V dO^T,
-//       dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T      (24 MFMAs)
-//   DV  rows = keys, columns = queries:  S = Q K^T, dV^T += dO^T P   (16)
-//   DK  rows = keys, columns = queries:  S = Q K^T, dP = dO V^T,
-//       dS = P (dP - delta), dK^T += Q^T dS                           (24)
-//   ST  rows = queries, columns = keys:  S^T = K Q^T, dP^T = V dO^T,
-//       z += P, y += P dP                                             (16)
-// (DQ and DK issue 8 more with the split dS.)
+// Two kernels.  The query-row kernel (DQ, and ST for the precise variant):
+// a workgroup of 4 wavefronts owns 128 queries (32 per wavefront) and walks
+// the 32-key tiles of its band through an LDS ring (HBM -> LDS buffer loads,
+// 3 tiles ahead, one barrier per tile).  Per wavefront and tile:
+//   DQ  S^T = K Q^T, dP^T = V dO^T, dS^T = P^T (dP^T - delta),
+//       dQ^T += K^T dS^T                                  (24 MFMAs)
+//   ST  S^T = K Q^T, dP^T = V dO^T, z += P, y += P dP     (16)
+// (DQ issues 8 more with the split dS.)  dV and dK come from one key-row
+// kernel, bwd_kv_kernel (below), on 16x16x32 MFMAs: S, dP, dV and dK in
+// 32 MFMAs of half the size per 16 keys and 32 queries, so it rebuilds S
+// once for both gradients.
 // The accumulator layout of v_mfma_f32_32x32x16_bf16 gives lane l column
 // l % 32 (a row item) and 16 column-tile items 8 (v/4) + 4 (l/32) + v%4, so
 // the packed probabilities feed the next product's B operand directly, as in
 // the forward kernel, and transposed operands come from ds_read_b64_tr_b16.
-// DQ reads its k tile, and DK its q tile, both whole and transposed, from one
-// LDS copy laid out with the bswz swizzle, which serves both reads without
-// bank conflicts.
+// DQ reads its k tile, and the key-row kernel its q and dout tiles, both
+// whole and transposed, from one LDS copy laid out with the bswz swizzle,
+// which serves both reads without bank conflicts.
 
 #include "swa_mfma.h"
 
@@ -46,21 +45,19 @@
 namespace swa {
 namespace {
 
-enum Mode { kDQ = 0, kDV = 1, kDK = 2, kST = 3 };
+enum Mode { kDQ = 0, kST = 1 };
 
 template <int D, int MODE>
 struct BCfg {
     static constexpr int NW = 4;                // wavefronts per workgroup
-    static constexpr int BM = 32 * NW;          // row items per workgroup
-    static constexpr int BN = 32;               // column items per tile
+    static constexpr int BM = 32 * NW;          // query rows per workgroup
+    static constexpr int BN = 32;               // keys per tile
     static constexpr int TILEB = BN * 2 * D;    // bytes per tile
-    static constexpr int NTL = 2;               // tile kinds per step
+    static constexpr int NTL = 2;               // tile kinds per step (k, v)
     static constexpr int PF = 3;                // tiles in flight ahead
     static constexpr int R = PF + 1;            // ring slots per tile kind
     static constexpr int NLD_W = TILEB / 1024 / NW;
-    // loads per wave per tile: the tiles, plus (DV, DK) one for the column
-    // items' statistics
-    static constexpr int NLD_T = NTL * NLD_W + (MODE == kDV ? 1 : MODE == kDK ? 2 : 0);
+    static constexpr int NLD_T = NTL * NLD_W;   // loads per wave per tile
     static constexpr int VM_WAIT = (PF - 1) * NLD_T;
     static_assert(D == 64 || D == 128, "head size");
     static_assert(VM_WAIT < 64, "vmcnt range");
@@ -72,7 +69,8 @@ struct BArgs {
     const bf16* v;
     const bf16* o;        // forward output (DQ: delta)
     const bf16* dout;
-    bf16* grad;           // dq, dk or dv, [B, H, T, D]
+    bf16* grad;           // DQ: dq; key kernel: dv   ([B, H, T, D])
+    bf16* grad2;          // key kernel: dk
     const float* lse;     // [B * H * T] log-sum-exp of the scaled scores (forward)
     float* delta;         // [B * H * T] dout . out (written by DQ; precise: by ST)
     float* lse_w;         // ST: [B * H * T] log normaliser of the rebuilt weights
@@ -90,17 +88,6 @@ __device__ inline bf16x8 pack8(const f32x16& s, int e0) {
     return p;
 }
 
-// Per-row statistics of the 16 column items a lane holds in an accumulator
-// (items 8 g + 4 hh + 0..3 of a tile), from the tile's 32 values in LDS.
-__device__ inline void read_stats(const float* st, int hh, float (&x)[16]) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const f32x4 w = *reinterpret_cast<const f32x4*>(st + 8 * g + 4 * hh);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[4 * g + e] = w[e];
-    }
-}
-
 // Eight values as two bf16 B operands whose sum is them to about 2^-16
 // relative: hi = bf16(x), lo = bf16(x - hi).
 __device__ inline void pack8_split(const f32x16& s, int e0, bf16x8& hi, bf16x8& lo) {
@@ -111,15 +98,12 @@ __device__ inline void pack8_split(const f32x16& s, int e0, bf16x8& hi, bf16x8& 
     }
 }
 
-// PREC: the precise variant (DQ: delta from ST; DQ, DK: split dS).
+// Query-row kernel (rows = queries, columns = keys): DQ, or ST (the row
+// statistics of the precise variant).  PREC: DQ takes ST's delta and splits dS.
 template <int D, int MODE, bool PREC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_bf16_kernel(BArgs a) {
     using C = BCfg<D, MODE>;
-    constexpr bool ROWQ = MODE == kDQ || MODE == kST;   // rows are queries (else keys)
     __shared__ __attribute__((aligned(1024))) char ring[C::NTL * C::R * C::TILEB];
-    // DV, DK: log2 normaliser and delta of the 32 column items of a tile
-    // (128 bytes each) per ring slot
-    __shared__ __attribute__((aligned(16))) float stats[C::R][64];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
@@ -129,8 +113,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int logical = xcd_logical_tile(bid, a.nblocks, a.remap, a.nrt, a.nfull);
     const int bh = logical / a.nrt;
     const int rti = logical - bh * a.nrt;
-    // longest bands first: the last query tiles (DQ), the first key tiles (DV, DK)
-    const int rt = ROWQ ? a.nrt - 1 - rti : rti;
+    const int rt = a.nrt - 1 - rti;             // longest bands (the last query tiles) first
     const int T = a.T, W = a.W;
     const int64_t off = (int64_t)bh * T * D;
     const bf16* Q = a.q + off;
@@ -138,109 +121,73 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bf16* V = a.v + off;
     const bf16* DO = a.dout + off;
 
-    const int r0 = rt * C::BM;                  // workgroup's row items [r0, r0 + BM)
-    const int rw0 = r0 + 32 * wave;             // this wave's rows
-    const int ri = rw0 + lr;                    // this lane's row item
-    // column band of the workgroup and of this wave
-    int c_lo, c_hi, w_lo, w_hi;
-    if (ROWQ) {                                 // keys j with 0 <= i - j < W
-        c_lo = max(r0 - W + 1, 0);
-        c_hi = min(r0 + C::BM, T);
-        w_lo = max(rw0 - W + 1, 0);
-        w_hi = min(rw0 + 32, T);
-    } else {                                    // queries i with 0 <= i - j < W
-        c_lo = r0;
-        c_hi = min(r0 + C::BM - 1 + W, T);
-        w_lo = rw0;
-        w_hi = min(rw0 + 31 + W, T);
-    }
+    const int r0 = rt * C::BM;                  // workgroup's queries [r0, r0 + BM)
+    const int rw0 = r0 + 32 * wave;             // this wave's queries
+    const int ri = rw0 + lr;                    // this lane's query
+    // keys j with 0 <= i - j < W, for the workgroup and for this wave
+    const int c_lo = max(r0 - W + 1, 0), c_hi = min(r0 + C::BM, T);
+    const int w_lo = max(rw0 - W + 1, 0), w_hi = min(rw0 + 32, T);
     const int t0 = c_lo / C::BN, t1 = (c_hi + C::BN - 1) / C::BN;
     const bool live = rw0 < T;
     const int wt0 = live ? w_lo / C::BN : t1, wt1 = live ? (w_hi + C::BN - 1) / C::BN : t1;
     auto needs = [&](int t) { return t >= wt0 && t < wt1; };
-    // every (row, column) pair of the tile inside the band and the sequence
+    // every (query, key) pair of the tile inside the band
     auto interior = [&](int t) {
         const int k0 = t * C::BN;
-        if (ROWQ) return k0 + 31 <= rw0 && rw0 + 31 - k0 < W;
-        return k0 >= rw0 + 31 && k0 + 31 - rw0 < W && k0 + 31 < T;
+        return k0 + 31 <= rw0 && rw0 + 31 - k0 < W;
     };
 
-    // register operands: the wave's 32 row items (B operands of the first
-    // products), clamped to the last row past the end
+    // register operands: the wave's 32 q and dout rows (B operands of S^T and
+    // dP^T), clamped to the last row past the end
     const int rc = min(ri, T - 1);
-    bf16x8 f0[D / 16], f1[D / 16];              // DQ: q, dout rows; DV/DK: k, v rows
+    bf16x8 f0[D / 16], f1[D / 16];
     {
-        const bf16* p0 = (ROWQ ? Q : K) + (int64_t)rc * D + 8 * hh;
-        const bf16* p1 = (ROWQ ? DO : V) + (int64_t)rc * D + 8 * hh;
+        const bf16* p0 = Q + (int64_t)rc * D + 8 * hh;
+        const bf16* p1 = DO + (int64_t)rc * D + 8 * hh;
 #pragma unroll
         for (int dc = 0; dc < D / 16; ++dc) {
             f0[dc] = *reinterpret_cast<const bf16x8*>(p0 + 16 * dc);
-            if (MODE != kDV) f1[dc] = *reinterpret_cast<const bf16x8*>(p1 + 16 * dc);
+            f1[dc] = *reinterpret_cast<const bf16x8*>(p1 + 16 * dc);
         }
     }
-    // DQ, ST: this row's log2 normaliser; DQ: delta = dout . out (also
-    // published for the DK kernel), or (precise) ST's delta
-    float Lrow = 0.f, drow = 0.f;
-    if (ROWQ) {
-        Lrow = a.lse[(int64_t)bh * T + rc] * kLog2e;
-        if (MODE == kDQ && PREC) {
-            drow = a.delta[(int64_t)bh * T + rc];
-        } else if (MODE == kDQ) {
-            const bf16* po = a.o + off + (int64_t)rc * D + 8 * hh;
-            float d = 0.f;
+    // this row's log2 normaliser; DQ: delta = dout . out (also published for
+    // the key kernel), or (precise) ST's delta
+    const float Lrow = a.lse[(int64_t)bh * T + rc] * kLog2e;
+    float drow = 0.f;
+    if (MODE == kDQ && PREC) {
+        drow = a.delta[(int64_t)bh * T + rc];
+    } else if (MODE == kDQ) {
+        const bf16* po = a.o + off + (int64_t)rc * D + 8 * hh;
+        float d = 0.f;
 #pragma unroll
-            for (int dc = 0; dc < D / 16; ++dc) {
-                const bf16x8 ov = *reinterpret_cast<const bf16x8*>(po + 16 * dc);
+        for (int dc = 0; dc < D / 16; ++dc) {
+            const bf16x8 ov = *reinterpret_cast<const bf16x8*>(po + 16 * dc);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) d = fmaf((float)f1[dc][e], (float)ov[e], d);
-            }
-            drow = swap_sum(d);
-            if (hh == 0 && ri < T) a.delta[(int64_t)bh * T + ri] = drow;
+            for (int e = 0; e < 8; ++e) d = fmaf((float)f1[dc][e], (float)ov[e], d);
         }
+        drow = swap_sum(d);
+        if (hh == 0 && ri < T) a.delta[(int64_t)bh * T + ri] = drow;
     }
     // land the register operands before any tile load is counted
     __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
 
     // ---- tile ring: kind x of tile t in slot x * R + (t - t0) % R
-    // DQ: 0 = K (read whole and transposed), 1 = V (rows whole)
-    // DV: 0 = Q (rows whole), 1 = dout (transposed reads)
-    // DK: 0 = Q (read whole and transposed), 1 = dout (rows whole)
-    // ST: 0 = K, 1 = V (rows whole)
-    constexpr int SW0 = MODE == kDV || MODE == kST ? kSwzK : kSwzB;   // swizzle of kind 0
-    constexpr int SW1 = MODE == kDV ? kSwzV : kSwzK;   // swizzle of kind 1
+    // 0 = K (DQ: read whole and transposed; ST: whole), 1 = V (rows whole)
+    constexpr int SW0 = MODE == kST ? kSwzK : kSwzB;   // swizzle of kind 0
     // Ring slot s of kind x (tile t lives in slot (t - t0) mod R); slot numbers
     // are compile-time constants at every call site (the key loop is unrolled
     // over the R = 4 slots), so LDS addresses carry them as immediates.
     static_assert(C::R == 4, "the loop is unrolled over 4 ring slots");
     auto slot = [&](int x, int s) { return ring + (x * C::R + s % C::R) * C::TILEB; };
-    const bf16* src[2];
-    src[0] = ROWQ ? K : Q;
-    src[1] = ROWQ ? V : DO;
     uint32_t off0[C::NLD_W], off1[C::NLD_W];
     tile_offsets<D, C::NW, SW0>(off0, wave, lane, 2 * D);
-    tile_offsets<D, C::NW, SW1>(off1, wave, lane, 2 * D);
+    tile_offsets<D, C::NW, kSwzK>(off1, wave, lane, 2 * D);
     const int slab = T * D * 2;
-    // DV, DK: lanes 0..7 of every wave copy the tile's 32 log2 normalisers
-    // and (DK) lanes 8..15 its 32 deltas into the slot's stats (all waves
-    // write the same bytes); past the sequence end the buffer range check
-    // gives 0.
-    const __amdgpu_buffer_rsrc_t lse_rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(a.lse) + (int64_t)bh * T, 0, T * 4, 0x00020000);
-    const __amdgpu_buffer_rsrc_t del_rs = __builtin_amdgcn_make_buffer_rsrc(
-        a.delta + (int64_t)bh * T, 0, T * 4, 0x00020000);
     auto load = [&](int t, int s) {   // tile t into ring slot s
         const int tt = min(t, t1 - 1);
         const int boff = tt * C::TILEB;
-#pragma unroll
-        for (int x = 0; x < C::NTL; ++x)
-            dma_tile(rows_rsrc(src[x], boff, slab), lds_addr(slot(x, s)), wave, x == 1 ? off1 : off0);
-        if (!ROWQ) {
-            const uint32_t sbase = lds_addr(&stats[s % C::R][0]);
-            // lane l < 8 (l < 16) fetches items 4 (l % 8) .. + 3 of L (delta)
-            const uint32_t soff = (tt * C::BN + 4 * (lane & 7)) * 4;
-            if (lane < 8) lds_load16(lse_rs, sbase, soff);
-            if (MODE == kDK && lane >= 8 && lane < 16) lds_load16(del_rs, sbase, soff);
-        }
+        dma_tile(rows_rsrc(K, boff, slab), lds_addr(slot(0, s)), wave, off0);
+        dma_tile(rows_rsrc(V, boff, slab), lds_addr(slot(1, s)), wave, off1);
     };
     // Wait until this wave's loads of the next tile have landed (at most the
     // PF - 1 newer tiles' loads in flight) and its LDS reads are done, then
@@ -262,7 +209,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int i = 0; i < C::PF; ++i) load(t0 + i, i);
     publish();                // tile t0 has landed
-    // one column tile j, in ring slot KS = (j - t0) mod 4
+    // one key tile j, in ring slot KS = (j - t0) mod 4
     auto step = [&](auto ks, int j) {
         constexpr int KS = decltype(ks)::value;
         load(j + C::PF, KS + C::PF);   // into the slot of tile j - 1, released by the last barrier
@@ -270,54 +217,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int k0 = j * C::BN;
             const char* A0 = slot(0, KS);
             const char* A1 = slot(1, KS);
-            float Ls[16], Ds[16];
-            if (!ROWQ) {
-                const float* st = &stats[KS][0];
-                read_stats(st, hh, Ls);
-                if (MODE == kDK) read_stats(st + 32, hh, Ds);
-            }
-            // first products: scores and, for DQ / DK, dP
+            // S^T = K Q^T and dP^T = V dO^T
             f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
             for (int dc = 0; dc < D / 16; ++dc) {
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row_frag<D, SW0>(A0, lr, hh, dc),
                                                             f0[dc], s, 0, 0, 0);
-                if (MODE != kDV)
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        read_row_frag<D, kSwzK>(A1, lr, hh, dc), f1[dc], dp, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row_frag<D, kSwzK>(A1, lr, hh, dc),
+                                                             f1[dc], dp, 0, 0, 0);
             }
-            // band mask: row item ri against column items k0 + 8 (v/4) + 4 hh + v%4
+            // band mask: query ri against keys k0 + 8 (v/4) + 4 hh + v%4
             if (!interior(j)) {
 #pragma unroll
                 for (int vv = 0; vv < 16; ++vv) {
                     const int col = k0 + 8 * (vv >> 2) + 4 * hh + (vv & 3);
-                    const int qq = ROWQ ? ri : col, kk = ROWQ ? col : ri;
-                    const bool ok = (unsigned)(qq - kk) < (unsigned)W && qq < T;
+                    const bool ok = (unsigned)(ri - col) < (unsigned)W && ri < T;
                     s[vv] = ok ? s[vv] : sfill;
                 }
             }
-            // P and (DQ, DK) dS; (ST) the row sums of P and P dP
+            // P and (DQ) dS; (ST) the row sums of P and P dP
 #pragma unroll
             for (int vv = 0; vv < 16; ++vv) {
-                const float L = ROWQ ? Lrow : Ls[vv] * kLog2e;
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[vv], c, -L));
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[vv], c, -Lrow));
                 if (MODE == kST) {
                     zsum += p;
                     ysum = __builtin_fmaf(p, dp[vv], ysum);
-                } else if (MODE == kDV) {
-                    s[vv] = p;
                 } else {
-                    s[vv] = p * (dp[vv] - (ROWQ ? drow : Ds[vv]));
+                    s[vv] = p * (dp[vv] - drow);
                 }
             }
-            if constexpr (MODE != kST) {
-                // accumulate: (DQ) dQ^T += K^T dS^T, (DV) dV^T += dO^T P, (DK) dK^T += Q^T dS
+            if constexpr (MODE == kDQ) {
+                // dQ^T += K^T dS^T (k transposed from the same LDS copy)
                 bf16x8 t0f[D / 32], t1f[D / 32];
-                // transposed operand: kind 0 (k or q) for DQ, DK; kind 1 (dout) for DV
-                const char* At = MODE == kDV ? A1 : A0;
-                read_v_chunk<D, MODE == kDV ? kSwzV : kSwzB>(At, 0, lane, t0f);
-                read_v_chunk<D, MODE == kDV ? kSwzV : kSwzB>(At, 1, lane, t1f);
-                if constexpr (PREC && MODE != kDV) {
+                read_v_chunk<D, kSwzB>(A0, 0, lane, t0f);
+                read_v_chunk<D, kSwzB>(A0, 1, lane, t1f);
+                if constexpr (PREC) {
                     bf16x8 h0, l0, h1, l1;
                     pack8_split(s, 0, h0, l0);
                     pack8_split(s, 8, h1, l1);
@@ -370,8 +304,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         return;
     }
 
-    // store (lane holds d = 32 db + 8 g + 4 hh + 0..3 of row item ri)
-    const float f = MODE == kDV ? 1.f : a.scale;
+    // store (lane holds d = 32 db + 8 g + 4 hh + 0..3 of query ri)
     if (ri < T) {
         bf16* row = a.grad + off + (int64_t)ri * D;
 #pragma unroll
@@ -380,10 +313,259 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int g = 0; g < 4; ++g) {
                 bf16x4 w;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * g + e] * f);
+                for (int e = 0; e < 4; ++e) w[e] = (bf16)(acc[db][4 * g + e] * a.scale);
                 *reinterpret_cast<bf16x4*>(row + 32 * db + 8 * g + 4 * hh) = w;
             }
     }
+}
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// Key-row kernel computing dV and dK together (rows = keys, columns =
+// queries), 16 key rows per wavefront on v_mfma_f32_16x16x32_bf16 so that
+// both accumulators fit beside the operands at two wavefronts per SIMD.  Per
+// wavefront and 32-query tile (two 16-query blocks):
+//   S^T = Q K^T, dP^T = dO V^T           (2 x D/32 MFMAs each; k, v rows of
+//                                          the wavefront stay in registers)
+//   P^T = exp2(S^T c - L), dS^T = P^T (dP^T - delta)
+//   dV^T += dO^T P^T, dK^T += Q^T dS^T    (D/16 MFMAs each, the transposed
+//                                          operands from ds_read_b64_tr_b16;
+//                                          the precise variant adds D/16 for
+//                                          the lo term of dS)
+// 16x16x32 operand layout: lane l gives row (or column) l % 16 and the eight
+// contraction items 8 (l / 16) .. + 7; the accumulator gives lane l column
+// l % 16 and rows 4 (l / 16) .. + 3.  A lane of group g = l / 16 thus holds
+// P^T, dS^T for its key and the queries 4g .. 4g+3 of both 16-query blocks,
+// which is the (permuted) contraction order of the B operand; the
+// transposed A operands are read in that same query order.  At 162 registers
+// three wavefronts fit a SIMD, so three workgroups share a CU, with a
+// three-slot ring (tiles two steps ahead) to fit their LDS.
+template <int D, bool PREC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void bwd_kv_kernel(BArgs a) {
+    constexpr int NW = 4, RW = 16, BM = NW * RW, BN = 32;
+    constexpr int TILEB = BN * 2 * D;
+    constexpr int PF = 2, R = PF + 1;
+    constexpr int NLD_W = TILEB / 1024 / NW;
+    constexpr int NLD_T = 2 * NLD_W + 2;            // Q, dout tiles; L and delta
+    constexpr int VM_WAIT = (PF - 1) * NLD_T;
+    constexpr int KC = D / 32;                      // 32-wide contraction steps over D
+    constexpr int DB = D / 16;                      // 16-row blocks of D
+    static_assert(VM_WAIT < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) char ring[2 * R * TILEB];
+    __shared__ __attribute__((aligned(16))) float stats[R][64];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l16 = lane & 15, g = lane >> 4;
+
+    const int logical = xcd_logical_tile(blockIdx.x, a.nblocks, a.remap, a.nrt, a.nfull);
+    const int bh = logical / a.nrt;
+    const int rt = logical - bh * a.nrt;            // longest bands (first key tiles) first
+    const int T = a.T, W = a.W;
+    const int64_t off = (int64_t)bh * T * D;
+    const bf16* Q = a.q + off;
+    const bf16* K = a.k + off;
+    const bf16* V = a.v + off;
+    const bf16* DO = a.dout + off;
+
+    const int r0 = rt * BM;                         // workgroup's keys [r0, r0 + BM)
+    const int rw0 = r0 + RW * wave;                 // this wave's keys
+    const int kr = rw0 + l16;                       // this lane's key
+    const int c_hi = min(r0 + BM - 1 + W, T);       // queries i with 0 <= i - j < W
+    const int t0 = r0 / BN, t1 = (c_hi + BN - 1) / BN;
+    const bool live = rw0 < T;
+    const int wt0 = live ? rw0 / BN : t1;
+    const int wt1 = live ? (min(rw0 + RW - 1 + W, T) + BN - 1) / BN : t1;
+    auto needs = [&](int t) { return t >= wt0 && t < wt1; };
+    auto interior = [&](int t) {
+        const int q0 = t * BN;
+        return q0 >= rw0 + RW - 1 && q0 + BN - 1 - rw0 < W && q0 + BN - 1 < T;
+    };
+
+    // B operands of S^T and dP^T: this lane's key row of k and of v,
+    // d = 32 kc + 8 g .. + 7 (rows past T read row T - 1; never stored)
+    bf16x8 kb[KC], vb[KC];
+    {
+        const int rc = min(kr, T - 1);
+        const bf16* pk = K + (int64_t)rc * D + 8 * g;
+        const bf16* pv = V + (int64_t)rc * D + 8 * g;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            kb[kc] = *reinterpret_cast<const bf16x8*>(pk + 32 * kc);
+            vb[kc] = *reinterpret_cast<const bf16x8*>(pv + 32 * kc);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
+
+    // ring: kind 0 = Q, kind 1 = dout, both read whole rows and transposed
+    // Ring slot s of kind x (tile t lives in slot (t - t0) mod R); the loop
+    // is unrolled over the R = 3 slots, so slot addresses are immediates.
+    static_assert(R == 3, "the loop is unrolled over 3 ring slots");
+    auto slot = [&](int x, int s) { return ring + (x * R + s % R) * TILEB; };
+    uint32_t offs[NLD_W];
+    tile_offsets<D, NW, kSwzB>(offs, wave, lane, 2 * D);
+    const int slab = T * D * 2;
+    const __amdgpu_buffer_rsrc_t lse_rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.lse) + (int64_t)bh * T, 0, T * 4, 0x00020000);
+    const __amdgpu_buffer_rsrc_t del_rs = __builtin_amdgcn_make_buffer_rsrc(
+        a.delta + (int64_t)bh * T, 0, T * 4, 0x00020000);
+    auto load = [&](int t, int s) {
+        const int tt = min(t, t1 - 1);
+        const int boff = tt * TILEB;
+        dma_tile(rows_rsrc(Q, boff, slab), lds_addr(slot(0, s)), wave, offs);
+        dma_tile(rows_rsrc(DO, boff, slab), lds_addr(slot(1, s)), wave, offs);
+        const uint32_t sbase = lds_addr(&stats[s % R][0]);
+        const uint32_t soff = (tt * BN + 4 * (lane & 7)) * 4;
+        if (lane < 8) lds_load16(lse_rs, sbase, soff);
+        if (lane >= 8 && lane < 16) lds_load16(del_rs, sbase, soff);
+    };
+    auto publish = [&]() {
+        __builtin_amdgcn_s_waitcnt((VM_WAIT & 15) | ((VM_WAIT >> 4) << 14) | (7 << 4) | (0 << 8));
+        __builtin_amdgcn_s_barrier();
+    };
+    // A operand rows of a tile: row 16 blk + l16, 16-byte chunk 4 kc + g
+    auto row_frag = [&](const char* tile, int blk, int kc) {
+        const int row = 16 * blk + l16;
+        return *reinterpret_cast<const bf16x8*>(tile + row * (2 * D) +
+                                                (((4 * kc + g) ^ bswz<D>(row)) << 4));
+    };
+    // Transposed A operand: lane l16 of group g gets tile[16 blk + 4 g + e][16 db + l16]
+    // for e = 0..3 (elements 4 blk + e of the bf16x8); source lane j reads row
+    // 16 blk + 4 g + j / 4 at columns 16 db + 4 (j % 4) .. + 3.
+    auto tr_frag = [&](const char* tile, int db) {
+        i16x4 part[2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            const int row = 16 * blk + 4 * g + (l16 >> 2);
+            const int col = 16 * db + 4 * (l16 & 3);
+            const int chunk = col >> 3;
+            part[blk] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t*)(tile + row * (2 * D) + ((chunk ^ bswz<D>(row)) << 4) + 2 * (col & 7)));
+        }
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4,
+                                                                  5, 6, 7));
+    };
+
+    f32x4v adv[DB], adk[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+        adv[db] = f32x4v{};
+        adk[db] = f32x4v{};
+    }
+    const float c = a.c;
+    const float sfill = c >= 0.f ? -__builtin_inff() : __builtin_inff();
+
+#pragma unroll
+    for (int i = 0; i < PF; ++i) load(t0 + i, i);
+    publish();
+    auto step = [&](auto ks, int j) {
+        constexpr int KS = decltype(ks)::value;
+        load(j + PF, KS + PF);
+        if (needs(j)) {
+            const char* TQ = slot(0, KS);
+            const char* TD = slot(1, KS);
+            f32x4v s[2], dp[2];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                s[blk] = f32x4v{};
+                dp[blk] = f32x4v{};
+#pragma unroll
+                for (int kc = 0; kc < KC; ++kc) {
+                    s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_frag(TQ, blk, kc), kb[kc],
+                                                                     s[blk], 0, 0, 0);
+                    dp[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_frag(TD, blk, kc), vb[kc],
+                                                                      dp[blk], 0, 0, 0);
+                }
+            }
+            // this lane: key kr, queries q0 + 16 blk + 4 g + i
+            const int q0 = j * BN;
+            if (!interior(j)) {
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int qq = q0 + 16 * blk + 4 * g + i;
+                        const bool ok = (unsigned)(qq - kr) < (unsigned)W && qq < T;
+                        s[blk][i] = ok ? s[blk][i] : sfill;
+                    }
+            }
+            const float* st = &stats[KS][0];
+            f32x4v Ls[2], Ds[2];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                Ls[blk] = *reinterpret_cast<const f32x4v*>(st + 16 * blk + 4 * g);
+                Ds[blk] = *reinterpret_cast<const f32x4v*>(st + 32 + 16 * blk + 4 * g);
+            }
+            float pv[8], dsv[8];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][i], c, -Ls[blk][i] * kLog2e));
+                    pv[4 * blk + i] = p;
+                    dsv[4 * blk + i] = p * (dp[blk][i] - Ds[blk][i]);
+                }
+            bf16x8 pp, ph, pl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pp[e] = (bf16)pv[e];
+                ph[e] = (bf16)dsv[e];
+                if constexpr (PREC) pl[e] = (bf16)(dsv[e] - (float)ph[e]);
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                adv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_frag(TD, db), pp, adv[db], 0, 0, 0);
+                const bf16x8 tq = tr_frag(TQ, db);
+                adk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tq, ph, adk[db], 0, 0, 0);
+                if constexpr (PREC)
+                    adk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tq, pl, adk[db], 0, 0, 0);
+            }
+        }
+        publish();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    for (int j = t0; j < t1;) {
+        step(I0{}, j);
+        if (++j >= t1) break;
+        step(I1{}, j);
+        if (++j >= t1) break;
+        step(I2{}, j);
+        ++j;
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // no LDS load may outlive the workgroup
+
+    // store: lane holds d = 16 db + 4 g + 0..3 of key kr
+    if (kr < T) {
+        bf16* rv = a.grad + off + (int64_t)kr * D;       // dv
+        bf16* rk = a.grad2 + off + (int64_t)kr * D;      // dk
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            bf16x4 wv, wk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                wv[e] = (bf16)adv[db][e];
+                wk[e] = (bf16)(adk[db][e] * a.scale);
+            }
+            *reinterpret_cast<bf16x4*>(rv + 16 * db + 4 * g) = wv;
+            *reinterpret_cast<bf16x4*>(rk + 16 * db + 4 * g) = wk;
+        }
+    }
+}
+
+template <int D, bool PREC>
+hipError_t launch_kv(BArgs a, int64_t B, int64_t H, hipStream_t st) {
+    constexpr int BM = 64;
+    a.nrt = (a.T + BM - 1) / BM;
+    const int64_t nblocks = B * H * a.nrt;
+    a.nblocks = (int)nblocks;
+    a.remap = nblocks % 8 == 0 ? 1 : 0;
+    a.nfull = xcd_longest_first_nfull(nblocks, a.nrt, (a.W - 1 + BM - 1) / BM);
+    void* args[] = {(void*)&a};
+    return hipLaunchKernel((const void*)bwd_kv_kernel<D, PREC>, dim3((unsigned)nblocks), dim3(256),
+                           args, 0, st);
 }
 
 template <int D, int MODE, bool PREC>
@@ -393,8 +575,7 @@ hipError_t launch_mode(BArgs a, int64_t B, int64_t H, hipStream_t st) {
     const int64_t nblocks = B * H * a.nrt;
     a.nblocks = (int)nblocks;
     a.remap = nblocks % 8 == 0 ? 1 : 0;
-    // row tiles within W - 1 of the sequence's far end (DQ: its start; DV, DK:
-    // its end) have shorter bands
+    // query tiles within W - 1 of the sequence's start have shorter bands
     a.nfull = xcd_longest_first_nfull(nblocks, a.nrt, (a.W - 1 + C::BM - 1) / C::BM);
     void* args[] = {(void*)&a};
     return hipLaunchKernel((const void*)bwd_bf16_kernel<D, MODE, PREC>, dim3((unsigned)nblocks),
@@ -416,10 +597,8 @@ hipError_t launch_all(BArgs a, float* lse_ws, bf16* dq, bf16* dk, bf16* dv, int6
     e = launch_mode<D, kDQ, PREC>(a, B, H, st);
     if (e != hipSuccess) return e;
     a.grad = dv;
-    e = launch_mode<D, kDV, false>(a, B, H, st);
-    if (e != hipSuccess) return e;
-    a.grad = dk;
-    return launch_mode<D, kDK, PREC>(a, B, H, st);
+    a.grad2 = dk;
+    return launch_kv<D, PREC>(a, B, H, st);
 }
 
 }  // namespace
