@@ -35,8 +35,8 @@
 // the packed probabilities feed the next product's B operand directly, as in
 // the forward kernel, and transposed operands come from ds_read_b64_tr_b16.
 // DQ reads its k tile, and the key-row kernel its q and dout tiles, both
-// whole and transposed, from one LDS copy laid out with the bswz swizzle,
-// which serves both reads without bank conflicts.
+// whole and transposed, from one LDS copy each (swizzles bswz and qswz, one
+// per operand layout), which serves both reads without bank conflicts.
 
 #include "swa_mfma.h"
 
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     static_assert(R == 3, "the loop is unrolled over 3 ring slots");
     auto slot = [&](int x, int s) { return ring + (x * R + s % R) * TILEB; };
     uint32_t offs[NLD_W];
-    tile_offsets<D, NW, kSwzB>(offs, wave, lane, 2 * D);
+    tile_offsets<D, NW, kSwzQ>(offs, wave, lane, 2 * D);
     const int slab = T * D * 2;
     const __amdgpu_buffer_rsrc_t lse_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(a.lse) + (int64_t)bh * T, 0, T * 4, 0x00020000);
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     auto row_frag = [&](const char* tile, int blk, int kc) {
         const int row = 16 * blk + l16;
         return *reinterpret_cast<const bf16x8*>(tile + row * (2 * D) +
-                                                (((4 * kc + g) ^ bswz<D>(row)) << 4));
+                                                (((4 * kc + g) ^ qswz<D>(row)) << 4));
     };
     // Transposed A operand: lane l16 of group g gets tile[16 blk + 4 g + e][16 db + l16]
     // for e = 0..3 (elements 4 blk + e of the bf16x8); source lane j reads row
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             const int col = 16 * db + 4 * (l16 & 3);
             const int chunk = col >> 3;
             part[blk] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4_t*)(tile + row * (2 * D) + ((chunk ^ bswz<D>(row)) << 4) + 2 * (col & 7)));
+                (lds_i16x4_t*)(tile + row * (2 * D) + ((chunk ^ qswz<D>(row)) << 4) + 2 * (col & 7)));
         }
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4,
                                                                   5, 6, 7));

@@ -79,12 +79,29 @@ __device__ inline uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
+// Tile read both ways in the 16x16x32 operand layout (whole rows: 16 lanes
+// over 16 rows of one chunk column; transposed: 4 rows x 32 bytes per 16
+// lanes).  The LDS services a wavefront's lanes in passes that pair lanes
+// l and l + 32 (16 of them per pass for 16-byte reads, 32 for 8-byte
+// reads), which the bit reversal above does not spread for this layout;
+// XOR-ing the chunk with 4, 8, 3 and 2 for row bits 0..3 (D = 128; 4, 3, 2
+// for bits 1..3 at D = 64) puts every pass of both reads on distinct banks.
+template <int D> __device__ inline int qswz(int row) {
+    if (D == 128)
+        return ((row & 1) ? 4 : 0) ^ ((row & 2) ? 8 : 0) ^ ((row & 4) ? 3 : 0) ^ ((row & 8) ? 2 : 0);
+    return ((row & 2) ? 4 : 0) ^ ((row & 4) ? 3 : 0) ^ ((row & 8) ? 2 : 0);
+}
+
 // Swizzle selectors for tile layouts in LDS.
 constexpr int kSwzK = 0;   // kswz: rows read whole (16 lanes over 16 rows of one chunk column)
 constexpr int kSwzV = 1;   // vswz: rows read through ds_read_b64_tr_b16
 constexpr int kSwzB = 2;   // bswz: rows read both ways
+constexpr int kSwzQ = 3;   // qswz: rows read both ways, 16x16x32 layout
 template <int D, int SW> __device__ inline int swz(int row) {
-    return SW == kSwzV ? vswz<D>(row) : SW == kSwzB ? bswz<D>(row) : kswz<D>(row);
+    return SW == kSwzV   ? vswz<D>(row)
+           : SW == kSwzB ? bswz<D>(row)
+           : SW == kSwzQ ? qswz<D>(row)
+                         : kswz<D>(row);
 }
 
 // Source offsets of one tile's loads (N 1-KiB loads per wave, NW waves).
