@@ -71,9 +71,11 @@ struct BArgs {
     const bf16* dout;
     bf16* grad;           // DQ: dq; key kernel: dv   ([B, H, T, D])
     bf16* grad2;          // key kernel: dk
-    const float* lse;     // [B * H * T] log-sum-exp of the scaled scores (forward)
-    float* delta;         // [B * H * T] dout . out (written by DQ; precise: by ST)
-    float* lse_w;         // ST: [B * H * T] log normaliser of the rebuilt weights
+    const float* lse;     // [B * H * T] log-sum-exp of the scaled scores (forward;
+                          // precise DQ: ST's lse_w)
+    float* delta;         // [B * H * T] -(dout . out) (written by DQ; precise: by ST)
+    float* lse_w;         // [B * H * T] log2 normaliser of the rebuilt weights, read
+                          // by the key kernel (written by DQ; precise: by ST)
     int T, W, nrt, nblocks, remap;
     int nfull;            // longest-first dispatch (xcd_logical_tile); -1: plain order
     float c;              // log2(e) * scale
@@ -150,12 +152,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             f1[dc] = *reinterpret_cast<const bf16x8*>(p1 + 16 * dc);
         }
     }
-    // this row's log2 normaliser; DQ: delta = dout . out (also published for
-    // the key kernel), or (precise) ST's delta
-    const float Lrow = a.lse[(int64_t)bh * T + rc] * kLog2e;
-    float drow = 0.f;
+    // this row's log2 normaliser (the forward's natural-log lse, or for the
+    // precise DQ ST's log2 output); DQ: delta = dout . out (published with
+    // the normaliser for the key kernel), or (precise) ST's delta
+    const float Lrow = (MODE == kDQ && PREC) ? a.lse[(int64_t)bh * T + rc]
+                                             : a.lse[(int64_t)bh * T + rc] * kLog2e;
+    // nd = -delta (the delta arrays hold -delta: it starts the dP products'
+    // accumulation, so they yield dP - delta directly)
+    float nd = 0.f;
     if (MODE == kDQ && PREC) {
-        drow = a.delta[(int64_t)bh * T + rc];
+        nd = a.delta[(int64_t)bh * T + rc];
     } else if (MODE == kDQ) {
         const bf16* po = a.o + off + (int64_t)rc * D + 8 * hh;
         float d = 0.f;
@@ -165,8 +171,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int e = 0; e < 8; ++e) d = fmaf((float)f1[dc][e], (float)ov[e], d);
         }
-        drow = swap_sum(d);
-        if (hh == 0 && ri < T) a.delta[(int64_t)bh * T + ri] = drow;
+        nd = -swap_sum(d);
+        if (hh == 0 && ri < T) {
+            a.delta[(int64_t)bh * T + ri] = nd;
+            a.lse_w[(int64_t)bh * T + ri] = Lrow;
+        }
     }
     // land the register operands before any tile load is counted
     __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
@@ -218,7 +227,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const char* A0 = slot(0, KS);
             const char* A1 = slot(1, KS);
             // S^T = K Q^T and dP^T = V dO^T
-            f32x16 s = f32x16{}, dp = f32x16{};
+            f32x16 s = f32x16{}, dp;
+#pragma unroll
+            for (int vv = 0; vv < 16; ++vv) dp[vv] = nd;
 #pragma unroll
             for (int dc = 0; dc < D / 16; ++dc) {
                 s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row_frag<D, SW0>(A0, lr, hh, dc),
@@ -243,7 +254,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     zsum += p;
                     ysum = __builtin_fmaf(p, dp[vv], ysum);
                 } else {
-                    s[vv] = p * (dp[vv] - drow);
+                    s[vv] = p * dp[vv];
                 }
             }
             if constexpr (MODE == kDQ) {
@@ -298,8 +309,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // each row's z and y over its band (lanes l, l ^ 32 hold halves)
         const float z = swap_sum(zsum), y = swap_sum(ysum);
         if (hh == 0 && ri < T) {
-            a.lse_w[(int64_t)bh * T + ri] = (Lrow + __builtin_amdgcn_logf(z)) * kLn2;
-            a.delta[(int64_t)bh * T + ri] = y / z;
+            a.lse_w[(int64_t)bh * T + ri] = Lrow + __builtin_amdgcn_logf(z);
+            a.delta[(int64_t)bh * T + ri] = -(y / z);
         }
         return;
     }
@@ -406,7 +417,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     tile_offsets<D, NW, kSwzQ>(offs, wave, lane, 2 * D);
     const int slab = T * D * 2;
     const __amdgpu_buffer_rsrc_t lse_rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(a.lse) + (int64_t)bh * T, 0, T * 4, 0x00020000);
+        a.lse_w + (int64_t)bh * T, 0, T * 4, 0x00020000);
     const __amdgpu_buffer_rsrc_t del_rs = __builtin_amdgcn_make_buffer_rsrc(
         a.delta + (int64_t)bh * T, 0, T * 4, 0x00020000);
     auto load = [&](int t, int s) {
@@ -464,11 +475,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         if (needs(j)) {
             const char* TQ = slot(0, KS);
             const char* TD = slot(1, KS);
+            const float* st = &stats[KS][0];
+            f32x4v Ls[2], Ds[2];
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                Ls[blk] = *reinterpret_cast<const f32x4v*>(st + 16 * blk + 4 * g);
+                Ds[blk] = *reinterpret_cast<const f32x4v*>(st + 32 + 16 * blk + 4 * g);
+            }
             f32x4v s[2], dp[2];
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk) {
                 s[blk] = f32x4v{};
-                dp[blk] = f32x4v{};
+                dp[blk] = Ds[blk];   // -delta: the products give dP - delta
 #pragma unroll
                 for (int kc = 0; kc < KC; ++kc) {
                     s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(row_frag(TQ, blk, kc), kb[kc],
@@ -489,21 +507,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                         s[blk][i] = ok ? s[blk][i] : sfill;
                     }
             }
-            const float* st = &stats[KS][0];
-            f32x4v Ls[2], Ds[2];
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                Ls[blk] = *reinterpret_cast<const f32x4v*>(st + 16 * blk + 4 * g);
-                Ds[blk] = *reinterpret_cast<const f32x4v*>(st + 32 + 16 * blk + 4 * g);
-            }
             float pv[8], dsv[8];
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][i], c, -Ls[blk][i] * kLog2e));
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[blk][i], c, -Ls[blk][i]));
                     pv[4 * blk + i] = p;
-                    dsv[4 * blk + i] = p * (dp[blk][i] - Ds[blk][i]);
+                    dsv[4 * blk + i] = p * dp[blk][i];
                 }
             bf16x8 pp, ph, pl;
 #pragma unroll
@@ -520,6 +531,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                 if constexpr (PREC)
                     adk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tq, pl, adk[db], 0, 0, 0);
             }
+            // issue order: the first two operand sets, then each set's
+            // products followed by the reads of the set after next
+            constexpr int MF = PREC ? 3 : 2;
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int i = 0; i < DB - 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
         }
         publish();
     };
@@ -582,13 +604,16 @@ hipError_t launch_mode(BArgs a, int64_t B, int64_t H, hipStream_t st) {
                            dim3(256), args, 0, st);
 }
 
-// lse_ws: workspace row normalisers (precise: written by ST from a.lse)
+// lse_ws: workspace log2 row normalisers for the key kernel, written by DQ
+// (precise: by ST) from a.lse.  It may be a.lse itself (the forward rerun
+// writes its lse there): each row is read and rewritten by the lane that
+// owns it, and rows past T, which read row T - 1, are never stored.
 template <int D, bool PREC>
 hipError_t launch_all(BArgs a, float* lse_ws, bf16* dq, bf16* dk, bf16* dv, int64_t B, int64_t H,
                       hipStream_t st) {
     hipError_t e;
+    a.lse_w = lse_ws;
     if constexpr (PREC) {
-        a.lse_w = lse_ws;
         e = launch_mode<D, kST, true>(a, B, H, st);
         if (e != hipSuccess) return e;
         a.lse = lse_ws;
