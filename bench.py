@@ -225,7 +225,7 @@ def main() -> int:
     # The GPU's clocks ramp up over the first ~50 ms of sustained matrix work;
     # 20 steps (~70 ms) reach the plateau before timing starts.
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "backward", "copy"], default="all",
                     help="profiling aid: run one kernel only (the JSON line is then partial)")
     ap.add_argument("--workload", default=PREFILL,
                     help="prefill workload for --only prefill (the default step always uses the "
@@ -274,9 +274,10 @@ def main() -> int:
     wd = si.WORKLOADS[DECODE]
     do_p = args.only in ("all", "prefill")
     do_d = args.only in ("all", "decode")
+    do_b = args.only in ("all", "backward")
     print(f"# device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}",
           file=sys.stderr, flush=True)
-    if do_p:
+    if do_p or do_b:
         q, k, v = si.workload_qkv(wp, dev)
         out = torch.empty_like(q)
     if do_d:
@@ -299,12 +300,13 @@ def main() -> int:
         if evs is not None:
             evs[2].record(stream)
 
-    for _ in range(args.warmup):
+    n_steps = 0 if args.only == "backward" else args.steps
+    for _ in range(args.warmup if n_steps else 0):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_steps)]
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(n_steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -319,14 +321,14 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": wall / args.steps * 1e3,
+        "ms_per_step": wall / n_steps * 1e3 if n_steps else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{PREFILL} + {DECODE}" if args.only == "all" else
-                   (wp.name if do_p else DECODE)},
+                   (wp.name if do_p or do_b else DECODE)},
     }
     if do_p:
         flops = prefill_flops(wp.B, wp.H, wp.T, wp.D, wp.W)
@@ -445,7 +447,7 @@ def main() -> int:
                          "ms_mean": tm, "projection_flop": proj, "attention_flop": att,
                          "TFLOPs": (proj + att) / (tm * 1e-3) / 1e12}
         del xm, wts, om, wsm
-    if do_p and args.only == "all":
+    if do_b:
         # Backward of the same layer: dq, dk, dv given dout (includes the
         # forward rerun that rebuilds the per-row softmax normalisers).
         gb = si.generator(wp.seed + 11, dev)
@@ -453,8 +455,9 @@ def main() -> int:
         gq, gk, gv = (torch.empty_like(q) for _ in range(3))
         wsb = torch.empty(int(swa.lib().swa_backward_workspace_bytes(wp.B, wp.H, wp.T)),
                           dtype=torch.uint8, device=dev)
+        # 30 warm-up launches: run alone (--only backward) the clocks start cold
         tb = time_launches(lambda: swa.swa_backward(q, k, v, out, dob, gq, gk, gv, wp.W,
-                                                    workspace=wsb, stream=stream), stream, 10, 3)
+                                                    workspace=wsb, stream=stream), stream, 10, 30)
         # training order: the forward keeps its row log-sum-exp for the backward
         lse = torch.empty((wp.B, wp.H, wp.T), dtype=torch.float32, device=dev)
         swa.swa_forward_lse(q, k, v, out, lse, wp.W, stream=stream)
@@ -467,6 +470,8 @@ def main() -> int:
                            "note": "five band products (S, dP, dV, dK, dQ) counted; the "
                                    "forward rerun (absent given lse) and the recomputed S "
                                    "products are not"}
+        if not do_p:
+            res["value"] = res["backward"]["TFLOPs_given_lse"]
         del dob, gq, gk, gv, wsb, lse
     if do_p and args.only == "all" and not args.no_more_prefill:
         # The other prefill workloads, each timed launch by launch (HIP events
