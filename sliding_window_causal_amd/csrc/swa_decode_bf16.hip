@@ -5,16 +5,27 @@
 //
 // The path is bound by HBM: every occupied slot's k and v row is read once
 // (2 * n * D * 2 bytes per (stream, head)) for 4 * n * D flops.  One
-// workgroup of 256 threads owns one (stream, head):
-//   phase 1  scores: a quad of 4 lanes owns a slot row; each lane reads its
-//            D/32 16-byte chunks (a quad reads 64 contiguous bytes per
-//            load), dots them against the query with v_dot2_f32_bf16, and
-//            the quad sums with two DPP steps.  Scores go to LDS, pre-scaled
-//            by log2(e)/sqrt(D).
+// workgroup of 256 threads owns one (stream, head); LPR lanes own one slot
+// row, lane c of them its 16-byte chunks LPR i + c.
+//   phase 1  scores: each lane dots its chunks against the query's
+//            (v_dot2_f32_bf16), the LPR lanes of a row sum with DPP steps,
+//            and the row's score goes to LDS, pre-scaled by log2(e)/sqrt(D).
 //   softmax  exact two-pass over the n LDS scores (max, then exp2 and sum).
-//   phase 2  output: the same quad/slot mapping streams v rows, each lane
-//            accumulating p * v for its 8 * D/32 columns; partial outputs
-//            are reduced across the 64 quads through LDS.
+//   phase 2  output: the same lane/slot mapping streams v rows, each lane
+//            accumulating p * v for its columns; partial outputs are reduced
+//            across the 256 / LPR row slots through LDS.
+// Two mappings.  Row-contiguous (LPR = D / 8, one chunk per lane): one
+// wavefront load covers whole consecutive rows, a contiguous KiB, and the
+// loads are non-temporal (the ring is read once).  Quad (LPR = 4, D / 32
+// chunks per lane): fewer vector instructions per byte.  Measured on 16 GiB
+// reads, 1-KiB-contiguous non-temporal loads reach 7.05-7.1 TB/s, ordinary
+// loads 6.2-6.35 TB/s whatever the pattern, and non-temporal loads that
+// cover 64 bytes of 16 rows per instruction (the quad mapping) 6.36-6.48.
+// With at least one workgroup per compute unit the launch is bound by HBM
+// and takes the row-contiguous mapping (7.0-7.1 TB/s against 6.2-6.3 for
+// the quad one from 512 workgroups on); with fewer, each workgroup's own
+// issue rate bounds it and the quad mapping is faster (46 against 62 us for
+// one stream of 32 heads, W = 4096).
 // Occupied slots are [0, min(pos + 1, W)): unoccupied slots are never read.
 
 #include "swa_internal.h"
@@ -25,13 +36,26 @@ namespace swa {
 namespace {
 
 constexpr int kDecThreads = 256;
-constexpr int kQuads = kDecThreads / 4;
-constexpr int kUnroll = 4;
+// launches of at least this many workgroups (one per compute unit) take
+// the row-contiguous mapping
+constexpr int64_t kDecRowsMinWGs = 256;
 
 // Sum over the 4 lanes of a quad (DPP quad_perm; no LDS traffic).
 __device__ inline float quad_sum(float x) {
     x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
     x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+    return x;
+}
+
+// Sum over the N lanes (4, 8 or 16) that hold one row, left in all of them
+// (DPP: quad exchanges, then the half-row and row mirrors).
+template <int N>
+__device__ inline float row_sum(float x) {
+    x = quad_sum(x);
+    if constexpr (N >= 8)
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, true));
+    if constexpr (N >= 16)
+        x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, true));
     return x;
 }
 
@@ -72,15 +96,23 @@ struct DecArgs {
     float c;              // log2(e) / sqrt(D)
 };
 
-template <int D>
+template <int D, bool ROWS>
 __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a) {
-    constexpr int CPL = D / 32;                 // 16-byte chunks per lane per row
+    constexpr int LPR = ROWS ? D / 8 : 4;       // lanes per row
+    constexpr int CPL = D / (8 * LPR);          // 16-byte chunks per lane per row
+    constexpr int RPG = kDecThreads / LPR;      // rows per workgroup and load
+    constexpr int UN = ROWS ? 16 : 4;           // loads per lane in flight (x CPL)
+    auto ld = [](const bf16* p) {
+        const u32x4* v = reinterpret_cast<const u32x4*>(p);
+        if constexpr (ROWS) return __builtin_nontemporal_load(v);
+        else return *v;
+    };
     extern __shared__ __attribute__((aligned(16))) float sm[];
     float* sc = sm;                             // scores / probabilities, later partial outputs
     __shared__ float red[kDecThreads / 64];
 
     const int tid = threadIdx.x;
-    const int quad = tid >> 2, sig = tid & 3;
+    const int cl = tid % LPR, rw = tid / LPR;   // chunk lane, row slot
     const int wave = tid >> 6, lane = tid & 63;
     const int64_t bid = blockIdx.x;
     const int64_t sh = bid / a.P;
@@ -119,32 +151,31 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a) {
         }
     }
 
-    // query chunks 4 i + sig
+    // query chunks LPR i + cl
     u32x4 qv[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
-        qv[i] = *reinterpret_cast<const u32x4*>(a.q + sh * D + (4 * i + sig) * 8);
+        qv[i] = *reinterpret_cast<const u32x4*>(a.q + sh * D + (LPR * i + cl) * 8);
 
     // ---- phase 1: scores
-    for (int r0 = lo; r0 < hi; r0 += kQuads * kUnroll) {
-        u32x4 kv[kUnroll][CPL];
+    for (int r0 = lo; r0 < hi; r0 += RPG * UN) {
+        u32x4 kv[UN][CPL];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int row = r0 + quad + kQuads * u;
+        for (int u = 0; u < UN; ++u) {
+            const int row = r0 + rw + RPG * u;
             const bf16* src = row == wslot ? Kn : Kr + (int64_t)row * D;
 #pragma unroll
             for (int i = 0; i < CPL; ++i)
-                kv[u][i] = row < hi ? *reinterpret_cast<const u32x4*>(src + (4 * i + sig) * 8)
-                                    : u32x4{0, 0, 0, 0};
+                kv[u][i] = row < hi ? ld(src + (LPR * i + cl) * 8) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int row = r0 + quad + kQuads * u;
+        for (int u = 0; u < UN; ++u) {
+            const int row = r0 + rw + RPG * u;
             float acc = 0.f;
 #pragma unroll
             for (int i = 0; i < CPL; ++i) acc = dot8(kv[u][i], qv[i], acc);
-            acc = quad_sum(acc);
-            if (sig == 0 && row < hi) sc[row - lo] = acc * a.c;
+            acc = row_sum<LPR>(acc);
+            if (cl == 0 && row < hi) sc[row - lo] = acc * a.c;
         }
     }
     __syncthreads();
@@ -176,20 +207,19 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a) {
     for (int i = 0; i < CPL; ++i)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
-    for (int r0 = lo; r0 < hi; r0 += kQuads * kUnroll) {
-        u32x4 vv[kUnroll][CPL];
+    for (int r0 = lo; r0 < hi; r0 += RPG * UN) {
+        u32x4 vv[UN][CPL];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int row = r0 + quad + kQuads * u;
+        for (int u = 0; u < UN; ++u) {
+            const int row = r0 + rw + RPG * u;
             const bf16* src = row == wslot ? Vn : Vr + (int64_t)row * D;
 #pragma unroll
             for (int i = 0; i < CPL; ++i)
-                vv[u][i] = row < hi ? *reinterpret_cast<const u32x4*>(src + (4 * i + sig) * 8)
-                                    : u32x4{0, 0, 0, 0};
+                vv[u][i] = row < hi ? ld(src + (LPR * i + cl) * 8) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int row = r0 + quad + kQuads * u;
+        for (int u = 0; u < UN; ++u) {
+            const int row = r0 + rw + RPG * u;
             const float pr = row < hi ? sc[row - lo] : 0.f;
 #pragma unroll
             for (int i = 0; i < CPL; ++i)
@@ -202,15 +232,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a) {
     }
     __syncthreads();   // every lane is done with the probabilities
 
-    // ---- reduce partial outputs over the 64 quads: sm[quad][d]
+    // ---- reduce partial outputs over the RPG row slots: sm[rw][d]
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sm[quad * D + (4 * i + sig) * 8 + e] = acc[i][e];
+        for (int e = 0; e < 8; ++e) sm[rw * D + (LPR * i + cl) * 8 + e] = acc[i][e];
     __syncthreads();
     if (tid < D) {
         float t = 0.f;
-        for (int qd = 0; qd < kQuads; ++qd) t += sm[qd * D + tid];
+        for (int r = 0; r < RPG; ++r) t += sm[r * D + tid];
         if (a.P == 1) {
             a.out[sh * D + tid] = (bf16)(cnt > 0 ? t / l : 0.f);
         } else {
@@ -275,27 +305,41 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
         out[sh * D + lane + 64 * r] = (bf16)(L > 0.f ? o[r] / L : 0.f);
 }
 
-template <int D>
-hipError_t launch(DecArgs a, int64_t S, hipStream_t stream) {
-    const int64_t floats = a.chunk > kQuads * D ? (int64_t)a.chunk : (int64_t)kQuads * D;
-    const unsigned lds = (unsigned)(floats * sizeof(float));
-    // the dynamic-LDS limit is raised once per device (bit dev of attr_done)
-    static std::atomic<uint64_t> attr_done{0};
+// Raise the kernel's dynamic-LDS limit to the largest score array, once
+// per device (bit dev of done).
+template <int D, bool ROWS>
+hipError_t allow_lds() {
+    static std::atomic<uint64_t> done{0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
     const uint64_t bit = 1ull << (dev & 63);
-    if (!(attr_done.load(std::memory_order_acquire) & bit)) {
-        hipError_t e = hipFuncSetAttribute((const void*)decode_bf16_kernel<D>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)(kDecodeMaxW * sizeof(float)));
-        if (e != hipSuccess) return e;
-        attr_done.fetch_or(bit, std::memory_order_release);
-    }
-    a.c = kLog2e / sqrtf((float)D);
+    if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute((const void*)decode_bf16_kernel<D, ROWS>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)(kDecodeMaxW * sizeof(float)));
+    if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
+
+template <int D, bool ROWS>
+hipError_t launch_mapping(const DecArgs& a, int64_t wgs, hipStream_t stream) {
+    // scores (one float per slot of the split), later the partial outputs
+    // of the RPG row slots
+    const int64_t red = (int64_t)(kDecThreads / (ROWS ? D / 8 : 4)) * D;
+    const int64_t floats = a.chunk > red ? (int64_t)a.chunk : red;
+    hipError_t e = allow_lds<D, ROWS>();
+    if (e != hipSuccess) return e;
     void* args[] = {(void*)&a};
-    hipError_t e = hipLaunchKernel((const void*)decode_bf16_kernel<D>,
-                                   dim3((unsigned)(S * a.H * a.P)), dim3(kDecThreads), args, lds,
-                                   stream);
+    return hipLaunchKernel((const void*)decode_bf16_kernel<D, ROWS>, dim3((unsigned)wgs),
+                           dim3(kDecThreads), args, (unsigned)(floats * sizeof(float)), stream);
+}
+
+template <int D>
+hipError_t launch(DecArgs a, int64_t S, hipStream_t stream) {
+    a.c = kLog2e / sqrtf((float)D);
+    const int64_t wgs = S * a.H * a.P;
+    hipError_t e = wgs >= kDecRowsMinWGs ? launch_mapping<D, true>(a, wgs, stream)
+                                         : launch_mapping<D, false>(a, wgs, stream);
     if (e != hipSuccess || a.P == 1) return e;
     const float* wo = a.ws_o;
     const float* wml = a.ws_ml;

@@ -185,3 +185,38 @@ def test_full_size_single_stream_split():
     torch.cuda.synchronize()
     ref = so.swa_decode(npy(qs), npy(kr), npy(vr), pos.cpu().tolist(), W)
     assert_close(out, ref, torch.bfloat16, "full-size split decode")
+
+
+@pytest.mark.parametrize("D,W", [(128, 97), (64, 64)])
+def test_both_lane_mappings(D, W):
+    """Launches of at least 256 workgroups read each slot row with D / 8
+    lanes and non-temporal loads; smaller ones with quads of lanes.  Both,
+    plain, split and fused with the append, against the oracle, on rings
+    fresh, partly filled, just full and wrapped."""
+    S, H = 16, 16                      # 256 workgroups: the row mapping
+    dtype = torch.bfloat16
+    pos = [[0, 1, W // 2, W - 1, W, 2 * W + 3, 3 * W - 1, 3 * W + 7][s % 8] for s in range(S)]
+    q, k, v = _case(S, H, D, W, pos, dtype, seed=90 + D)
+    kr, vr = _rings(k, v, pos, W, dtype)
+    qs = torch.stack([q[s, :, pos[s]] for s in range(S)]).contiguous()
+    p = torch.tensor(pos, dtype=torch.int64, device=DEV)
+    ref = so.swa_decode(npy(qs), npy(kr), npy(vr), pos, W)
+    rows_map = swa.decode(qs, kr, vr, p)
+    split = swa.decode(qs, kr, vr, p, split=True)
+    # two streams alone: 32 workgroups, the quad mapping
+    quad_map = swa.decode(qs[:2].contiguous(), kr[:2].contiguous(), vr[:2].contiguous(), p[:2])
+    torch.cuda.synchronize()
+    assert_close(rows_map, ref, dtype, "row mapping")
+    assert_close(split, ref, dtype, "split")
+    assert_close(quad_map, ref[:2], dtype, "quad mapping")
+    # fused append in the row mapping: the rings up to pos - 1 plus the token
+    prev = [max(x - 1, 0) for x in pos]
+    kr2, vr2 = _rings(k, v, prev, W, dtype)
+    for s in range(S):
+        if pos[s] == 0:
+            kr2[s].fill_(float("nan"))
+            vr2[s].fill_(float("nan"))
+    take = lambda x: torch.stack([x[s, :, pos[s]] for s in range(S)]).contiguous()
+    fused = swa.decode_append(qs, take(k), take(v), kr2, vr2, p)
+    torch.cuda.synchronize()
+    assert_close(fused, ref, dtype, "fused append, row mapping")
