@@ -47,6 +47,11 @@ int forward(const void* q, const void* k, const void* v, void* out, int64_t B, i
     }
     if (dtype == SWA_F32) {
         if (D > kMaxRowD) return SWA_ERR_UNSUPPORTED;
+        if (swa::prefill_f32_supports(q, k, v, out, T, D, L))
+            return from_hip(swa::launch_prefill_f32((const float*)q, (const float*)k,
+                                                    (const float*)v, (float*)out, B, H, T, (int)D,
+                                                    W, L, sc, st, lse));
+        // other head sizes, alignment or strides: one wavefront per row
         return from_hip(swa::launch_rowwise_prefill<float>((const float*)q, (const float*)k,
                                                            (const float*)v, (float*)out, B, H, T,
                                                            (int)D, W, L, sc, st, lse));

@@ -88,6 +88,15 @@ hipError_t launch_prefill_bf16(const bf16* q, const bf16* k, const bf16* v, bf16
                                const Layout& L, float scale, hipStream_t stream,
                                float* lse = nullptr);
 
+// fp32 MFMA prefill (v_mfma_f32_32x32x2_f32): D in {32, 64, 128}, 16-byte
+// aligned pointers, every stride a multiple of 4 elements
+// (prefill_f32_supports); lse as for launch_prefill_bf16.
+bool prefill_f32_supports(const void* q, const void* k, const void* v, const void* out,
+                          int64_t T, int64_t D, const Layout& L);
+hipError_t launch_prefill_f32(const float* q, const float* k, const float* v, float* out,
+                              int64_t B, int64_t H, int64_t T, int D, int64_t W, const Layout& L,
+                              float scale, hipStream_t stream, float* lse = nullptr);
+
 // bf16 MFMA chunk continuation of a ring (q, kc, vc, out contiguous
 // [S, H, C, D], rings [S, H, W, D]); D in {64, 128}, 16-byte aligned
 // pointers, slabs under 2 GiB (chunk_bf16_supports).

@@ -1,0 +1,215 @@
+// Causal sliding-window attention prefill in fp32 on gfx950 matrix cores
+// (v_mfma_f32_32x32x2_f32: fp32 operands, fp32 products and sums).
+//
+// Band-only iteration as in the bf16 kernel ("NNX Sliding-Window
+// Attention", A local mask is not a sparse implementation): a wavefront owns
+// 32 consecutive queries of one (batch, head) and walks the 32-key tiles
+// that meet their band, keys j with i - W < j <= i ("27. Sliding-Window
+// Attention", step 2), masking (a select to -inf) only the tiles that
+// straddle an edge of the band.  Per tile:
+//   S^T = K Q^T     D/2 MFMAs.  Lane l supplies row l % 32 (key, or for Q^T
+//                   the query) and contraction slot l / 32; MFMA (g, e)
+//                   pairs head dimension 8 g + e (slot 0) with 8 g + 4 + e
+//                   (slot 1), so each lane loads 16 contiguous bytes per four
+//                   MFMAs.  The accumulator gives lane l query l % 32 and
+//                   keys 8 (v/4) + 4 (l/32) + v%4 (the layout of the bf16
+//                   kernel's score tile).
+//   softmax         online: row max over the tile (in-lane, then the lane
+//                   pair l, l ^ 32), O and the row sum rescaled when the max
+//                   grows, p = exp2((s - m) c) with c = log2(e) * scale.
+//   O^T += V^T P^T  D/2 MFMAs: MFMA (i, e) takes key 8 i + e in slot 0 and
+//                   8 i + 4 + e in slot 1, so the B operand is the lane's own
+//                   probability p[4 i + e] (no exchange) and the A operand
+//                   one element of a v row (32 lanes read 128 contiguous
+//                   bytes).
+// The four wavefronts of a workgroup are independent (no LDS, no barrier):
+// they take consecutive query tiles of one (batch, head), so their key tiles
+// are shared through the L2.
+
+#include "swa_internal.h"
+
+namespace swa {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct F32Args {
+    const float* q;
+    const float* k;
+    const float* v;
+    float* out;
+    float* lse;     // optional: ln(sum_j exp(s_ij * scale)) at lse[bh * T + i]
+    Layout L;       // element strides (D axis contiguous)
+    int H, T, W;    // W = min(W, T)
+    int nqt;        // 32-query tiles per (b, h)
+    int nwaves;     // B * H * nqt
+    float c;        // log2(e) * |scale|
+    int qneg;       // scale < 0: q negated (exact) and |scale| used
+};
+
+__device__ inline float swap_max32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float swap_sum32(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_f32_kernel(F32Args a) {
+    static_assert(D % 32 == 0 && D <= 128, "head size");
+    const int lane = threadIdx.x & 63;
+    const int lr = lane & 31, hf = lane >> 5;
+    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (gw >= a.nwaves) return;
+    const int bh = gw / a.nqt;
+    const int qt = gw - bh * a.nqt;
+    const int b = bh / a.H, h = bh - b * a.H;
+    const int T = a.T, W = a.W;
+    const float* __restrict__ Q = a.q + b * a.L.q.b + h * a.L.q.h;
+    const float* __restrict__ K = a.k + b * a.L.k.b + h * a.L.k.h;
+    const float* __restrict__ V = a.v + b * a.L.v.b + h * a.L.v.h;
+    const int64_t qrs = a.L.q.t, krs = a.L.k.t, vrs = a.L.v.t;
+
+    const int q0 = qt * 32;
+    const int qi = q0 + lr;
+    // Q^T operand: q[qi][8 g + 4 hf .. + 3] (rows past T read row T - 1 and
+    // are never stored)
+    f32x4 qf[D / 8];
+    {
+        const float* qp = Q + (int64_t)min(qi, T - 1) * qrs + 4 * hf;
+#pragma unroll
+        for (int g = 0; g < D / 8; ++g) {
+            qf[g] = *reinterpret_cast<const f32x4*>(qp + 8 * g);
+            if (a.qneg) qf[g] = -qf[g];
+        }
+    }
+    const float c = a.c;
+    const int t0 = max(q0 - W + 1, 0) / 32;
+    const int t1 = (min(q0 + 32, T) + 31) / 32;
+
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+    float m = -__builtin_inff();     // running row max (raw score units)
+    float lsum = 0.f;                // this lane's half of the row sum
+
+    for (int t = t0; t < t1; ++t) {
+        const int k0 = 32 * t;
+        // S^T = K Q^T
+        f32x16 s = f32x16{};
+        {
+            const float* kp = K + (int64_t)min(k0 + lr, T - 1) * krs + 4 * hf;
+#pragma unroll
+            for (int g = 0; g < D / 8; ++g) {
+                const f32x4 kf = *reinterpret_cast<const f32x4*>(kp + 8 * g);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    s = __builtin_amdgcn_mfma_f32_32x32x2f32(kf[e], qf[g][e], s, 0, 0, 0);
+            }
+        }
+        // band mask on tiles that straddle an edge (keys past T lie above
+        // every valid query's diagonal)
+        const bool interior = k0 + 31 <= q0 && q0 + 31 - k0 < W;
+        if (!interior) {
+#pragma unroll
+            for (int vv = 0; vv < 16; ++vv) {
+                const int key = k0 + 8 * (vv >> 2) + 4 * hf + (vv & 3);
+                s[vv] = (unsigned)(qi - key) < (unsigned)W ? s[vv] : -__builtin_inff();
+            }
+        }
+        float mx = s[0];
+#pragma unroll
+        for (int vv = 1; vv < 16; ++vv) mx = fmaxf(mx, s[vv]);
+        mx = swap_max32(mx);
+        if (mx > m) {
+            // m = -inf before the row's first key: nothing to rescale
+            const float alpha = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m - mx) * c);
+            m = mx;
+            lsum *= alpha;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+        }
+        // (s - m) c: the row's max key gets exp2(0) = 1 exactly (a fused
+        // s c - m c would leave the rounding of m c), so W = 1 returns v
+        const float mr = m == -__builtin_inff() ? 0.f : m;
+#pragma unroll
+        for (int vv = 0; vv < 16; ++vv) {
+            s[vv] = __builtin_amdgcn_exp2f((s[vv] - mr) * c);
+            lsum += s[vv];
+        }
+        // O^T += V^T P^T
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int key = min(k0 + 8 * i + 4 * hf + e, T - 1);
+                const float* vp = V + (int64_t)key * vrs + lr;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+                    o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vp[32 * db], s[4 * i + e], o[db], 0,
+                                                                 0, 0);
+            }
+    }
+
+    if (qi >= T) return;
+    const float l = swap_sum32(lsum);
+    const float inv = 1.f / l;
+    if (a.lse != nullptr && hf == 0)
+        a.lse[(int64_t)bh * T + qi] = (m * c + __builtin_amdgcn_logf(l)) * kLn2;
+    // lane holds d = 32 db + 8 g + 4 hf + 0..3 of query qi
+    float* orow = a.out + b * a.L.o.b + h * a.L.o.h + (int64_t)qi * a.L.o.t;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * g + 4 * hf) =
+                f32x4{o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
+                      o[db][4 * g + 3] * inv};
+}
+
+bool strides_ok4(const Strides& s) {
+    return s.b >= 0 && s.h >= 0 && s.t >= 0 && s.b % 4 == 0 && s.h % 4 == 0 && s.t % 4 == 0;
+}
+
+}  // namespace
+
+bool prefill_f32_supports(const void* q, const void* k, const void* v, const void* out,
+                          int64_t T, int64_t D, const Layout& L) {
+    if (D != 32 && D != 64 && D != 128) return false;
+    for (const void* p : {q, k, v, out})
+        if (((uintptr_t)p & 15) != 0) return false;
+    for (const Strides* s : {&L.q, &L.k, &L.v, &L.o})
+        if (!strides_ok4(*s)) return false;
+    return T < ((int64_t)1 << 30);
+}
+
+hipError_t launch_prefill_f32(const float* q, const float* k, const float* v, float* out,
+                              int64_t B, int64_t H, int64_t T, int D, int64_t W, const Layout& L,
+                              float scale, hipStream_t stream, float* lse) {
+    F32Args a = {};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.lse = lse;
+    a.L = L;
+    a.H = (int)H;
+    a.T = (int)T;
+    a.W = (int)(W < T ? W : T);
+    a.nqt = (int)((T + 31) / 32);
+    const int64_t nwaves = B * H * a.nqt;
+    a.nwaves = (int)nwaves;
+    a.c = kLog2e * fabsf(scale);
+    a.qneg = scale < 0.f ? 1 : 0;
+    const dim3 grid((unsigned)((nwaves + 3) / 4));
+    void* args[] = {(void*)&a};
+    const void* kern = D == 128 ? (const void*)prefill_f32_kernel<128>
+                     : D == 64  ? (const void*)prefill_f32_kernel<64>
+                                : (const void*)prefill_f32_kernel<32>;
+    return hipLaunchKernel(kern, grid, dim3(256), args, 0, stream);
+}
+
+}  // namespace swa
