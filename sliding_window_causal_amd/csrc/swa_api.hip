@@ -179,6 +179,11 @@ int swa_backward(const void* q, const void* k, const void* v, const void* out, c
             (const bf*)q, (const bf*)k, (const bf*)v, (const bf*)out, (const bf*)dout, (bf*)dq,
             (bf*)dk, (bf*)dv, lse_ws, delta, B, H, T, (int)D, W, sc, st));
     }
+    if (swa::backward_f32_supports(q, k, v, out, dout, dq, dk, dv, T, D))
+        return from_hip(swa::launch_backward_f32(
+            (const float*)q, (const float*)k, (const float*)v, (const float*)out,
+            (const float*)dout, (float*)dq, (float*)dk, (float*)dv, lse, lse_ws, delta, B, H, T,
+            (int)D, W, sc, st));
     return from_hip(swa::launch_rowwise_backward<float>(
         (const float*)q, (const float*)k, (const float*)v, (const float*)out, (const float*)dout,
         (float*)dq, (float*)dk, (float*)dv, lse_ws, delta, B, H, T, (int)D, W, sc, st));

@@ -97,6 +97,20 @@ hipError_t launch_prefill_f32(const float* q, const float* k, const float* v, fl
                               int64_t B, int64_t H, int64_t T, int D, int64_t W, const Layout& L,
                               float scale, hipStream_t stream, float* lse = nullptr);
 
+// fp32 matrix-core backward (contiguous [B, H, T, D], D in {32, 64, 128},
+// 16-byte aligned): unless lse_in is given, the fp32 forward again for the
+// per-row log-sum-exp (into lse; its output goes to dq); then a query-row
+// kernel (dq; writes the log2 normalisers to lse and dout . out to delta)
+// and a key-row kernel (dk, dv).
+bool backward_f32_supports(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const void* dq, const void* dk, const void* dv,
+                           int64_t T, int64_t D);
+hipError_t launch_backward_f32(const float* q, const float* k, const float* v, const float* o,
+                               const float* dout, float* dq, float* dk, float* dv,
+                               const float* lse_in, float* lse, float* delta, int64_t B,
+                               int64_t H, int64_t T, int D, int64_t W, float scale,
+                               hipStream_t stream);
+
 // bf16 MFMA chunk continuation of a ring (q, kc, vc, out contiguous
 // [S, H, C, D], rings [S, H, W, D]); D in {64, 128}, 16-byte aligned
 // pointers, slabs under 2 GiB (chunk_bf16_supports).
