@@ -135,6 +135,10 @@ int swa_decode(const void* q, const void* kring, const void* vring, const int64_
     }
     if (dtype == SWA_F32) {
         if (D > kMaxRowD) return SWA_ERR_UNSUPPORTED;
+        if (swa::decode_f32_supports(q, kring, vring, out, D, W))
+            return from_hip(swa::launch_decode_f32((const float*)q, (const float*)kring,
+                                                   (const float*)vring, pos, (float*)out, S, H,
+                                                   (int)D, W, st));
         return from_hip(swa::launch_rowwise_decode<float>((const float*)q, (const float*)kring,
                                                           (const float*)vring, pos, (float*)out, S,
                                                           H, (int)D, W, st));

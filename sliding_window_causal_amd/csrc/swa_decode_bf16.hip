@@ -47,8 +47,9 @@ __device__ inline float quad_sum(float x) {
     return x;
 }
 
-// Sum over the N lanes (4, 8 or 16) that hold one row, left in all of them
-// (DPP: quad exchanges, then the half-row and row mirrors).
+// Sum over the N lanes (4, 8, 16 or 32) that hold one row, left in all of
+// them (DPP: quad exchanges, then the half-row and row mirrors; a lane
+// exchange for the two 16-lane rows of 32).
 template <int N>
 __device__ inline float row_sum(float x) {
     x = quad_sum(x);
@@ -56,6 +57,7 @@ __device__ inline float row_sum(float x) {
         x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, true));
     if constexpr (N >= 16)
         x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, true));
+    if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);
     return x;
 }
 
@@ -74,21 +76,51 @@ __device__ inline float dot8(const u32x4& k, const u32x4& q, float acc) {
 __device__ inline float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ inline float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
+// One 16-byte chunk of a row (8 bf16 or 4 fp32 elements): its dot product
+// with the query's chunk, and acc[e] += p * element e.
+template <typename E>
+__device__ inline float chunk_dot(const u32x4& k, const u32x4& q, float acc) {
+    if constexpr (sizeof(E) == 2) {
+        return dot8(k, q, acc);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t kj = k[j], qj = q[j];
+            acc = fmaf(__uint_as_float(kj), __uint_as_float(qj), acc);
+        }
+        return acc;
+    }
+}
+template <typename E>
+__device__ inline void chunk_axpy(float p, const u32x4& v, float (&acc)[16 / sizeof(E)]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t vj = v[j];
+        if constexpr (sizeof(E) == 2) {
+            acc[2 * j] = fmaf(p, bf_lo(vj), acc[2 * j]);
+            acc[2 * j + 1] = fmaf(p, bf_hi(vj), acc[2 * j + 1]);
+        } else {
+            acc[j] = fmaf(p, __uint_as_float(vj), acc[j]);
+        }
+    }
+}
+
 // Arguments of one decode launch.  A launch has S * H * P workgroups: split
 // sp of (stream, head) sh covers the occupied slots [sp * chunk,
 // min(n, (sp + 1) * chunk)).  With P = 1 the workgroup writes the output;
 // otherwise it writes its unnormalised partial output, max and sum to the
 // workspace and decode_combine_kernel merges the P partials.
+template <typename E>
 struct DecArgs {
-    const bf16* q;
-    const bf16* kring;
-    const bf16* vring;
+    const E* q;
+    const E* kring;
+    const E* vring;
     const int64_t* pos;
-    bf16* out;
-    const bf16* knew;     // fused append: k, v of the current token ([S, H, D]), else null
-    const bf16* vnew;
-    bf16* kring_w;        // the rings again, writable (fused append only)
-    bf16* vring_w;
+    E* out;
+    const E* knew;        // fused append: k, v of the current token ([S, H, D]), else null
+    const E* vnew;
+    E* kring_w;           // the rings again, writable (fused append only)
+    E* vring_w;
     float* ws_o;          // [S * H * P, D] partial outputs (P > 1)
     float* ws_ml;         // [S * H * P, 2] partial (max, sum) (P > 1)
     int64_t H, W;
@@ -96,13 +128,15 @@ struct DecArgs {
     float c;              // log2(e) / sqrt(D)
 };
 
-template <int D, bool ROWS>
-__global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a) {
-    constexpr int LPR = ROWS ? D / 8 : 4;       // lanes per row
-    constexpr int CPL = D / (8 * LPR);          // 16-byte chunks per lane per row
+template <typename E, int D, bool ROWS>
+__global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs<E> a) {
+    constexpr int EPC = 16 / (int)sizeof(E);   // elements per 16-byte chunk
+    constexpr int LPR = ROWS ? D / EPC : 4;     // lanes per row
+    constexpr int CPL = D / (EPC * LPR);        // 16-byte chunks per lane per row
     constexpr int RPG = kDecThreads / LPR;      // rows per workgroup and load
-    constexpr int UN = ROWS ? 16 : 4;           // loads per lane in flight (x CPL)
-    auto ld = [](const bf16* p) {
+    // loads per lane in flight (x CPL)
+    constexpr int UN = ROWS ? 16 : (sizeof(E) == 2 ? 4 : 2);
+    auto ld = [](const E* p) {
         const u32x4* v = reinterpret_cast<const u32x4*>(p);
         if constexpr (ROWS) return __builtin_nontemporal_load(v);
         else return *v;
@@ -126,16 +160,16 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a) {
     const int lo = sp * a.chunk;
     const int hi = min(n, lo + a.chunk);       // rows [lo, hi); empty when lo >= hi
     const int cnt = hi > lo ? hi - lo : 0;
-    const bf16* __restrict__ Kr = a.kring + sh * W * D;
-    const bf16* __restrict__ Vr = a.vring + sh * W * D;
+    const E* __restrict__ Kr = a.kring + sh * W * D;
+    const E* __restrict__ Vr = a.vring + sh * W * D;
     // Fused append: slot p mod W holds the current token, read from knew /
     // vnew instead of the ring (which this launch writes).
     // The slot is written by the one split that covers it (split 0 for a
     // negative position, which has no occupied slots: the slot index is
     // reduced into [0, W) as the plain append does).
     int wslot = -1;
-    const bf16* __restrict__ Kn = nullptr;
-    const bf16* __restrict__ Vn = nullptr;
+    const E* __restrict__ Kn = nullptr;
+    const E* __restrict__ Vn = nullptr;
     if (a.knew != nullptr) {
         int64_t w64 = p % W;
         w64 = w64 < 0 ? w64 + W : w64;
@@ -144,10 +178,10 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a) {
         Vn = a.vnew + sh * D;
         if (p >= 0) wslot = wsl;                // always inside [0, n)
         const bool owner = p >= 0 ? (wsl >= lo && wsl < hi) : sp == 0;
-        if (owner && tid < D / 8) {
-            const int64_t dst = (sh * W + wsl) * D + tid * 8;
-            *reinterpret_cast<u32x4*>(a.kring_w + dst) = *reinterpret_cast<const u32x4*>(Kn + tid * 8);
-            *reinterpret_cast<u32x4*>(a.vring_w + dst) = *reinterpret_cast<const u32x4*>(Vn + tid * 8);
+        if (owner && tid < D / EPC) {
+            const int64_t dst = (sh * W + wsl) * D + tid * EPC;
+            *reinterpret_cast<u32x4*>(a.kring_w + dst) = *reinterpret_cast<const u32x4*>(Kn + tid * EPC);
+            *reinterpret_cast<u32x4*>(a.vring_w + dst) = *reinterpret_cast<const u32x4*>(Vn + tid * EPC);
         }
     }
 
@@ -155,7 +189,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a) {
     u32x4 qv[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
-        qv[i] = *reinterpret_cast<const u32x4*>(a.q + sh * D + (LPR * i + cl) * 8);
+        qv[i] = *reinterpret_cast<const u32x4*>(a.q + sh * D + (LPR * i + cl) * EPC);
 
     // ---- phase 1: scores
     for (int r0 = lo; r0 < hi; r0 += RPG * UN) {
@@ -163,17 +197,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a) {
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
             const int row = r0 + rw + RPG * u;
-            const bf16* src = row == wslot ? Kn : Kr + (int64_t)row * D;
+            const E* src = row == wslot ? Kn : Kr + (int64_t)row * D;
 #pragma unroll
             for (int i = 0; i < CPL; ++i)
-                kv[u][i] = row < hi ? ld(src + (LPR * i + cl) * 8) : u32x4{0, 0, 0, 0};
+                kv[u][i] = row < hi ? ld(src + (LPR * i + cl) * EPC) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
             const int row = r0 + rw + RPG * u;
             float acc = 0.f;
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) acc = dot8(kv[u][i], qv[i], acc);
+            for (int i = 0; i < CPL; ++i) acc = chunk_dot<E>(kv[u][i], qv[i], acc);
             acc = row_sum<LPR>(acc);
             if (cl == 0 && row < hi) sc[row - lo] = acc * a.c;
         }
@@ -202,32 +236,27 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a) {
     const float l = (red[0] + red[1]) + (red[2] + red[3]);
 
     // ---- phase 2: o = sum_r p_r v_r over this lane's columns
-    float acc[CPL][8];
+    float acc[CPL][EPC];
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+        for (int e = 0; e < EPC; ++e) acc[i][e] = 0.f;
     for (int r0 = lo; r0 < hi; r0 += RPG * UN) {
         u32x4 vv[UN][CPL];
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
             const int row = r0 + rw + RPG * u;
-            const bf16* src = row == wslot ? Vn : Vr + (int64_t)row * D;
+            const E* src = row == wslot ? Vn : Vr + (int64_t)row * D;
 #pragma unroll
             for (int i = 0; i < CPL; ++i)
-                vv[u][i] = row < hi ? ld(src + (LPR * i + cl) * 8) : u32x4{0, 0, 0, 0};
+                vv[u][i] = row < hi ? ld(src + (LPR * i + cl) * EPC) : u32x4{0, 0, 0, 0};
         }
 #pragma unroll
         for (int u = 0; u < UN; ++u) {
             const int row = r0 + rw + RPG * u;
             const float pr = row < hi ? sc[row - lo] : 0.f;
 #pragma unroll
-            for (int i = 0; i < CPL; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc[i][2 * j] = fmaf(pr, bf_lo(vv[u][i][j]), acc[i][2 * j]);
-                    acc[i][2 * j + 1] = fmaf(pr, bf_hi(vv[u][i][j]), acc[i][2 * j + 1]);
-                }
+            for (int i = 0; i < CPL; ++i) chunk_axpy<E>(pr, vv[u][i], acc[i]);
         }
     }
     __syncthreads();   // every lane is done with the probabilities
@@ -236,13 +265,13 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs a) {
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sm[rw * D + (LPR * i + cl) * 8 + e] = acc[i][e];
+        for (int e = 0; e < EPC; ++e) sm[rw * D + (LPR * i + cl) * EPC + e] = acc[i][e];
     __syncthreads();
     if (tid < D) {
         float t = 0.f;
         for (int r = 0; r < RPG; ++r) t += sm[r * D + tid];
         if (a.P == 1) {
-            a.out[sh * D + tid] = (bf16)(cnt > 0 ? t / l : 0.f);
+            a.out[sh * D + tid] = (E)(cnt > 0 ? t / l : 0.f);
         } else {
             a.ws_o[bid * D + tid] = t;
             if (tid == 0) {
@@ -307,46 +336,49 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
 
 // Raise the kernel's dynamic-LDS limit to the largest score array, once
 // per device (bit dev of done).
-template <int D, bool ROWS>
+template <typename E, int D, bool ROWS>
 hipError_t allow_lds() {
     static std::atomic<uint64_t> done{0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
     const uint64_t bit = 1ull << (dev & 63);
     if (done.load(std::memory_order_acquire) & bit) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute((const void*)decode_bf16_kernel<D, ROWS>,
+    hipError_t e = hipFuncSetAttribute((const void*)decode_bf16_kernel<E, D, ROWS>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)(kDecodeMaxW * sizeof(float)));
     if (e == hipSuccess) done.fetch_or(bit, std::memory_order_release);
     return e;
 }
 
-template <int D, bool ROWS>
-hipError_t launch_mapping(const DecArgs& a, int64_t wgs, hipStream_t stream) {
+template <typename E, int D, bool ROWS>
+hipError_t launch_mapping(const DecArgs<E>& a, int64_t wgs, hipStream_t stream) {
     // scores (one float per slot of the split), later the partial outputs
     // of the RPG row slots
-    const int64_t red = (int64_t)(kDecThreads / (ROWS ? D / 8 : 4)) * D;
+    const int64_t red = (int64_t)(kDecThreads / (ROWS ? D / (16 / (int)sizeof(E)) : 4)) * D;
     const int64_t floats = a.chunk > red ? (int64_t)a.chunk : red;
-    hipError_t e = allow_lds<D, ROWS>();
+    hipError_t e = allow_lds<E, D, ROWS>();
     if (e != hipSuccess) return e;
     void* args[] = {(void*)&a};
-    return hipLaunchKernel((const void*)decode_bf16_kernel<D, ROWS>, dim3((unsigned)wgs),
+    return hipLaunchKernel((const void*)decode_bf16_kernel<E, D, ROWS>, dim3((unsigned)wgs),
                            dim3(kDecThreads), args, (unsigned)(floats * sizeof(float)), stream);
 }
 
-template <int D>
-hipError_t launch(DecArgs a, int64_t S, hipStream_t stream) {
+template <typename E, int D>
+hipError_t launch(DecArgs<E> a, int64_t S, hipStream_t stream) {
     a.c = kLog2e / sqrtf((float)D);
     const int64_t wgs = S * a.H * a.P;
-    hipError_t e = wgs >= kDecRowsMinWGs ? launch_mapping<D, true>(a, wgs, stream)
-                                         : launch_mapping<D, false>(a, wgs, stream);
+    hipError_t e = wgs >= kDecRowsMinWGs ? launch_mapping<E, D, true>(a, wgs, stream)
+                                         : launch_mapping<E, D, false>(a, wgs, stream);
     if (e != hipSuccess || a.P == 1) return e;
-    const float* wo = a.ws_o;
-    const float* wml = a.ws_ml;
-    int P = a.P;
-    void* cargs[] = {(void*)&wo, (void*)&wml, (void*)&a.out, (void*)&P};
-    return hipLaunchKernel((const void*)decode_combine_kernel<D>, dim3((unsigned)(S * a.H)),
-                           dim3(64), cargs, 0, stream);
+    if constexpr (sizeof(E) == 2) {        // splits: bf16 only
+        const float* wo = a.ws_o;
+        const float* wml = a.ws_ml;
+        int P = a.P;
+        void* cargs[] = {(void*)&wo, (void*)&wml, (void*)&a.out, (void*)&P};
+        return hipLaunchKernel((const void*)decode_combine_kernel<D>, dim3((unsigned)(S * a.H)),
+                               dim3(64), cargs, 0, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 // ---- ring append -----------------------------------------------------------
@@ -452,7 +484,7 @@ hipError_t launch_decode_bf16(const bf16* q, const bf16* kring, const bf16* vrin
                               const int64_t* pos, bf16* out, int64_t S, int64_t H, int D,
                               int64_t W, const bf16* knew, const bf16* vnew, void* workspace,
                               hipStream_t stream) {
-    DecArgs a = {};
+    DecArgs<bf16> a = {};
     a.q = q;
     a.kring = kring;
     a.vring = vring;
@@ -470,8 +502,34 @@ hipError_t launch_decode_bf16(const bf16* q, const bf16* kring, const bf16* vrin
         a.ws_o = (float*)workspace;
         a.ws_ml = a.ws_o + S * H * a.P * D;
     }
-    if (D == 128) return launch<128>(a, S, stream);
-    return launch<64>(a, S, stream);
+    if (D == 128) return launch<bf16, 128>(a, S, stream);
+    return launch<bf16, 64>(a, S, stream);
+}
+
+bool decode_f32_supports(const void* q, const void* kring, const void* vring, const void* out,
+                         int64_t D, int64_t W) {
+    if ((D != 32 && D != 64 && D != 128) || W > kDecodeMaxW) return false;
+    for (const void* p : {q, kring, vring, out})
+        if (((uintptr_t)p & 15) != 0) return false;
+    return true;
+}
+
+hipError_t launch_decode_f32(const float* q, const float* kring, const float* vring,
+                             const int64_t* pos, float* out, int64_t S, int64_t H, int D,
+                             int64_t W, hipStream_t stream) {
+    DecArgs<float> a = {};
+    a.q = q;
+    a.kring = kring;
+    a.vring = vring;
+    a.pos = pos;
+    a.out = out;
+    a.H = H;
+    a.W = W;
+    a.P = 1;
+    a.chunk = (int)W;
+    if (D == 128) return launch<float, 128>(a, S, stream);
+    if (D == 64) return launch<float, 64>(a, S, stream);
+    return launch<float, 32>(a, S, stream);
 }
 
 hipError_t launch_ring_append(const void* knew, const void* vnew, void* kring, void* vring,

@@ -93,3 +93,25 @@ def test_f32_full_size_sampled_rows():
         qh, kh, vh = (npy(x[0, h]) for x in (q, k, v))
         ref = so.swa_rows(qh[None], kh[None], vh[None], W, rows)[0]
         close(out[0, h, rows], ref, f"head {h}")
+
+
+@pytest.mark.parametrize("D,W,S,H", [(32, 50, 2, 3), (64, 97, 16, 16), (128, 64, 2, 2), (128, 40, 32, 8)])
+def test_f32_decode(D, W, S, H):
+    """fp32 decode on the bf16 decode kernel's two lane mappings (quads of
+    lanes below 256 workgroups, D / 4 lanes per slot row from 256 up), rings
+    fresh, partly filled, full and wrapped."""
+    pos = [[0, 1, W // 2, W - 1, W, 2 * W + 3, 3 * W - 1, 3 * W + 7][s % 8] for s in range(S)]
+    T = max(pos) + 1
+    g = si.generator(7400 + D + W, DEV)
+    q, k, v = (si.normal((S, H, T, D), g, torch.float32, DEV) for _ in range(3))
+    kr, vr = so.ring_fill(npy(k), npy(v), pos, W)
+    to = lambda x: torch.from_numpy(x).float().to(DEV)
+    kr, vr = to(kr), to(vr)
+    qs = torch.stack([q[s, :, pos[s]] for s in range(S)]).contiguous()
+    p = torch.tensor(pos, dtype=torch.int64, device=DEV)
+    out = swa.decode(qs, kr, vr, p)
+    torch.cuda.synchronize()
+    ref = so.swa_decode(npy(qs), npy(kr), npy(vr), pos, W)
+    close(out, ref, "decode")
+    rows = np.stack([so.swa_rows(npy(q[s]), npy(k[s]), npy(v[s]), W, [pos[s]])[:, 0] for s in range(S)])
+    close(out, rows, "decode vs prefill row")
