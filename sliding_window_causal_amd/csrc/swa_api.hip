@@ -328,6 +328,11 @@ int chunk_forward(const void* q, const void* kc, const void* vc, const void* kri
             (const swa::bf16*)q, (const swa::bf16*)kc, (const swa::bf16*)vc,
             (const swa::bf16*)kring, (const swa::bf16*)vring, pos0, (swa::bf16*)out, S, H, C,
             (int)D, W, st));
+    if (dtype == SWA_F32 && swa::chunk_f32_supports(q, kc, vc, kring, vring, out, C, D, W))
+        return from_hip(swa::launch_chunk_f32((const float*)q, (const float*)kc,
+                                              (const float*)vc, (const float*)kring,
+                                              (const float*)vring, pos0, (float*)out, S, H, C,
+                                              (int)D, W, st));
     if (dtype == SWA_F32)
         return from_hip(swa::launch_rowwise_chunk<float>((const float*)q, (const float*)kc,
                                                          (const float*)vc, (const float*)kring,

@@ -97,6 +97,14 @@ hipError_t launch_prefill_f32(const float* q, const float* k, const float* v, fl
                               int64_t B, int64_t H, int64_t T, int D, int64_t W, const Layout& L,
                               float scale, hipStream_t stream, float* lse = nullptr);
 
+// fp32 MFMA chunk continuation of a ring (q, kc, vc, out contiguous
+// [S, H, C, D], rings [S, H, W, D]); D in {32, 64, 128}, 16-byte aligned.
+bool chunk_f32_supports(const void* q, const void* kc, const void* vc, const void* kring,
+                        const void* vring, const void* out, int64_t C, int64_t D, int64_t W);
+hipError_t launch_chunk_f32(const float* q, const float* kc, const float* vc, const float* kring,
+                            const float* vring, const int64_t* pos0, float* out, int64_t S,
+                            int64_t H, int64_t C, int D, int64_t W, hipStream_t stream);
+
 // fp32 matrix-core backward (contiguous [B, H, T, D], D in {32, 64, 128},
 // 16-byte aligned): unless lse_in is given, the fp32 forward again for the
 // per-row log-sum-exp (into lse; its output goes to dq); then a query-row

@@ -25,6 +25,13 @@
 // The four wavefronts of a workgroup are independent (no LDS, no barrier):
 // they take consecutive query tiles of one (batch, head), so their key tiles
 // are shared through the L2.
+//
+// CHUNK: the continuation of a ring ("25. Sliding-Window Causal Attention
+// for Streaming Inference", Problem: the bounded cache; "27. Sliding-Window
+// Attention", Problem, the rolling buffer).  Stream s's chunk holds
+// positions p0 .. p0 + C - 1 (q, k, v, out [S, H, C, D]); keys before p0
+// come from ring slot (position mod W).  Each lane addresses its own key
+// rows, so a tile may straddle the ring and the chunk.
 
 #include "swa_internal.h"
 
@@ -41,7 +48,10 @@ struct F32Args {
     float* out;
     float* lse;     // optional: ln(sum_j exp(s_ij * scale)) at lse[bh * T + i]
     Layout L;       // element strides (D axis contiguous)
-    int H, T, W;    // W = min(W, T)
+    int H, T, W;    // rows of q (T, or C for a chunk); W = min(W, T) (a chunk: the ring's W)
+    const float* kring;       // chunk continuation: [S, H, W, D] rings
+    const float* vring;
+    const int64_t* pos0;      // chunk continuation: first position of stream s's chunk
     int nqt;        // 32-query tiles per (b, h)
     int nwaves;     // B * H * nqt
     float c;        // log2(e) * |scale|
@@ -57,7 +67,7 @@ __device__ inline float swap_sum32(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D>
+template <int D, bool CHUNK>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(F32Args a) {
     static_assert(D % 32 == 0 && D <= 128, "head size");
     const int lane = threadIdx.x & 63;
@@ -74,7 +84,33 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(F32Args a) {
     const int64_t qrs = a.L.q.t, krs = a.L.k.t, vrs = a.L.v.t;
 
     const int q0 = qt * 32;
-    const int qi = q0 + lr;
+    const int qi = q0 + lr;                 // this lane's row of q and out
+    // positions: row r of the chunk is position p0 + r (p0 = 0 for a prefill)
+    // (chunk: relative to an origin at least W + 32 below the chunk, so
+    // positions stay in int whatever the stream's length; omod is the
+    // origin's ring slot)
+    int p0 = 0, omod = 0;
+    const float* __restrict__ Kr = nullptr;
+    const float* __restrict__ Vr = nullptr;
+    if constexpr (CHUNK) {
+        int64_t x = a.pos0[b];
+        x = x < 0 ? 0 : x;
+        const int64_t origin = x >= (int64_t)W + 32 ? x - W - 32 : 0;
+        p0 = (int)(x - origin);
+        omod = (int)(origin % W);
+        Kr = a.kring + (int64_t)bh * W * D;
+        Vr = a.vring + (int64_t)bh * W * D;
+    }
+    const int qpos = p0 + qi;
+    // row of key position x: ring slot (x + omod) mod W below p0, else row
+    // x - p0 of k / v (past the last row: the last row, above every valid
+    // query's diagonal)
+    auto key_row = [&](const float* __restrict__ M, const float* __restrict__ R, int64_t rs,
+                       int x) -> const float* {
+        if constexpr (CHUNK)
+            if (x < p0) return R + (int64_t)((x + omod) % W) * D;
+        return M + (int64_t)min(x - p0, T - 1) * rs;
+    };
     // Q^T operand: q[qi][8 g + 4 hf .. + 3] (rows past T read row T - 1 and
     // are never stored)
     f32x4 qf[D / 8];
@@ -87,8 +123,10 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(F32Args a) {
         }
     }
     const float c = a.c;
-    const int t0 = max(q0 - W + 1, 0) / 32;
-    const int t1 = (min(q0 + 32, T) + 31) / 32;
+    // key positions [kbeg, kend): the band of the wave's valid rows, in
+    // 32-key tiles from kbeg (tile-aligned for a prefill)
+    const int kbeg = CHUNK ? max(p0 + q0 - W + 1, 0) : max(q0 - W + 1, 0) / 32 * 32;
+    const int kend = p0 + min(q0 + 32, T);
 
     f32x16 o[D / 32];
 #pragma unroll
@@ -96,12 +134,11 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(F32Args a) {
     float m = -__builtin_inff();     // running row max (raw score units)
     float lsum = 0.f;                // this lane's half of the row sum
 
-    for (int t = t0; t < t1; ++t) {
-        const int k0 = 32 * t;
+    for (int k0 = kbeg; k0 < kend; k0 += 32) {
         // S^T = K Q^T
         f32x16 s = f32x16{};
         {
-            const float* kp = K + (int64_t)min(k0 + lr, T - 1) * krs + 4 * hf;
+            const float* kp = key_row(K, Kr, krs, k0 + lr) + 4 * hf;
 #pragma unroll
             for (int g = 0; g < D / 8; ++g) {
                 const f32x4 kf = *reinterpret_cast<const f32x4*>(kp + 8 * g);
@@ -112,12 +149,12 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(F32Args a) {
         }
         // band mask on tiles that straddle an edge (keys past T lie above
         // every valid query's diagonal)
-        const bool interior = k0 + 31 <= q0 && q0 + 31 - k0 < W;
+        const bool interior = k0 + 31 <= p0 + q0 && p0 + q0 + 31 - k0 < W;
         if (!interior) {
 #pragma unroll
             for (int vv = 0; vv < 16; ++vv) {
                 const int key = k0 + 8 * (vv >> 2) + 4 * hf + (vv & 3);
-                s[vv] = (unsigned)(qi - key) < (unsigned)W ? s[vv] : -__builtin_inff();
+                s[vv] = (unsigned)(qpos - key) < (unsigned)W ? s[vv] : -__builtin_inff();
             }
         }
         float mx = s[0];
@@ -145,8 +182,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(F32Args a) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int key = min(k0 + 8 * i + 4 * hf + e, T - 1);
-                const float* vp = V + (int64_t)key * vrs + lr;
+                const float* vp = key_row(V, Vr, vrs, k0 + 8 * i + 4 * hf + e) + lr;
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
                     o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vp[32 * db], s[4 * i + e], o[db], 0,
@@ -157,7 +193,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(F32Args a) {
     if (qi >= T) return;
     const float l = swap_sum32(lsum);
     const float inv = 1.f / l;
-    if (a.lse != nullptr && hf == 0)
+    if (!CHUNK && a.lse != nullptr && hf == 0)
         a.lse[(int64_t)bh * T + qi] = (m * c + __builtin_amdgcn_logf(l)) * kLn2;
     // lane holds d = 32 db + 8 g + 4 hf + 0..3 of query qi
     float* orow = a.out + b * a.L.o.b + h * a.L.o.h + (int64_t)qi * a.L.o.t;
@@ -206,9 +242,45 @@ hipError_t launch_prefill_f32(const float* q, const float* k, const float* v, fl
     a.qneg = scale < 0.f ? 1 : 0;
     const dim3 grid((unsigned)((nwaves + 3) / 4));
     void* args[] = {(void*)&a};
-    const void* kern = D == 128 ? (const void*)prefill_f32_kernel<128>
-                     : D == 64  ? (const void*)prefill_f32_kernel<64>
-                                : (const void*)prefill_f32_kernel<32>;
+    const void* kern = D == 128 ? (const void*)prefill_f32_kernel<128, false>
+                     : D == 64  ? (const void*)prefill_f32_kernel<64, false>
+                                : (const void*)prefill_f32_kernel<32, false>;
+    return hipLaunchKernel(kern, grid, dim3(256), args, 0, stream);
+}
+
+bool chunk_f32_supports(const void* q, const void* kc, const void* vc, const void* kring,
+                        const void* vring, const void* out, int64_t C, int64_t D, int64_t W) {
+    if (D != 32 && D != 64 && D != 128) return false;
+    for (const void* p : {q, kc, vc, kring, vring, out})
+        if (((uintptr_t)p & 15) != 0) return false;
+    // positions (below 2^30 past the chunk start) in int
+    return C < ((int64_t)1 << 29) && W < ((int64_t)1 << 29);
+}
+
+hipError_t launch_chunk_f32(const float* q, const float* kc, const float* vc, const float* kring,
+                            const float* vring, const int64_t* pos0, float* out, int64_t S,
+                            int64_t H, int64_t C, int D, int64_t W, hipStream_t stream) {
+    F32Args a = {};
+    a.q = q;
+    a.k = kc;
+    a.v = vc;
+    a.out = out;
+    a.L = contiguous_layout(H, C, D);
+    a.H = (int)H;
+    a.T = (int)C;
+    a.W = (int)W;
+    a.kring = kring;
+    a.vring = vring;
+    a.pos0 = pos0;
+    a.nqt = (int)((C + 31) / 32);
+    const int64_t nwaves = S * H * a.nqt;
+    a.nwaves = (int)nwaves;
+    a.c = kLog2e / sqrtf((float)D);
+    const dim3 grid((unsigned)((nwaves + 3) / 4));
+    void* args[] = {(void*)&a};
+    const void* kern = D == 128 ? (const void*)prefill_f32_kernel<128, true>
+                     : D == 64  ? (const void*)prefill_f32_kernel<64, true>
+                                : (const void*)prefill_f32_kernel<32, true>;
     return hipLaunchKernel(kern, grid, dim3(256), args, 0, stream);
 }
 

@@ -115,3 +115,37 @@ def test_f32_decode(D, W, S, H):
     close(out, ref, "decode")
     rows = np.stack([so.swa_rows(npy(q[s]), npy(k[s]), npy(v[s]), W, [pos[s]])[:, 0] for s in range(S)])
     close(out, rows, "decode vs prefill row")
+
+
+@pytest.mark.parametrize("D,W,C,pos0", [(32, 45, 70, [0, 44, 45, 3 * 45 + 7]),
+                                        (128, 64, 100, [5, 63, 64, 1000]),
+                                        (64, 100, 33, [2 ** 31 + 77, 99, 7, 0])])
+def test_f32_chunk(D, W, C, pos0):
+    """fp32 chunk continuation on the matrix cores: tiles that straddle the
+    ring and the chunk, rings fresh, partly filled, full and wrapped, and a
+    stream position past 2^31 (positions taken relative to an origin)."""
+    S, H = len(pos0), 2
+    g = si.generator(7500 + D + W, DEV)
+    qc, kc, vc = (si.normal((S, H, C, D), g, torch.float32, DEV) for _ in range(3))
+    # ring contents: tokens p0 - W .. p0 - 1 of each stream at slot (t mod W)
+    kprev, vprev = (si.normal((S, H, W, D), g, torch.float32, DEV) for _ in range(2))
+    kr = torch.full((S, H, W, D), float("nan"), device=DEV)
+    vr = torch.full_like(kr, float("nan"))
+    for s, p0 in enumerate(pos0):
+        for j in range(W):
+            t = p0 - W + j
+            if t >= 0:
+                kr[s, :, t % W] = kprev[s, :, j]
+                vr[s, :, t % W] = vprev[s, :, j]
+    p = torch.tensor(pos0, dtype=torch.int64, device=DEV)
+    out = swa.chunk_attention(qc, kc, vc, kr, vr, p)
+    torch.cuda.synchronize()
+    # the oracle on the explicit sequence: the W ring tokens (those that
+    # exist), then the chunk
+    for s, p0 in enumerate(pos0):
+        nprev = min(p0, W)
+        keys = torch.cat([kprev[s, :, W - nprev:], kc[s]], dim=1)
+        vals = torch.cat([vprev[s, :, W - nprev:], vc[s]], dim=1)
+        qs = torch.cat([torch.zeros((H, nprev, D), device=DEV), qc[s]], dim=1)
+        ref = so.swa_rows(npy(qs), npy(keys), npy(vals), W, range(nprev, nprev + C))
+        close(out[s], ref, f"stream {s} (p0 {p0})")
