@@ -16,15 +16,14 @@
 //   key rows    S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS
 //               (2 D MFMAs per tile)
 // Masked entries get weight 0 by a select after the exponential, so any
-// finite scale, negative included, works unchanged.
+// finite scale, negative included, works unchanged.  Consecutive workgroups
+// (consecutive 32-row tiles of a head) run on one XCD, sharing its L2.
 
-#include "swa_internal.h"
+#include "swa_mfma.h"
 
 namespace swa {
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct BF32Args {
     const float* q;
@@ -41,6 +40,7 @@ struct BF32Args {
     int T, W;           // W = min(W, T)
     int ntile;          // 32-row tiles per (b, h)
     int nwaves;         // B * H * ntile
+    int remap;          // 1: consecutive workgroups on one XCD (xcd_logical_tile)
     float cs;           // log2(e) * scale (signed)
     float scale;
 };
@@ -56,7 +56,7 @@ template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_f32_query_kernel(BF32Args a) {
     const int lane = threadIdx.x & 63;
     const int lr = lane & 31, hf = lane >> 5;
-    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int gw = xcd_logical_tile(blockIdx.x, gridDim.x, a.remap, 1, -1) * 4 + (threadIdx.x >> 6);
     if (gw >= a.nwaves) return;
     const int bh = gw / a.ntile;
     const int q0 = (gw - bh * a.ntile) * 32;
@@ -145,7 +145,7 @@ template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, D == 128 ? 1 : 2))) void bwd_f32_key_kernel(BF32Args a) {
     const int lane = threadIdx.x & 63;
     const int lr = lane & 31, hf = lane >> 5;
-    const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int gw = xcd_logical_tile(blockIdx.x, gridDim.x, a.remap, 1, -1) * 4 + (threadIdx.x >> 6);
     if (gw >= a.nwaves) return;
     const int bh = gw / a.ntile;
     const int k0 = (gw - bh * a.ntile) * 32;
@@ -230,9 +230,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 
 }
 
 template <int D>
-hipError_t launch_both(const BF32Args& a, hipStream_t st) {
-    void* args[] = {(void*)&a};
+hipError_t launch_both(BF32Args a, hipStream_t st) {
     const dim3 grid((unsigned)((a.nwaves + 3) / 4));
+    a.remap = grid.x % 8 == 0 ? 1 : 0;
+    void* args[] = {(void*)&a};
     hipError_t e = hipLaunchKernel((const void*)bwd_f32_query_kernel<D>, grid, dim3(256), args, 0, st);
     if (e != hipSuccess) return e;
     return hipLaunchKernel((const void*)bwd_f32_key_kernel<D>, grid, dim3(256), args, 0, st);
