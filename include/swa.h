@@ -170,8 +170,10 @@ int64_t swa_decode_workspace_bytes(int64_t S, int64_t H, int64_t D, int64_t W, i
  *                     ignored; concurrent calls need separate workspaces.
  *   workspace_bytes : its size; too small (or null when needed) returns
  *                     SWA_ERR_INVALID_ARG.
- * Other arguments, layouts and dtypes as swa_decode (fp32, and bf16 windows
- * over 16384 slots, run swa_decode's kernels and use no workspace).
+ * Other arguments, layouts and dtypes as swa_decode.  bf16 (D in {64, 128})
+ * and fp32 with D in {32, 64, 128} and 16-byte aligned pointers split;
+ * other fp32 shapes, and windows over 16384 slots, run swa_decode's kernels
+ * and use no workspace.
  */
 int swa_decode_split(const void* q, const void* kring, const void* vring, const int64_t* pos,
                      void* out, int64_t S, int64_t H, int64_t D, int64_t W, int dtype,
@@ -190,8 +192,9 @@ int swa_decode_split(const void* q, const void* kring, const void* vring, const 
  *   workspace    : as swa_decode_split
  * A negative pos[s] writes slot pos mod W reduced into [0, W), as
  * swa_ring_append does, and gives a zero output (no occupied slots).
- * fp32, and bf16 windows over 16384 slots, run the append kernel and then
- * swa_decode's kernels, in stream order.
+ * Shapes that do not split (see swa_decode_split; for fp32 also unaligned
+ * knew / vnew) run the append kernel and then swa_decode's kernels, in
+ * stream order.
  */
 int swa_decode_append(const void* q, const void* knew, const void* vnew, void* kring, void* vring,
                       const int64_t* pos, void* out, int64_t S, int64_t H, int64_t D, int64_t W,

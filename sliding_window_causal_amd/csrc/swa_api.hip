@@ -135,10 +135,10 @@ int swa_decode(const void* q, const void* kring, const void* vring, const int64_
     }
     if (dtype == SWA_F32) {
         if (D > kMaxRowD) return SWA_ERR_UNSUPPORTED;
-        if (swa::decode_f32_supports(q, kring, vring, out, D, W))
+        if (swa::decode_f32_supports(q, kring, vring, out, nullptr, nullptr, D, W))
             return from_hip(swa::launch_decode_f32((const float*)q, (const float*)kring,
                                                    (const float*)vring, pos, (float*)out, S, H,
-                                                   (int)D, W, st));
+                                                   (int)D, W, nullptr, nullptr, nullptr, st));
         return from_hip(swa::launch_rowwise_decode<float>((const float*)q, (const float*)kring,
                                                           (const float*)vring, pos, (float*)out, S,
                                                           H, (int)D, W, st));
@@ -196,16 +196,21 @@ int swa_backward(const void* q, const void* k, const void* v, const void* out, c
 int64_t swa_decode_workspace_bytes(int64_t S, int64_t H, int64_t D, int64_t W, int dtype) {
     if (!positive(S) || !positive(H) || !positive(D) || !positive(W)) return -SWA_ERR_INVALID_ARG;
     if (!fits(S, H, W, D)) return -SWA_ERR_UNSUPPORTED;
-    if (dtype != SWA_BF16 || (D != 64 && D != 128) || W > swa::kDecodeMaxW) return 0;
-    return swa::decode_workspace_bytes(S, H, D, W);
+    if (W > swa::kDecodeMaxW) return 0;
+    if (dtype == SWA_BF16 && (D == 64 || D == 128)) return swa::decode_workspace_bytes(S, H, D, W);
+    if (dtype == SWA_F32 && (D == 32 || D == 64 || D == 128))
+        return swa::decode_workspace_bytes(S, H, D, W);
+    return 0;
 }
 
 namespace {
 
 // Shared checks of the workspace-taking decode entries; returns SWA_OK or a
-// status, and sets *split when the split-window bf16 kernel applies.
-int check_decode_ws(int64_t S, int64_t H, int64_t D, int64_t W, int dtype, const void* ws,
-                    int64_t ws_bytes, bool* split) {
+// status, and sets *split when the split-window kernel applies (bf16; fp32
+// with the alignment decode_f32_supports asks for, knew / vnew included).
+int check_decode_ws(const void* q, const void* kring, const void* vring, const void* out,
+                    const void* knew, const void* vnew, int64_t S, int64_t H, int64_t D,
+                    int64_t W, int dtype, const void* ws, int64_t ws_bytes, bool* split) {
     if (!positive(S) || !positive(H) || !positive(D) || !positive(W)) return SWA_ERR_INVALID_ARG;
     if (ws_bytes < 0) return SWA_ERR_INVALID_ARG;
     if (!fits(S, H, W, D) || S * H * swa::kDecMaxSplits >= ((int64_t)1 << 31))
@@ -216,7 +221,8 @@ int check_decode_ws(int64_t S, int64_t H, int64_t D, int64_t W, int dtype, const
     const int64_t need = swa_decode_workspace_bytes(S, H, D, W, dtype);
     if (need > 0 && (!ws || ws_bytes < need || ((uintptr_t)ws & 15) != 0))
         return SWA_ERR_INVALID_ARG;
-    *split = dtype == SWA_BF16 && W <= swa::kDecodeMaxW;
+    *split = (dtype == SWA_BF16 && W <= swa::kDecodeMaxW) ||
+             (dtype == SWA_F32 && swa::decode_f32_supports(q, kring, vring, out, knew, vnew, D, W));
     return SWA_OK;
 }
 
@@ -227,9 +233,16 @@ int swa_decode_split(const void* q, const void* kring, const void* vring, const 
                      void* workspace, int64_t workspace_bytes, void* stream) {
     if (!q || !kring || !vring || !pos || !out) return SWA_ERR_INVALID_ARG;
     bool split = false;
-    const int rc = check_decode_ws(S, H, D, W, dtype, workspace, workspace_bytes, &split);
+    const int rc = check_decode_ws(q, kring, vring, out, nullptr, nullptr, S, H, D, W, dtype,
+                                   workspace, workspace_bytes, &split);
     if (rc != SWA_OK) return rc;
     if (!split) return swa_decode(q, kring, vring, pos, out, S, H, D, W, dtype, stream);
+    void* ws = swa_decode_workspace_bytes(S, H, D, W, dtype) > 0 ? workspace : nullptr;
+    if (dtype == SWA_F32)
+        return from_hip(swa::launch_decode_f32((const float*)q, (const float*)kring,
+                                               (const float*)vring, pos, (float*)out, S, H,
+                                               (int)D, W, nullptr, nullptr, ws,
+                                               (hipStream_t)stream));
     return from_hip(swa::launch_decode_bf16(
         (const swa::bf16*)q, (const swa::bf16*)kring, (const swa::bf16*)vring, pos,
         (swa::bf16*)out, S, H, (int)D, W, nullptr, nullptr,
@@ -242,7 +255,8 @@ int swa_decode_append(const void* q, const void* knew, const void* vnew, void* k
                       int dtype, void* workspace, int64_t workspace_bytes, void* stream) {
     if (!q || !knew || !vnew || !kring || !vring || !pos || !out) return SWA_ERR_INVALID_ARG;
     bool split = false;
-    const int rc = check_decode_ws(S, H, D, W, dtype, workspace, workspace_bytes, &split);
+    const int rc = check_decode_ws(q, kring, vring, out, knew, vnew, S, H, D, W, dtype, workspace,
+                                   workspace_bytes, &split);
     if (rc != SWA_OK) return rc;
     if (!split) {
         // no fused kernel for this shape: append, then decode, in stream order
@@ -250,6 +264,12 @@ int swa_decode_append(const void* q, const void* knew, const void* vnew, void* k
         if (r != SWA_OK) return r;
         return swa_decode(q, kring, vring, pos, out, S, H, D, W, dtype, stream);
     }
+    if (dtype == SWA_F32)
+        return from_hip(swa::launch_decode_f32(
+            (const float*)q, (const float*)kring, (const float*)vring, pos, (float*)out, S, H,
+            (int)D, W, (const float*)knew, (const float*)vnew,
+            swa_decode_workspace_bytes(S, H, D, W, dtype) > 0 ? workspace : nullptr,
+            (hipStream_t)stream));
     return from_hip(swa::launch_decode_bf16(
         (const swa::bf16*)q, (const swa::bf16*)kring, (const swa::bf16*)vring, pos,
         (swa::bf16*)out, S, H, (int)D, W, (const swa::bf16*)knew, (const swa::bf16*)vnew,

@@ -288,11 +288,11 @@ __global__ __launch_bounds__(kDecThreads) void decode_bf16_kernel(DecArgs<E> a) 
 // wavefront per row: lane p holds split p's (max, sum) (P <= 64), M and the
 // weighted sum come from wave reductions, and the output loop takes each
 // split's weight from its lane and keeps eight splits' loads in flight.
-template <int D>
+template <typename E, int D>
 __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ ws_o,
                                                             const float* __restrict__ ws_ml,
-                                                            bf16* __restrict__ out, int P) {
-    constexpr int R = D / 64;
+                                                            E* __restrict__ out, int P) {
+    constexpr int R = (D + 63) / 64;            // columns lane + 64 r (those below D)
     const int64_t sh = blockIdx.x;
     const int lane = threadIdx.x;
     const float* ml = ws_ml + 2 * sh * P;
@@ -317,7 +317,8 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
 #pragma unroll
         for (int u = 0; u < 8; ++u)
 #pragma unroll
-            for (int r = 0; r < R; ++r) y[u][r] = p + u < P ? po[(int64_t)(p + u) * D + 64 * r] : 0.f;
+            for (int r = 0; r < R; ++r)
+                y[u][r] = p + u < P && lane + 64 * r < D ? po[(int64_t)(p + u) * D + 64 * r] : 0.f;
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             // weight of split p + u: 0 for an empty split, whose row is never used
@@ -331,7 +332,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     }
 #pragma unroll
     for (int r = 0; r < R; ++r)
-        out[sh * D + lane + 64 * r] = (bf16)(L > 0.f ? o[r] / L : 0.f);
+        if (lane + 64 * r < D) out[sh * D + lane + 64 * r] = (E)(L > 0.f ? o[r] / L : 0.f);
 }
 
 // Raise the kernel's dynamic-LDS limit to the largest score array, once
@@ -370,15 +371,12 @@ hipError_t launch(DecArgs<E> a, int64_t S, hipStream_t stream) {
     hipError_t e = wgs >= kDecRowsMinWGs ? launch_mapping<E, D, true>(a, wgs, stream)
                                          : launch_mapping<E, D, false>(a, wgs, stream);
     if (e != hipSuccess || a.P == 1) return e;
-    if constexpr (sizeof(E) == 2) {        // splits: bf16 only
-        const float* wo = a.ws_o;
-        const float* wml = a.ws_ml;
-        int P = a.P;
-        void* cargs[] = {(void*)&wo, (void*)&wml, (void*)&a.out, (void*)&P};
-        return hipLaunchKernel((const void*)decode_combine_kernel<D>, dim3((unsigned)(S * a.H)),
-                               dim3(64), cargs, 0, stream);
-    }
-    return hipErrorInvalidValue;
+    const float* wo = a.ws_o;
+    const float* wml = a.ws_ml;
+    int P = a.P;
+    void* cargs[] = {(void*)&wo, (void*)&wml, (void*)&a.out, (void*)&P};
+    return hipLaunchKernel((const void*)decode_combine_kernel<E, D>, dim3((unsigned)(S * a.H)),
+                           dim3(64), cargs, 0, stream);
 }
 
 // ---- ring append -----------------------------------------------------------
@@ -455,8 +453,8 @@ hipError_t launch_combine_bf16(const float* ws_o, const float* ws_ml, bf16* out,
                                int P, int D, hipStream_t stream) {
     if (P < 1 || P > 64) return hipErrorInvalidValue;
     void* cargs[] = {(void*)&ws_o, (void*)&ws_ml, (void*)&out, (void*)&P};
-    const void* k = D == 128 ? (const void*)decode_combine_kernel<128>
-                             : (const void*)decode_combine_kernel<64>;
+    const void* k = D == 128 ? (const void*)decode_combine_kernel<bf16, 128>
+                             : (const void*)decode_combine_kernel<bf16, 64>;
     return hipLaunchKernel(k, dim3((unsigned)rows), dim3(64), cargs, 0, stream);
 }
 
@@ -507,26 +505,35 @@ hipError_t launch_decode_bf16(const bf16* q, const bf16* kring, const bf16* vrin
 }
 
 bool decode_f32_supports(const void* q, const void* kring, const void* vring, const void* out,
-                         int64_t D, int64_t W) {
+                         const void* knew, const void* vnew, int64_t D, int64_t W) {
     if ((D != 32 && D != 64 && D != 128) || W > kDecodeMaxW) return false;
-    for (const void* p : {q, kring, vring, out})
-        if (((uintptr_t)p & 15) != 0) return false;
+    for (const void* p : {q, kring, vring, out, knew, vnew})
+        if (((uintptr_t)p & 15) != 0) return false;    // (null passes)
     return true;
 }
 
 hipError_t launch_decode_f32(const float* q, const float* kring, const float* vring,
                              const int64_t* pos, float* out, int64_t S, int64_t H, int D,
-                             int64_t W, hipStream_t stream) {
+                             int64_t W, const float* knew, const float* vnew, void* workspace,
+                             hipStream_t stream) {
     DecArgs<float> a = {};
     a.q = q;
     a.kring = kring;
     a.vring = vring;
     a.pos = pos;
     a.out = out;
+    a.knew = knew;
+    a.vnew = vnew;
+    a.kring_w = const_cast<float*>(kring);
+    a.vring_w = const_cast<float*>(vring);
     a.H = H;
     a.W = W;
-    a.P = 1;
-    a.chunk = (int)W;
+    a.P = workspace ? decode_splits(S, H, W) : 1;
+    a.chunk = (int)((W + a.P - 1) / a.P);
+    if (a.P > 1) {
+        a.ws_o = (float*)workspace;
+        a.ws_ml = a.ws_o + S * H * a.P * D;
+    }
     if (D == 128) return launch<float, 128>(a, S, stream);
     if (D == 64) return launch<float, 64>(a, S, stream);
     return launch<float, 32>(a, S, stream);

@@ -157,13 +157,15 @@ hipError_t launch_decode_bf16(const bf16* q, const bf16* kring, const bf16* vrin
                               hipStream_t stream);
 
 // Chunk append into the ring; any D >= 1; elem_bytes is 2 or 4.
-// fp32 ring decode on the same kernel (no split, no fused append): D in
-// {32, 64, 128}, W <= kDecodeMaxW, 16-byte aligned pointers.
+// fp32 ring decode on the same kernel (split and fused append as for bf16):
+// D in {32, 64, 128}, W <= kDecodeMaxW, 16-byte aligned pointers (knew and
+// vnew may be null).
 bool decode_f32_supports(const void* q, const void* kring, const void* vring, const void* out,
-                         int64_t D, int64_t W);
+                         const void* knew, const void* vnew, int64_t D, int64_t W);
 hipError_t launch_decode_f32(const float* q, const float* kring, const float* vring,
                              const int64_t* pos, float* out, int64_t S, int64_t H, int D,
-                             int64_t W, hipStream_t stream);
+                             int64_t W, const float* knew, const float* vnew, void* workspace,
+                             hipStream_t stream);
 
 hipError_t launch_ring_append_chunk(const void* kc, const void* vc, void* kring, void* vring,
                                     const int64_t* pos0, int64_t S, int64_t H, int64_t C,

@@ -162,7 +162,11 @@ def test_decode_workspace_bytes():
     need = L.swa_decode_workspace_bytes(1, 4, 128, 4096, swa.SWA_BF16)
     assert need > 0 and need % 4 == 0
     assert L.swa_decode_workspace_bytes(1024, 4, 128, 4096, swa.SWA_BF16) == 0
-    assert L.swa_decode_workspace_bytes(1, 4, 128, 4096, swa.SWA_F32) == 0
+    # fp32 splits for the head sizes of its matrix-path kernel, at the same sizes
+    assert L.swa_decode_workspace_bytes(1, 4, 128, 4096, swa.SWA_F32) == need
+    assert L.swa_decode_workspace_bytes(1, 4, 32, 4096, swa.SWA_F32) > 0
+    assert L.swa_decode_workspace_bytes(1, 4, 48, 4096, swa.SWA_F32) == 0
+    assert L.swa_decode_workspace_bytes(1, 4, 128, 16385, swa.SWA_F32) == 0
     assert L.swa_decode_workspace_bytes(0, 4, 128, 4096, swa.SWA_BF16) == -swa.SWA_ERR_INVALID_ARG
     assert L.swa_decode_workspace_bytes(1, 4, 128, -1, swa.SWA_BF16) == -swa.SWA_ERR_INVALID_ARG
 
@@ -360,9 +364,10 @@ def test_noalloc_scratch_covers_every_split_size():
     L = swa.lib()
     worst = 0
     for sh in range(1, 600):
-        for D in (64, 128):
+        for dtype, D in ((swa.SWA_BF16, 64), (swa.SWA_BF16, 128), (swa.SWA_F32, 32),
+                         (swa.SWA_F32, 64), (swa.SWA_F32, 128)):
             for W in (1, 255, 256, 257, 1000, 4096, 8191, 16384):
-                n = L.swa_decode_workspace_bytes(1, sh, D, W, swa.SWA_BF16)
+                n = L.swa_decode_workspace_bytes(1, sh, D, W, dtype)
                 assert n >= 0
                 worst = max(worst, n)
     assert 0 < worst <= swa.NOALLOC_SCRATCH_BYTES

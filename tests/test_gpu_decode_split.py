@@ -85,7 +85,8 @@ def test_split_decode_matches_oracle(S, H, D, W, pos):
 def test_small_batch_uses_a_workspace():
     assert swa.swa_decode_workspace_bytes(1, 32, 128, 4096, torch.bfloat16) > 0
     assert swa.swa_decode_workspace_bytes(256, 32, 128, 4096, torch.bfloat16) == 0
-    assert swa.swa_decode_workspace_bytes(1, 32, 128, 4096, torch.float32) == 0
+    assert swa.swa_decode_workspace_bytes(1, 32, 128, 4096, torch.float32) > 0
+    assert swa.swa_decode_workspace_bytes(1, 32, 48, 4096, torch.float32) == 0
 
 
 @pytest.mark.parametrize("dtype,D,W", [(torch.bfloat16, 128, 600), (torch.bfloat16, 64, 37),

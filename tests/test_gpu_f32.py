@@ -149,3 +149,40 @@ def test_f32_chunk(D, W, C, pos0):
         qs = torch.cat([torch.zeros((H, nprev, D), device=DEV), qc[s]], dim=1)
         ref = so.swa_rows(npy(qs), npy(keys), npy(vals), W, range(nprev, nprev + C))
         close(out[s], ref, f"stream {s} (p0 {p0})")
+
+
+@pytest.mark.parametrize("D,W,S,H,pos", [(128, 4096, 1, 4, [4095 + 777]), (32, 300, 3, 2, [5, 298, 1201]),
+                                         (64, 1000, 2, 3, [0, 999 * 3 + 5])])
+def test_f32_split_and_fused_decode(D, W, S, H, pos):
+    """fp32 split decode (partials merged by the combine kernel, which also
+    handles D = 32 with half its lanes idle) and the fused append + decode,
+    against the oracle; the fused launch bitwise equal to append then split
+    decode."""
+    T = max(pos) + 1
+    g = si.generator(7600 + D + W, DEV)
+    q, k, v = (si.normal((S, H, T, D), g, torch.float32, DEV) for _ in range(3))
+    assert swa.swa_decode_workspace_bytes(S, H, D, W, torch.float32) > 0
+    to = lambda x: torch.from_numpy(x).float().to(DEV)
+    kr, vr = (to(x) for x in so.ring_fill(npy(k), npy(v), pos, W))
+    qs = torch.stack([q[s, :, pos[s]] for s in range(S)]).contiguous()
+    p = torch.tensor(pos, dtype=torch.int64, device=DEV)
+    split = swa.decode(qs, kr, vr, p, split=True)
+    noalloc = torch.empty_like(qs)
+    swa.swa_decode_split_noalloc(qs, kr, vr, p, noalloc)
+    prev = [max(x - 1, 0) for x in pos]
+    kr2, vr2 = (to(x) for x in so.ring_fill(npy(k), npy(v), prev, W))
+    for s in range(S):
+        if pos[s] == 0:
+            kr2[s].fill_(float("nan"))
+            vr2[s].fill_(float("nan"))
+    kr3, vr3 = kr2.clone(), vr2.clone()
+    take = lambda x: torch.stack([x[s, :, pos[s]] for s in range(S)]).contiguous()
+    fused = swa.decode_append(qs, take(k), take(v), kr2, vr2, p)
+    swa.swa_ring_append(take(k), take(v), kr3, vr3, p)
+    unfused = swa.decode(qs, kr3, vr3, p, split=True)
+    torch.cuda.synchronize()
+    ref = so.swa_decode(npy(qs), npy(kr), npy(vr), pos, W)
+    close(split, ref, "split decode")
+    close(fused, ref, "fused append + decode")
+    assert torch.equal(noalloc, split)
+    assert torch.equal(fused, unfused)
