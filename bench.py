@@ -377,7 +377,7 @@ def main() -> int:
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": gbs / PEAK_HBM_GBS,
                          "traffic": read_traffic("decode_bf16_s256_w4096_traffic.txt", sha),
-                         "kernel": "decode_bf16_kernel<128>", "kernel_source_sha": sha},
+                         "kernel": "decode_bf16_kernel<bf16,128,rows>", "kernel_source_sha": sha},
         }
         if not do_p:
             res["value"], res["unit"] = gbs, "GB/s"
