@@ -45,11 +45,6 @@ struct BF32Args {
     float scale;
 };
 
-__device__ inline float pair_sum(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 __device__ inline f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
 template <int D>
@@ -80,7 +75,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         dl = __builtin_fmaf(df[g][2], of[2], dl);
         dl = __builtin_fmaf(df[g][3], of[3], dl);
     }
-    const float delta = pair_sum(dl);
+    const float delta = swap_sum(dl);
     const float L2 = a.lse[(int64_t)bh * T + rc] * kLog2e;
     if (hf == 0 && qi < T) {
         a.l2[(int64_t)bh * T + qi] = L2;

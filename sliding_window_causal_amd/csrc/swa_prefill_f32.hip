@@ -40,7 +40,6 @@
 namespace swa {
 namespace {
 
-
 struct F32Args {
     const float* q;
     const float* k;
@@ -58,15 +57,6 @@ struct F32Args {
     float c;        // log2(e) * |scale|
     int qneg;       // scale < 0: q negated (exact) and |scale| used
 };
-
-__device__ inline float swap_max32(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ inline float swap_sum32(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 template <int D, bool CHUNK>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(F32Args a) {
@@ -162,7 +152,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(F32Args a) {
         float mx = s[0];
 #pragma unroll
         for (int vv = 1; vv < 16; ++vv) mx = fmaxf(mx, s[vv]);
-        mx = swap_max32(mx);
+        mx = swap_max(mx);
         if (mx > m) {
             // m = -inf before the row's first key: nothing to rescale
             const float alpha = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m - mx) * c);
@@ -193,7 +183,7 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(F32Args a) {
     }
 
     if (qi >= T) return;
-    const float l = swap_sum32(lsum);
+    const float l = swap_sum(lsum);
     const float inv = 1.f / l;
     if (!CHUNK && a.lse != nullptr && hf == 0)
         a.lse[(int64_t)bh * T + qi] = (m * c + __builtin_amdgcn_logf(l)) * kLn2;

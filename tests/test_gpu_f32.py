@@ -186,3 +186,34 @@ def test_f32_split_and_fused_decode(D, W, S, H, pos):
     close(fused, ref, "fused append + decode")
     assert torch.equal(noalloc, split)
     assert torch.equal(fused, unfused)
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+def test_f32_out_of_window_corruption_is_bitwise_invisible(D):
+    """k[j0] and v[j0] set to +-3e38 (finite fp32; the dot products with q
+    overflow): every row outside [j0, j0 + W - 1] keeps its output and its
+    log-sum-exp bit for bit.  j0 runs over tile edges, keys at i - W for
+    tile-aligned rows i, and keys a wavefront walks but does not need."""
+    T, W = 300, 100
+    g = si.generator(7700 + D, DEV)
+    q, k, v = (si.normal((1, 2, T, D), g, torch.float32, DEV) for _ in range(3))
+
+    def fwd(kk, vv):
+        out = torch.empty_like(q)
+        lse = torch.empty((1, 2, T), dtype=torch.float32, device=DEV)
+        swa.swa_forward_lse(q, kk, vv, out, lse, W)
+        torch.cuda.synchronize()
+        return out, lse
+
+    base, lbase = fwd(k, v)
+    sign = torch.where(torch.arange(D, device=DEV) % 2 == 0, 1.0, -1.0)
+    for j0 in (0, 31, 32, 63, 64 - W + 100, 95, 96, 127, 128, 159, 160 - W + 100, 191, 250, T - W - 1, T - 1):
+        k2, v2 = k.clone(), v.clone()
+        k2[:, :, j0] = 3e38 * sign
+        v2[:, :, j0] = -3e38 * sign
+        out, lse = fwd(k2, v2)
+        rows = np.array([i for i in range(T) if not (j0 <= i <= j0 + W - 1)])
+        if len(rows) == 0:
+            continue
+        assert torch.equal(out[:, :, rows], base[:, :, rows]), f"j0={j0}: rows changed"
+        assert torch.equal(lse[:, :, rows], lbase[:, :, rows]), f"j0={j0}: lse changed"
