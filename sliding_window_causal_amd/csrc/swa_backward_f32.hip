@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, D == 128 ? 1 : 2))) void bwd_f32_key_kernel(BF32Args a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_f32_key_kernel(BF32Args a) {
     const int lane = threadIdx.x & 63;
     const int lr = lane & 31, hf = lane >> 5;
     const int gw = xcd_logical_tile(blockIdx.x, gridDim.x, a.remap, 1, -1) * 4 + (threadIdx.x >> 6);
@@ -206,6 +206,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 
                     adk[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(Q[r + 32 * db], dp[4 * i + e],
                                                                    adk[db], 0, 0, 0);
                 }
+                // bound the operand loads in flight (two waves per SIMD)
+                if (D == 128 && (e & 1)) __builtin_amdgcn_sched_barrier(0);
             }
     }
     if (kr >= T) return;
