@@ -5,7 +5,8 @@ Both run the same kernels, so the outputs must be bit-identical; each is
 also checked against the fp64 oracle at the bf16 bar
 |gpu - oracle| <= 2e-2 + 1e-2 |oracle|.  Two calls in a row, the second with
 smaller sizes, show that what the first call left in the library's static
-scratch does not leak into the second.
+scratch does not leak into the second.  A last case captures the call in a
+HIP graph and replays it with new inputs placed in the captured buffers.
 """
 
 import numpy as np
@@ -63,3 +64,36 @@ def test_noalloc_without_a_split_runs_the_plain_decode():
     swa.swa_decode_split_noalloc(q, kr, vr, pos, got)
     torch.cuda.synchronize()
     assert torch.equal(got, ref)
+
+
+def test_noalloc_decode_replays_in_a_hip_graph():
+    """What the entry point is for: a decode step captured in a HIP graph
+    (no allocation, no workspace, no memset in the captured work) and
+    replayed with new queries and write positions placed in the captured
+    buffers between replays; each replay equals an eager call on the same
+    inputs, bit for bit."""
+    S, H, D, W = 2, 8, 128, 1024
+    q, kr, vr, pos = si.decode_inputs(S, H, D, W, torch.bfloat16, 11, DEV)
+    assert 0 < swa.swa_decode_workspace_bytes(S, H, D, W, torch.bfloat16) <= swa.NOALLOC_SCRATCH_BYTES
+    out = torch.empty_like(q)
+    # an eager call first: the library looks up its scratch address and sets
+    # kernel attributes outside the capture
+    swa.swa_decode_split_noalloc(q, kr, vr, pos, out)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        swa.swa_decode_split_noalloc(q, kr, vr, pos, out)
+    torch.cuda.synchronize()
+    gen = si.generator(12, DEV)
+    rng = np.random.default_rng(13)
+    for r in range(3):
+        q.copy_(si.normal(tuple(q.shape), gen, torch.bfloat16, DEV))
+        pos.copy_(torch.tensor(rng.integers(0, 3 * W, S), dtype=torch.int64, device=DEV))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = torch.empty_like(q)
+        swa.swa_decode_split_noalloc(q, kr, vr, pos, ref)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {r}"
+    del graph
