@@ -1,17 +1,18 @@
 // One-token decode against a bounded W-slot ring of keys and values, bf16
 // (or fp32: the kernel's element type E) in and out, fp32 arithmetic.  The
-// ring is the bounded cache that keeps only
-// the window ("25. Sliding-Window Causal Attention for Streaming Inference",
-// Problem; "Sliding Window Attention", Key Advantages: a KV cache of size W).
+// ring is the bounded cache that keeps only the window ("25. Sliding-Window
+// Causal Attention for Streaming Inference", Problem; "Sliding Window
+// Attention", Key Advantages: a KV cache of size W).
 //
 // The path is bound by HBM: every occupied slot's k and v row is read once
-// (2 * n * D * 2 bytes per (stream, head)) for 4 * n * D flops.  One
+// (2 * n * D * sizeof(E) bytes per (stream, head)) for 4 * n * D flops.  One
 // workgroup of 256 threads owns one (stream, head); LPR lanes own one slot
 // row, lane c of them its 16-byte chunks LPR i + c (8 bf16 or 4 fp32
 // elements each).
 //   phase 1  scores: each lane dots its chunks against the query's
-//            (v_dot2_f32_bf16; fp32 FMAs), the LPR lanes of a row sum with DPP steps,
-//            and the row's score goes to LDS, pre-scaled by log2(e)/sqrt(D).
+//            (v_dot2_f32_bf16; fp32 FMAs), the LPR lanes of a row sum with
+//            DPP steps, and the row's score goes to LDS, pre-scaled by
+//            log2(e)/sqrt(D).
 //   softmax  exact two-pass over the n LDS scores (max, then exp2 and sum).
 //   phase 2  output: the same lane/slot mapping streams v rows, each lane
 //            accumulating p * v for its columns; partial outputs are reduced
@@ -20,15 +21,14 @@
 // chunk per lane): one wavefront load covers whole consecutive rows, a
 // contiguous KiB, and the loads are non-temporal (the ring is read once).
 // Quad (LPR = 4, several chunks per lane): fewer vector instructions per
-// byte.  Measured on 16 GiB
-// reads, 1-KiB-contiguous non-temporal loads reach 7.05-7.1 TB/s, ordinary
-// loads 6.2-6.35 TB/s whatever the pattern, and non-temporal loads that
-// cover 64 bytes of 16 rows per instruction (the quad mapping) 6.36-6.48.
-// With at least one workgroup per compute unit the launch is bound by HBM
-// and takes the row-contiguous mapping (7.0-7.1 TB/s against 6.2-6.3 for
-// the quad one from 512 workgroups on); with fewer, each workgroup's own
-// issue rate bounds it and the quad mapping is faster (46 against 62 us for
-// one stream of 32 heads, W = 4096).
+// byte.  Measured on 16 GiB reads, 1-KiB-contiguous non-temporal loads reach
+// 7.05-7.1 TB/s, ordinary loads 6.2-6.35 TB/s whatever the pattern, and
+// non-temporal loads that cover 64 bytes of 16 rows per instruction (the
+// quad mapping) 6.36-6.48.  With at least one workgroup per compute unit the
+// launch is bound by HBM and takes the row-contiguous mapping (7.0-7.1 TB/s
+// against 6.2-6.3 for the quad one from 512 workgroups on); with fewer, each
+// workgroup's own issue rate bounds it and the quad mapping is faster (46
+// against 62 us for one stream of 32 heads, W = 4096).
 // Occupied slots are [0, min(pos + 1, W)): unoccupied slots are never read.
 
 #include "swa_internal.h"
