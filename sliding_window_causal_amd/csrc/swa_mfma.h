@@ -178,13 +178,27 @@ inline int xcd_longest_first_nfull(int64_t nblocks, int64_t nper, int64_t nshort
 }
 
 // Band mask of a tile starting at key k0: key j is visible to query qi iff
-// 0 <= qi - j < W (one unsigned compare).
+// 0 <= qi - j < W; the other scores become -inf (bit for bit, whatever they
+// held, +inf and NaN included).
 __device__ inline void mask_tile(f32x16& s, int qi, int k0, int hh, int W) {
+    // Register v holds key offset kof = 8 (v / 4) + v % 4 (0 .. 27) past
+    // k0 + 4 hh.  The visible offsets, base - W < kof <= base, are one range
+    // of bits of vis, and each score keeps its bits or becomes -inf by a
+    // bitwise select on its bit (no compares and no lane masks: 16 fewer
+    // instructions per masked tile than compare-and-select).
     const int base = qi - k0 - 4 * hh;
+    const int h1 = min(max(base + 1, 0), 29);
+    const int l0 = min(max(base - W + 1, 0), 28);
+    uint32_t vis = (1u << h1) - (1u << l0);
+    // keeps the per-score masks from being computed ahead, out of a loop,
+    // into registers of their own
+    asm volatile("" : "+v"(vis));
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
         const int kof = 8 * (v >> 2) + (v & 3);
-        s[v] = (unsigned)(base - kof) < (unsigned)W ? s[v] : -__builtin_inff();
+        // keep: bit kof of vis, sign-extended (all ones or zero)
+        const int keep = __builtin_amdgcn_sbfe((int)vis, kof, 1);
+        s[v] = __int_as_float((__float_as_int(s[v]) & keep) | ((int)0xff800000u & ~keep));
     }
 }
 
