@@ -184,8 +184,9 @@ __device__ inline void mask_tile(f32x16& s, int qi, int k0, int hh, int W) {
     // Register v holds key offset kof = 8 (v / 4) + v % 4 (0 .. 27) past
     // k0 + 4 hh.  The visible offsets, base - W < kof <= base, are one range
     // of bits of vis, and each score keeps its bits or becomes -inf by a
-    // bitwise select on its bit (no compares and no lane masks: 16 fewer
-    // instructions per masked tile than compare-and-select).
+    // bitwise select on its bit: 42 vector instructions per masked tile
+    // against 48 and 16 wait states for compare-and-select, whose lane-mask
+    // results cannot be read back to back.
     const int base = qi - k0 - 4 * hh;
     const int h1 = min(max(base + 1, 0), 29);
     const int l0 = min(max(base - W + 1, 0), 28);
