@@ -319,8 +319,10 @@ int swa_ring_append_chunk(const void* kc, const void* vc, void* kring, void* vri
  * takes each row's sum of the rebuilt weights and delta_i = sum_j P_ij dP_ij
  * in fp32 (rows renormalised), and dS reaches the matrix cores as two bf16
  * terms, which keeps the gradients within the bf16 tolerance at any scale.
- * Other shapes run row-wise kernels (one wavefront per query row, then per
- * key row; fp32 arithmetic, delta as that band sum).
+ * fp32 with D in {32, 64, 128} and 16-byte aligned pointers runs on the fp32
+ * matrix cores (delta_i = dout_i . out_i).  Other shapes run row-wise
+ * kernels (one wavefront per query row, then per key row; fp32 arithmetic,
+ * delta as the band sum above).
  */
 int64_t swa_backward_workspace_bytes(int64_t B, int64_t H, int64_t T);
 int swa_backward(const void* q, const void* k, const void* v, const void* out, const void* dout,
