@@ -1,7 +1,7 @@
 """GPU: the fp32 matrix-core prefill and backward (head sizes 32, 64, 128)
 against the fp64 oracle, at sizes that span several 32-row tiles with ragged
 tails, windows from 1 past T, scales of both signs; W = 1 bit for bit; and
-sampled rows of a full [1, 32, 8192, 128] layer.
+sampled rows of a full [1, 32, 8192, 128] layer, forward and backward.
 
 Bars: max |gpu - oracle| <= 1e-5 (outputs); 1e-5 * max(1, max |oracle|)
 (gradients, log-sum-exp).
@@ -93,6 +93,36 @@ def test_f32_full_size_sampled_rows():
         qh, kh, vh = (npy(x[0, h]) for x in (q, k, v))
         ref = so.swa_rows(qh[None], kh[None], vh[None], W, rows)[0]
         close(out[0, h, rows], ref, f"head {h}")
+
+
+def test_f32_full_size_backward_sampled_rows():
+    """The fp32 backward of a full [1, 32, 8192, 128] layer, W = 4096, on the
+    matrix cores with the forward's log-sum-exp kept and with the forward
+    rerun (bit for bit the same): dq of sampled query rows and dk, dv of
+    sampled key rows (window and tile edges, sequence ends, random rows) in
+    three heads against the oracle's band-only gradients."""
+    B, H, T, D, W = 1, 32, 8192, 128, 4096
+    g = si.generator(7400, DEV)
+    q, k, v, do = (si.normal((B, H, T, D), g, torch.float32, DEV) for _ in range(4))
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=DEV)
+    swa.swa_forward_lse(q, k, v, out, lse, W)
+    kept = [torch.empty_like(q) for _ in range(3)]
+    rerun = [torch.empty_like(q) for _ in range(3)]
+    swa.swa_backward(q, k, v, out, do, *kept, W, lse=lse)
+    swa.swa_backward(q, k, v, out, do, *rerun, W)
+    torch.cuda.synchronize()
+    for x, y in zip(kept, rerun):
+        assert torch.equal(x, y), "kept lse and forward rerun differ"
+    q_rows = si.sample_rows(T, W, n_random=8, seed=7401)
+    k_rows = [0, 32, W - 1, W, T - W, T - 1, 5000]
+    for h in (0, 17, H - 1):
+        rq, rk, rv = so.swa_backward_rows(npy(q[0, h]), npy(k[0, h]), npy(v[0, h]), W,
+                                          npy(do[0, h]), q_rows, k_rows)
+        dq, dk, dv = kept
+        close(dq[0, h][torch.as_tensor(q_rows, device=DEV)], rq, f"dq head {h}", rel=True)
+        close(dk[0, h][torch.as_tensor(k_rows, device=DEV)], rk, f"dk head {h}", rel=True)
+        close(dv[0, h][torch.as_tensor(k_rows, device=DEV)], rv, f"dv head {h}", rel=True)
 
 
 @pytest.mark.parametrize("D,W,S,H", [(32, 50, 2, 3), (64, 97, 16, 16), (128, 64, 2, 2), (128, 40, 32, 8)])
