@@ -6,6 +6,7 @@ bad tensors before reaching the library."""
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 import torch
@@ -371,3 +372,43 @@ def test_noalloc_scratch_covers_every_split_size():
                 assert n >= 0
                 worst = max(worst, n)
     assert 0 < worst <= swa.NOALLOC_SCRATCH_BYTES
+
+
+def test_header_compiles_as_c_and_a_c_program_links(tmp_path):
+    """include/swa.h is plain C: a C99 program that includes it (with -Wall
+    -Werror -pedantic) links against libswa.so and gets the documented status
+    codes from calls that fail validation, so no GPU is touched."""
+    src = tmp_path / "abi.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <string.h>
+#include "swa.h"
+
+int main(void) {
+    int bad = 0;
+    int rc;
+    if (swa_abi_version() != 2) bad |= 1;
+    if (strlen(swa_status_string(SWA_ERR_INVALID_ARG)) == 0) bad |= 2;
+    rc = swa_forward(NULL, NULL, NULL, NULL, 1, 1, 8, 64, 4, SWA_BF16, NULL);
+    if (rc != SWA_ERR_INVALID_ARG) bad |= 4;
+    rc = swa_decode((void*)0x1000, (void*)0x1000, (void*)0x1000, (const int64_t*)0x1000,
+                    (void*)0x1000, 1, 1, 64, 0, SWA_BF16, NULL);
+    if (rc != SWA_ERR_INVALID_ARG) bad |= 8;
+    rc = swa_forward((void*)0x1000, (void*)0x1000, (void*)0x1000, (void*)0x1000,
+                     1, 1, 8, 64, 4, 7, NULL);
+    if (rc != SWA_ERR_UNSUPPORTED) bad |= 16;
+    if (swa_decode_workspace_bytes(0, 1, 64, 8, SWA_BF16) >= 0) bad |= 32;
+    printf("%d\n", bad);
+    return bad;
+}
+''')
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(swa.LIB_PATH)
+    cc = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-pedantic", str(src),
+                         "-I", os.path.join(ROOT, "include"), "-L", libdir, "-lswa",
+                         f"-Wl,-rpath,{libdir}", "-o", str(exe)],
+                        stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert cc.returncode == 0, cc.stdout
+    run = subprocess.run([str(exe)], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True,
+                         timeout=120)
+    assert run.returncode == 0, run.stdout
