@@ -412,3 +412,15 @@ int main(void) {
     run = subprocess.run([str(exe)], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True,
                          timeout=120)
     assert run.returncode == 0, run.stdout
+
+
+def test_missing_library_raises_instead_of_falling_back(monkeypatch, tmp_path):
+    """There is no CPU or other fallback: without libswa.so every entry point
+    raises (here with the library path pointed at a file that does not exist
+    and the loaded handle dropped)."""
+    monkeypatch.setattr(swa, "LIB_PATH", str(tmp_path / "libswa.so"))
+    monkeypatch.setattr(swa, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        swa.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        swa.abi_version()
