@@ -397,11 +397,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             // 1 for rows keeping their reference (also rows still fully
             // masked, where m - m would be NaN); 0 when m = -inf.
             const float alpha = __builtin_amdgcn_exp2f(raise ? (m - mx) * c : 0.f);
+            // A row whose reference was -inf has accumulated nothing (every
+            // score so far was -inf), so only rows raising a finite
+            // reference need the rescale; a wavefront's first keys skip it.
+            const bool rescale = __any(raise && m != -__builtin_inff());
             m = raise ? mx : m;
             mref = m == -__builtin_inff() ? 0.f : m * c;
-            lsum *= alpha;
+            if (rescale) {
+                lsum *= alpha;
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+                for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+            }
         }
     };
 
