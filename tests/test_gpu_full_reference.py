@@ -65,3 +65,59 @@ def test_full_size_prefill_every_element_against_fp32_band_attention(name):
             assert ratio <= 1.0, f"{name} b={b} rows [{i0}, {i1}): {ratio:.3f} of the bar"
         del qf, kf, vf
     print(f"{name}: worst error {worst:.3f} of the bf16 bar")
+
+
+@torch.no_grad()
+def band_attention_backward(q, k, v, do, W, scale):
+    """fp32 gradients of band attention for one batch entry (q, k, v, do:
+    [H, T, D] float32), block by block over the queries: P and dP over each
+    block's band, delta from the block's own fp32 output, dS = P (dP - delta),
+    dq = dS k scale, and dk += dS^T q scale, dv += P^T do over the band."""
+    H, T, D = q.shape
+    dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    for i0 in range(0, T, BQ):
+        i1 = min(T, i0 + BQ)
+        lo = max(0, i0 - W + 1)
+        kb, vb = k[:, lo:i1].contiguous(), v[:, lo:i1].contiguous()
+        qb, dob = q[:, i0:i1].contiguous(), do[:, i0:i1].contiguous()
+        s = torch.matmul(qb, kb.transpose(1, 2).contiguous()) * scale
+        i = torch.arange(i0, i1, device=q.device).view(-1, 1)
+        j = torch.arange(lo, i1, device=q.device).view(1, -1)
+        s = s.masked_fill(~((i - j >= 0) & (i - j < W)), float("-inf"))
+        p = torch.softmax(s, dim=-1)
+        o = torch.matmul(p, vb)
+        dp = torch.matmul(dob, vb.transpose(1, 2).contiguous())
+        delta = (dob * o).sum(-1, keepdim=True)
+        ds = p * (dp - delta)
+        dq[:, i0:i1] = torch.matmul(ds, kb) * scale
+        dk[:, lo:i1] += torch.matmul(ds.transpose(1, 2).contiguous(), qb) * scale
+        dv[:, lo:i1] += torch.matmul(p.transpose(1, 2).contiguous(), dob)
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("name", ["prefill_bf16_b1_h32_t8192_d128_w4096",
+                                  "prefill_bf16_b8_h32_t4096_d128_w1024"])
+def test_full_size_backward_every_element_against_fp32_band_attention(name):
+    """The bf16 backward of the prefill workloads as the benchmark launches it
+    (given the forward's log-sum-exp): every element of dq, dk and dv against
+    the fp32 gradients above, at the bf16 bar."""
+    w = si.WORKLOADS[name]
+    q, k, v = si.workload_qkv(w, DEV)
+    do = si.normal(tuple(q.shape), si.generator(w.seed + 11, DEV), torch.bfloat16, DEV)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=DEV)
+    swa.swa_forward_lse(q, k, v, out, lse, w.W)
+    grads = [torch.empty_like(q) for _ in range(3)]
+    swa.swa_backward(q, k, v, out, do, *grads, w.W, lse=lse)
+    torch.cuda.synchronize()
+    W = min(w.W, w.T)
+    worst = {"dq": 0.0, "dk": 0.0, "dv": 0.0}
+    for b in range(w.B):
+        refs = band_attention_backward(q[b].float(), k[b].float(), v[b].float(), do[b].float(),
+                                       W, 1.0 / math.sqrt(w.D))
+        for nm, g, r in zip(("dq", "dk", "dv"), grads, refs):
+            ratio = ((g[b].float() - r).abs() / (BF_ATOL + BF_RTOL * r.abs())).max().item()
+            worst[nm] = max(worst[nm], ratio)
+            assert ratio <= 1.0, f"{name} b={b} {nm}: {ratio:.3f} of the bar"
+        del refs
+    print(f"{name}: worst error of the bf16 bar {worst}")
