@@ -1,6 +1,6 @@
 """GPU: every element of the three full-size bf16 prefill workloads, launched
-as the benchmark launches them, against a plain fp32 band attention written
-with torch on the GPU (score blocks of 512 queries against the keys of their
+as the benchmark launches them (and of the backward of two of them), against
+a plain fp32 band attention (and its gradients) written with torch on the GPU (score blocks of 512 queries against the keys of their
 band, the band predicate 0 <= i - j < W as a mask, softmax, weighted sum:
 "27. Sliding-Window Attention", Step-by-Step Approach).  The fp64 oracle
 stays the authority (it checks sampled rows of the same launches in
