@@ -121,3 +121,40 @@ def test_full_size_backward_every_element_against_fp32_band_attention(name):
             assert ratio <= 1.0, f"{name} b={b} {nm}: {ratio:.3f} of the bar"
         del refs
     print(f"{name}: worst error of the bf16 bar {worst}")
+
+
+@pytest.mark.parametrize("S,C", [(1, 2048), (4, 512), (1, 128)])
+def test_chunk_benchmark_shapes_every_element(S, C):
+    """The chunk continuation at the shapes the benchmark times (32 heads, D
+    128, full 4096-slot rings, first position 5W + 123, inputs drawn as it
+    draws them), plain and split: every element against the fp32 band
+    attention over the sequence the ring and the chunk hold (the W - 1
+    positions before the chunk from ring slot position mod W, then the
+    chunk's keys)."""
+    w = si.WORKLOADS["prefill_bf16_b1_h32_t8192_d128_w4096"]
+    H, D, W = w.H, w.D, w.W
+    g = si.generator(w.seed, DEV)
+    qc, kc, vc = (si.normal((S, H, C, D), g, torch.bfloat16, DEV) for _ in range(3))
+    kr = si.normal((S, H, W, D), g, torch.bfloat16, DEV)
+    vr = si.normal((S, H, W, D), g, torch.bfloat16, DEV)
+    p0 = 5 * W + 123
+    pos0 = torch.tensor([p0] * S, dtype=torch.int64, device=DEV)
+    plain = torch.empty_like(qc)
+    swa.swa_chunk_forward(qc, kc, vc, kr, vr, pos0, plain)
+    ws = torch.empty(max(swa.swa_chunk_workspace_bytes(S, H, C, D, W, torch.bfloat16), 1),
+                     dtype=torch.uint8, device=DEV)
+    split = torch.empty_like(qc)
+    swa.swa_chunk_forward_split(qc, kc, vc, kr, vr, pos0, split, ws)
+    torch.cuda.synchronize()
+    slots = (p0 - W + 1 + torch.arange(W - 1, device=DEV)) % W
+    for s in range(S):
+        kf = torch.cat([kr[s][:, slots], kc[s]], dim=1).float()
+        vf = torch.cat([vr[s][:, slots], vc[s]], dim=1).float()
+        qf = torch.cat([torch.zeros((H, W - 1, D), device=DEV), qc[s].float()], dim=1)
+        for i0 in range(W - 1, W - 1 + C, BQ):
+            i1 = min(W - 1 + C, i0 + BQ)
+            ref = band_attention_block(qf, kf, vf, i0, i1, W)
+            for tag, o in (("plain", plain), ("split", split)):
+                got = o[s, :, i0 - (W - 1):i1 - (W - 1)].float()
+                ratio = ((got - ref).abs() / (BF_ATOL + BF_RTOL * ref.abs())).max().item()
+                assert ratio <= 1.0, f"{tag} S={S} C={C} s={s} rows {i0 - W + 1}..: {ratio:.3f}"
