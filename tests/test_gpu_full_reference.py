@@ -1,6 +1,7 @@
 """GPU: every element of the three full-size bf16 prefill workloads, launched
-as the benchmark launches them (and of the backward of two of them), against
-a plain fp32 band attention (and its gradients) written with torch on the GPU (score blocks of 512 queries against the keys of their
+as the benchmark launches them (and of the backward of two of them, of the
+chunk shapes, and of an fp32 layer in fp64), against a plain band attention
+(and its gradients) written with torch on the GPU (score blocks of 512 queries against the keys of their
 band, the band predicate 0 <= i - j < W as a mask, softmax, weighted sum:
 "27. Sliding-Window Attention", Step-by-Step Approach).  The fp64 oracle
 stays the authority (it checks sampled rows of the same launches in
@@ -158,3 +159,24 @@ def test_chunk_benchmark_shapes_every_element(S, C):
                 got = o[s, :, i0 - (W - 1):i1 - (W - 1)].float()
                 ratio = ((got - ref).abs() / (BF_ATOL + BF_RTOL * ref.abs())).max().item()
                 assert ratio <= 1.0, f"{tag} S={S} C={C} s={s} rows {i0 - W + 1}..: {ratio:.3f}"
+
+
+def test_fp32_full_layer_every_element_against_fp64_band_attention():
+    """The fp32 matrix-core prefill of a full [1, 32, 8192, 128] layer, W 4096:
+    every element against the same band attention computed in fp64 with torch
+    on the GPU, at the fp32 bar max |gpu - ref| <= 1e-5."""
+    B, H, T, D, W = 1, 32, 8192, 128, 4096
+    g = si.generator(7300, DEV)
+    q, k, v = (si.normal((B, H, T, D), g, torch.float32, DEV) for _ in range(3))
+    out = torch.empty_like(q)
+    swa.swa_forward(q, k, v, out, W)
+    torch.cuda.synchronize()
+    qd, kd, vd = q[0].double(), k[0].double(), v[0].double()
+    worst = 0.0
+    for i0 in range(0, T, BQ):
+        i1 = min(T, i0 + BQ)
+        ref = band_attention_block(qd, kd, vd, i0, i1, W)
+        err = (out[0, :, i0:i1].double() - ref).abs().max().item()
+        worst = max(worst, err)
+        assert err <= 1e-5, f"rows [{i0}, {i1}): max abs err {err:.3e}"
+    print(f"fp32 layer: worst abs error {worst:.3e}")
