@@ -1,17 +1,19 @@
-"""GPU: every element of the three full-size bf16 prefill workloads, launched
-as the benchmark launches them (and of the backward of two of them, of the
-chunk shapes, and of an fp32 layer in fp64), against a plain band attention
-(and its gradients) written with torch on the GPU (score blocks of 512 queries against the keys of their
-band, the band predicate 0 <= i - j < W as a mask, softmax, weighted sum:
-"27. Sliding-Window Attention", Step-by-Step Approach).  The fp64 oracle
-stays the authority (it checks sampled rows of the same launches in
-test_gpu_parity.py); this supplementary check covers all B*H*T*D outputs,
-which the oracle cannot do in seconds at these sizes.  It shares nothing with
-the library: torch's own matrix products (fp32, contiguous operands) and
-elementwise operations.
+"""GPU: every output element of the launches the benchmark times, against a
+plain band attention written with torch on the GPU: score blocks of 512
+queries against the keys of their band, the band predicate 0 <= i - j < W as
+a mask, softmax, weighted sum ("27. Sliding-Window Attention", Step-by-Step
+Approach), and its gradients block by block.  Covered: the three full-size
+bf16 prefill workloads, the backward of two of them, the chunk continuation
+at the benchmark's shapes, and a full fp32 layer (against fp64).  The fp64
+oracle stays the authority (it checks sampled rows of the same launches in
+test_gpu_parity.py and the others); this supplementary check covers all
+outputs, which the oracle cannot do in seconds at these sizes.  It shares
+nothing with the library: torch's own matrix products (contiguous operands)
+and elementwise operations.
 
-Bar: the bf16 one, |gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise; fp32
-against fp64 differs by about 1e-6 here, far inside it.
+Bars: the bf16 one, |gpu - ref| <= 2e-2 + 1e-2 |ref| elementwise, against an
+fp32 reference (fp32 against fp64 differs by about 1e-6 here, far inside
+it); the fp32 one, max |gpu - ref| <= 1e-5, against an fp64 reference.
 """
 
 import math
