@@ -4,7 +4,8 @@ queries against the keys of their band, the band predicate 0 <= i - j < W as
 a mask, softmax, weighted sum ("27. Sliding-Window Attention", Step-by-Step
 Approach), and its gradients block by block.  Covered: the three full-size
 bf16 prefill workloads, the backward of two of them, the chunk continuation
-at the benchmark's shapes, and a full fp32 layer (against fp64).  The fp64
+at the benchmark's shapes, a full fp32 layer and the fp32 decode at the
+decode benchmark's shape (those two against fp64).  The fp64
 oracle stays the authority (it checks sampled rows of the same launches in
 test_gpu_parity.py and the others); this supplementary check covers all
 outputs, which the oracle cannot do in seconds at these sizes.  It shares
@@ -182,3 +183,27 @@ def test_fp32_full_layer_every_element_against_fp64_band_attention():
         worst = max(worst, err)
         assert err <= 1e-5, f"rows [{i0}, {i1}): max abs err {err:.3e}"
     print(f"fp32 layer: worst abs error {worst:.3e}")
+
+
+def test_fp32_decode_full_size_every_element_against_fp64():
+    """The fp32 instantiation of the decode kernel at the decode benchmark's
+    shape (256 streams, 32 heads, D 128, full 4096-slot rings): every element
+    against softmax(q k^T / sqrt(D)) v over each ring's occupied slots (all of
+    them: every position is past W), in fp64 with torch, at the fp32 bar."""
+    S, H, D, W = 256, 32, 128, 4096
+    q, kr, vr, pos = si.decode_inputs(S, H, D, W, torch.float32, 8100, DEV)
+    assert bool((pos >= W).all())
+    out = swa.decode(q, kr, vr, pos)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for s0 in range(0, S, 16):
+        qd = q[s0:s0 + 16].double().reshape(-1, 1, D)
+        kd = kr[s0:s0 + 16].double().reshape(-1, W, D)
+        vd = vr[s0:s0 + 16].double().reshape(-1, W, D)
+        sc = torch.matmul(qd, kd.transpose(1, 2).contiguous()) / math.sqrt(D)
+        ref = torch.matmul(torch.softmax(sc, dim=-1), vd).reshape(-1, H, D)
+        err = (out[s0:s0 + 16].double() - ref).abs().max().item()
+        worst = max(worst, err)
+        assert err <= 1e-5, f"streams [{s0}, {s0 + 16}): max abs err {err:.3e}"
+        del qd, kd, vd, sc, ref
+    print(f"fp32 decode: worst abs error {worst:.3e}")
