@@ -4,8 +4,8 @@ queries against the keys of their band, the band predicate 0 <= i - j < W as
 a mask, softmax, weighted sum ("27. Sliding-Window Attention", Step-by-Step
 Approach), and its gradients block by block.  Covered: the three full-size
 bf16 prefill workloads, the backward of two of them, the chunk continuation
-at the benchmark's shapes, a full fp32 layer and the fp32 decode at the
-decode benchmark's shape (those two against fp64).  The fp64
+at the benchmark's shapes, the module of one layer, a full fp32 layer and
+the fp32 decode at the decode benchmark's shape (those two against fp64).  The fp64
 oracle stays the authority (it checks sampled rows of the same launches in
 test_gpu_parity.py and the others); this supplementary check covers all
 outputs, which the oracle cannot do in seconds at these sizes.  It shares
@@ -207,3 +207,38 @@ def test_fp32_decode_full_size_every_element_against_fp64():
         assert err <= 1e-5, f"streams [{s0}, {s0 + 16}): max abs err {err:.3e}"
         del qd, kd, vd, sc, ref
     print(f"fp32 decode: worst abs error {worst:.3e}")
+
+
+def test_module_full_size_every_element():
+    """The module of one 32-head layer as the benchmark launches it (d_model
+    4096 = 32 x 128, T 8192, W 4096, inputs and weights drawn as it draws
+    them): every output element against the same module in fp32 with torch
+    (x @ w projections with the biases, 32 heads of band attention, output
+    projection), at the bf16 bar."""
+    w = si.WORKLOADS["prefill_bf16_b1_h32_t8192_d128_w4096"]
+    dm, H, D, T, W = w.H * w.D, w.H, w.D, w.T, w.W
+    g = si.generator(w.seed + 7, DEV)
+    x = si.normal((w.B, T, dm), g, torch.bfloat16, DEV)
+    wts = [si.normal((dm, dm), g, torch.float32, DEV).mul_(dm ** -0.5).to(torch.bfloat16)
+           for _ in range(4)]
+    bss = [torch.zeros(dm, dtype=torch.bfloat16, device=DEV) for _ in range(4)]
+    out = torch.empty_like(x)
+    ws = torch.empty(swa.swa_mha_workspace_bytes(w.B, T, dm, torch.bfloat16),
+                     dtype=torch.uint8, device=DEV)
+    swa.swa_mha_forward(x, wts[0], bss[0], wts[1], bss[1], wts[2], bss[2], wts[3], bss[3], out,
+                        H, W, workspace=ws)
+    torch.cuda.synchronize()
+    xf = x[0].float()
+    wf = [t.float() for t in wts]
+    bf = [t.float() for t in bss]
+    # [T, dm] -> [H, T, D]
+    heads = [(torch.matmul(xf, wf[i]) + bf[i]).view(T, H, D).transpose(0, 1).contiguous()
+             for i in range(3)]
+    o = torch.empty((H, T, D), dtype=torch.float32, device=DEV)
+    for i0 in range(0, T, BQ):
+        o[:, i0:i0 + BQ] = band_attention_block(heads[0], heads[1], heads[2], i0,
+                                                min(T, i0 + BQ), W)
+    ref = torch.matmul(o.transpose(0, 1).reshape(T, dm), wf[3]) + bf[3]
+    ratio = ((out[0].float() - ref).abs() / (BF_ATOL + BF_RTOL * ref.abs())).max().item()
+    print(f"module: worst error {ratio:.3f} of the bf16 bar")
+    assert ratio <= 1.0, f"{ratio:.3f} of the bar"
