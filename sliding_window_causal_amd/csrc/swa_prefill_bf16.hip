@@ -335,6 +335,52 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             lds_load16_global(lds + (wave * C::NLD_W + i) * 1024, src + logical * 8);
         }
     };
+    // Chunk continuation: the tiles of a stream (K or V) are loaded in order,
+    // and away from the tile holding p0r and a ring wrap they are whole rows
+    // at consecutive addresses (a run of ring slots, then the chunk).  A
+    // cursor holds the next tile's address while tiles stay regular, and ev,
+    // the first tile from which the general per-tile logic takes over again.
+    struct Cursor {
+        const char* p;      // next tile's first row
+        int left;           // bytes from p to the end of its slab (0 past it)
+        int ev;             // first tile index that needs the general path
+    };
+    // cursor for tile t as the first of a regular run, or ev = t if tile t
+    // itself needs the general path
+    auto cursor_at = [&](int t, const bf16* Cbh, const bf16* Rbh, int tb, int cslab, Cursor& cu) {
+        const int k0 = t * C::BN;
+        if (k0 >= p0r) {
+            const int off = (k0 - p0r) * (tb / C::BN);
+            cu.p = reinterpret_cast<const char*>(Cbh) + off;
+            cu.left = max(cslab - off, 0);
+            cu.ev = INT32_MAX;
+            return;
+        }
+        const int s0 = ring_slot(k0 + omod);
+        if (k0 + C::BN <= p0r && s0 + C::BN <= W) {
+            cu.p = reinterpret_cast<const char*>(Rbh) + s0 * 2 * D;
+            cu.left = rslab - s0 * 2 * D;
+            // regular ring tiles run until the slots reach W or the tile
+            // holding p0r
+            cu.ev = min(t + (W - s0) / C::BN, p0r / C::BN);
+            return;
+        }
+        cu.ev = t;
+    };
+    auto load_cursor = [&](int t, const bf16* Cbh, const bf16* Rbh, int tb, int cslab,
+                           const uint32_t (&off)[C::NLD_W], uint32_t lds, bool isv, Cursor& cu) {
+        if (t < cu.ev) {
+            dma_tile(__builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(cu.p), 0, cu.left,
+                                                       0x00020000),
+                     lds, wave, off);
+            cu.p += tb;
+            cu.left = max(cu.left - tb, 0);
+        } else {
+            load_chunk_tile(t, Cbh, Rbh, tb, cslab, off, lds, isv);
+            cursor_at(t + 1, Cbh, Rbh, tb, cslab, cu);
+        }
+    };
+    Cursor kcur = {}, vcur = {};
     // Prefill: the next K and V tiles to load, as an address and the bytes
     // left from there to the end of the band's last tile (0 past it: such
     // loads read nothing and write zeros).  Tiles are loaded in order, so
@@ -345,7 +391,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // tile t into ring slot s (s = t - t0 modulo the ring)
     auto load_k = [&](int t, int s) {
         if constexpr (CHUNK) {
-            load_chunk_tile(t, Kbh, Krh, ktb, kslab, koff, lds_addr(kslot_n(s)), false);
+            load_cursor(t, Kbh, Krh, ktb, kslab, koff, lds_addr(kslot_n(s)), false, kcur);
         } else {
             dma_tile(rows_rsrc(reinterpret_cast<const bf16*>(kp), 0, kr), lds_addr(kslot_n(s)),
                      wave, koff);
@@ -355,7 +401,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     };
     auto load_v = [&](int t, int s) {
         if constexpr (CHUNK) {
-            load_chunk_tile(t, Vbh, Vrh, vtb, vslab, voff, lds_addr(vslot_n(s)), true);
+            load_cursor(t, Vbh, Vrh, vtb, vslab, voff, lds_addr(vslot_n(s)), true, vcur);
         } else {
             dma_tile(rows_rsrc(reinterpret_cast<const bf16*>(vp), 0, vr), lds_addr(vslot_n(s)),
                      wave, voff);
@@ -419,7 +465,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     lsum = 0.f;
     f_lo = careful ? 0 : fa;
     f_len = careful ? 0 : flen;
-    if constexpr (!CHUNK) {
+    if constexpr (CHUNK) {
+        cursor_at(t0, Kbh, Krh, ktb, kslab, kcur);
+        cursor_at(t0, Vbh, Vrh, vtb, vslab, vcur);
+    } else {
         // t0 * 32 < T, so the first tile starts inside both slabs.  The
         // range ends with the band: tiles past it are zeros, not reads.
         kp = reinterpret_cast<const char*>(Kbh) + (int64_t)t0 * ktb;
