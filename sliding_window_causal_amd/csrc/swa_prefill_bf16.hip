@@ -424,10 +424,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         for (int v = 2; v < 16; v += 2) mx = fmaxf(fmaxf(mx, s[v]), s[v + 1]);
         return swap_max(mx);
     };
-    // Reference update for a freshly computed (and masked) score tile whose
-    // row max is mx: raise m if mx exceeds it by more than 2^8 and rescale
-    // what has been accumulated so far.  Runs between tiles, outside the
-    // MFMA/VALU overlap regions.
     // Scores of a tile outside this wave's band: all -inf, so its
     // probabilities are exact zeros whatever its keys hold (a finite key can
     // still overflow the fp32 dot product).  The empty asm keeps this a
@@ -437,6 +433,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[v] = -__builtin_inff();
     };
+    // Reference update for a freshly computed (and masked) score tile whose
+    // row max is mx: raise m if mx exceeds it by more than 2^8 and rescale
+    // what has been accumulated so far.  Runs between tiles, outside the
+    // MFMA/VALU overlap regions.
     auto raise_ref = [&](float mx) {
         const bool raise = mx > m + tau;               // false while the row is fully masked
         if (__any(raise)) {
