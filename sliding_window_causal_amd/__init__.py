@@ -271,6 +271,8 @@ def swa_backward(q, k, v, out, dout, dq, dk, dv, window_size: int, scale=None, l
         raise SWAError(-need, status_string(-need))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    else:
+        _given_workspace(workspace, q.device)
     _check(lib().swa_backward(*[_ptr(t) for t in ts[:5]], None if lse is None else _ptr(lse),
                               *[_ptr(t) for t in ts[5:]], B, H, T, D, W, scale, code,
                               _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -313,12 +315,19 @@ def _decode_dims(q, kring, vring, pos, out):
     return S, H, D, kring.shape[2]
 
 
+def _given_workspace(workspace, device):
+    if not isinstance(workspace, torch.Tensor) or workspace.device != device or \
+            not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    return workspace
+
+
 def _workspace(q, S, H, D, W, workspace):
     need = swa_decode_workspace_bytes(S, H, D, W, _DTYPES[q.dtype])
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    elif workspace.device != q.device or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous tensor on q's device")
+    else:
+        _given_workspace(workspace, q.device)
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -418,6 +427,8 @@ def swa_chunk_forward_split(q, kc, vc, kring, vring, pos0, out, workspace=None,
     need = swa_chunk_workspace_bytes(S, H, C, D, W, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _given_workspace(workspace, q.device)
     _check(lib().swa_chunk_forward_split(_ptr(q), _ptr(kc), _ptr(vc), _ptr(kring), _ptr(vring),
                                          _ptr(pos0), _ptr(out), S, H, C, D, W, code,
                                          _ptr(workspace),
@@ -473,6 +484,8 @@ def swa_mha_forward(x, wq, bq, wk, bk, wv, bv, wo, bo, out, num_heads: int, wind
     need = swa_mha_workspace_bytes(B, T, dm, x.dtype)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    else:
+        _given_workspace(workspace, x.device)
     ptr = lambda t: None if t is None else _ptr(t)
     _check(lib().swa_mha_forward(_ptr(x), _ptr(wq), ptr(bq), _ptr(wk), ptr(bk), _ptr(wv), ptr(bv),
                                  _ptr(wo), ptr(bo), _ptr(out), B, T, dm, int(num_heads), W, code,

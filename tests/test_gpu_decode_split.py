@@ -221,3 +221,26 @@ def test_both_lane_mappings(D, W):
     fused = swa.decode_append(qs, take(k), take(v), kr2, vr2, p)
     torch.cuda.synchronize()
     assert_close(fused, ref, dtype, "fused append, row mapping")
+
+
+def test_workspace_on_another_device_is_rejected_before_any_launch():
+    """A caller workspace that is not a contiguous tensor on the inputs' device
+    raises in the binding (split decode, fused append, chunk split, backward),
+    before the library is called."""
+    q, kr, vr, pos = si.decode_inputs(1, 4, 128, 256, torch.bfloat16, 3, DEV)
+    out = torch.empty_like(q)
+    host_ws = torch.empty(1 << 20, dtype=torch.uint8)
+    strided_ws = torch.empty(2 << 20, dtype=torch.uint8, device=DEV)[::2]
+    for ws in (host_ws, strided_ws):
+        with pytest.raises(ValueError, match="workspace"):
+            swa.swa_decode_split(q, kr, vr, pos, out, workspace=ws)
+        with pytest.raises(ValueError, match="workspace"):
+            swa.swa_decode_append(q, q, q, kr, vr, pos, out, workspace=ws)
+    qc = torch.zeros((1, 4, 64, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError, match="workspace"):
+        swa.swa_chunk_forward_split(qc, qc, qc, kr, vr, pos, torch.empty_like(qc),
+                                    workspace=host_ws)
+    t = torch.zeros((1, 2, 64, 128), dtype=torch.bfloat16, device=DEV)
+    g = [torch.empty_like(t) for _ in range(3)]
+    with pytest.raises(ValueError, match="workspace"):
+        swa.swa_backward(t, t, t, t, t, *g, 16, workspace=host_ws)
